@@ -1,0 +1,27 @@
+"""Paged KV cache decode for AMD MI355X (gfx950).
+
+The compute lives in a HIP shared library (``libpkv.so``) behind a C ABI
+declared in ``include/pkv.h``; ``paged_kv_cache_440_amd._lib`` is its thin
+ctypes binding. Importing this package does not load the library: the API
+names below load it on first use, and fail loudly if it was not built.
+"""
+
+_API = (
+    "kv_cache_append",
+    "copy_blocks",
+    "paged_attention_decode",
+    "paged_attention_workspace_size",
+    "status_string",
+    "library",
+    "DTYPE_CODES",
+    "PkvError",
+)
+
+__all__ = list(_API)
+
+
+def __getattr__(name):
+    if name in _API:
+        from . import _lib
+        return getattr(_lib, name)
+    raise AttributeError(name)
