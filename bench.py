@@ -1,0 +1,221 @@
+"""Decode-step benchmark: paged KV cache append + paged attention on one GPU.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--partition P]
+
+A step is one pass of the whole hot path over one batch: the workload's
+copy-on-write block copies (none for the OPT-13B layer), the append of each
+sequence's new K/V, and paged decode attention (partition pass plus the
+log-sum-exp reduce). Inputs are generated on the host, uploaded once, and
+are resident in HBM when timing starts. Prints ONE JSON line on stdout.
+
+The CPU baseline is the float64 oracle (append + attention over the same
+host inputs), timed on the host after the GPU measurement.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attention tokens/s + achieved KV HBM GB/s (% of MI355X peak)"
+PEAK_HBM_GBPS = 8000.0
+DTYPE_NAMES = {"torch.float32": "f32", "torch.float16": "f16", "torch.bfloat16": "bf16"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    csrc = os.path.join(ROOT, "paged_kv_cache_440_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, partition: int, achieved_bytes: float):
+    """HBM bytes per attention launch from the committed rocprofv3 --pmc
+    summary, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_p{partition}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w):
+    """The oracle, as it stands, on the host: one decode step (append, then
+    attention) over the whole batch, single-threaded float64 numpy."""
+    import torch
+    from threadpoolctl import threadpool_limits
+    from oracle import paged_decode_attention, pool_after_append
+
+    def bits(t):
+        return t.contiguous().view(torch.int16 if t.element_size() == 2 else torch.int32).numpy()
+
+    def widen(a):
+        t = torch.from_numpy(a).view(w.dtype)
+        return t.numpy() if w.dtype == torch.float16 else t.float().numpy()
+
+    q = widen(bits(w.q))
+    kb, vb = bits(w.k_pool), bits(w.v_pool)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        k2, v2 = pool_after_append(kb, vb, bits(w.k_new), bits(w.v_new), w.block_tables,
+                                   w.seq_lens, w.block_size)
+        paged_decode_attention(q, widen(k2), widen(v2), w.block_tables, w.seq_lens,
+                               w.block_size, w.scale)
+        dt = time.perf_counter() - t0
+    return {"value": w.num_seqs / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole batch ({w.num_seqs} sequences, all heads): one append + "
+                      f"attention step, float64 numpy, one thread, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="opt13b_fp16")
+    ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        log(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+            "this library has no multi-GPU path.")
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_440_amd as pkv
+    from paged_kv_cache_440_amd import workloads as wl
+
+    kw = {}
+    if args.block_size is not None:
+        kw["block_size"] = args.block_size
+    t0 = time.perf_counter()
+    w = wl.make(args.workload, **kw)
+    log(f"[bench] workload {w.name}: B={w.num_seqs} H={w.num_heads} Hkv={w.num_kv_heads} "
+        f"D={w.head_dim} bs={w.block_size} dtype={w.dtype} KV={w.kv_bytes() / 1e9:.3f} GB "
+        f"pool={w.num_blocks} blocks (generated in {time.perf_counter() - t0:.1f} s)")
+
+    dev = torch.device("cuda:0")
+    pkv.library()
+    kp, vp = w.k_pool.to(dev), w.v_pool.to(dev)
+    q = w.q.to(dev)
+    k_new, v_new = w.k_new.to(dev), w.v_new.to(dev)
+    tables = torch.from_numpy(w.block_tables).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    pairs = torch.from_numpy(np.ascontiguousarray(w.copy_pairs, np.int32)).to(dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    need = pkv.paged_attention_workspace_size(w.num_seqs, w.num_heads, w.head_dim, w.max_seq_len,
+                                              args.partition)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    max_len = w.max_seq_len
+    stream = torch.cuda.current_stream()
+
+    def attention():
+        pkv.paged_attention_decode(out, q, kp, vp, tables, lens, max_len, w.scale,
+                                   partition_size=args.partition, workspace=ws, stream=stream)
+
+    def step(ev=None):
+        pkv.copy_blocks(kp, vp, pairs, stream=stream)
+        pkv.kv_cache_append(k_new, v_new, kp, vp, tables, lens, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        attention()
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step wall time over K steps
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+
+    # the attention call, bracketed by events on the stream it is launched on
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    kv_bytes = w.kv_bytes()
+    achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
+    tokens_per_s = w.num_seqs / (ms_per_step * 1e-3)
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us, attention {attn_ms * 1e3:.1f} us, "
+        f"{achieved:.0f} GB/s of KV = {100 * achieved / PEAK_HBM_GBPS:.1f}% of 8 TB/s, "
+        f"{tokens_per_s:.0f} tokens/s")
+
+    traffic = measured_traffic(w.name, args.partition, kv_bytes)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on the host")
+        cpu = cpu_baseline(w)
+        log(f"[bench] oracle: {cpu['value']:.2f} tokens/s ({cpu['sample']})")
+
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAMES[str(w.dtype)],
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "num_seqs": w.num_seqs,
+            "num_heads": w.num_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "seq_len_total": int(w.seq_lens.sum()),
+            "max_seq_len": w.max_seq_len,
+            "partition_size": args.partition,
+            "kv_bytes_per_step": kv_bytes,
+        },
+        "attention_us": attn_ms * 1e3,
+        "kv_gbps": achieved,
+        "kv_frac_of_peak": achieved / PEAK_HBM_GBPS,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,161 @@
+/*
+ * pkv.h - paged KV cache decode on AMD MI355X (gfx950): C ABI.
+ *
+ * Three operations over a KV cache cut into fixed-size blocks, each sequence
+ * finding its blocks through a block table (supersilo.blog vLLM/PagedAttention
+ * summary, section "PagedAttention의 설계" -- cited below as [summary];
+ * hjr-study-book "Day 3: KV 캐시와 Continuous Batching", section 4.2):
+ *   pkv_kv_cache_append        store the new token's K/V in the slot its table names
+ *   pkv_copy_blocks            copy whole blocks (the copy behind copy-on-write sharing)
+ *   pkv_paged_attention_decode single-query attention over each sequence's
+ *                              blocks, one softmax over all valid tokens
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every pointer argument is a DEVICE pointer to memory the caller
+ *   allocated on the current HIP device and keeps alive until the enqueued work
+ *   has finished. The library allocates and frees nothing.
+ * Streams. `stream` is a hipStream_t (NULL = the null stream). Each call only
+ *   enqueues kernels on it and returns; results are visible to later work on
+ *   the same stream. Calls on different streams that touch the same pool
+ *   buffers race (the caller orders them).
+ * Layouts (row-major, no padding):
+ *   k_pool, v_pool   [num_blocks][num_kv_heads][block_size][head_dim]
+ *   block_tables     int32 [num_seqs][max_blocks_per_seq]: logical block b of
+ *                    sequence i lives in physical block block_tables[i][b]
+ *   seq_lens         int32 [num_seqs]: number of valid tokens of each sequence
+ *                    INCLUDING the token appended this step (0 = padding row)
+ *   q, out           [num_seqs][num_heads][head_dim]
+ *   k_new, v_new     [num_seqs][num_kv_heads][head_dim]
+ *   block_mapping    int32 [num_pairs][2] = (source block, destination block)
+ * Element types.  pkv_dtype; all of q, k_new, v_new, k_pool, v_pool share one.
+ * Supported shapes.  head_dim 64 or 128; block_size a power of two in [8, 256];
+ *   num_heads / num_kv_heads in {1, 2, 4, 8}.
+ * Device-resident values (table entries, seq_lens, block_mapping) are the
+ *   caller's contract and are not read by the host. The kernels never access
+ *   memory outside the buffers described above: a table entry outside
+ *   [0, num_blocks) is clamped into range by attention (its result is then
+ *   meaningless) and skipped by append and copy; a length above
+ *   max_blocks_per_seq * block_size (or above max_seq_len, for attention) is
+ *   clamped to it.
+ * Errors.  Every entry point returns a pkv_status. Host-checkable problems
+ *   return a negative status before anything is enqueued; PKV_ERR_HIP means the
+ *   HIP runtime rejected a launch. No C++ exception crosses this interface.
+ * Threads.  No mutable global state: calls are reentrant.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define PKV_API __attribute__((visibility("default")))
+#else
+#define PKV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_INVALID = -1,     /* null pointer, negative size, inconsistent arguments */
+    PKV_ERR_UNSUPPORTED = -2, /* head_dim / block_size / head grouping / dtype not built */
+    PKV_ERR_WORKSPACE = -3,   /* split-K workspace missing, misaligned or too small */
+    PKV_ERR_HIP = -4          /* the HIP runtime reported an error when launching */
+} pkv_status;
+
+/*
+ * Store each sequence's new token ([summary] section "자기회귀 생성과 KV 캐시":
+ * a decode step appends the new token's K/V after the cached ones; Day 3
+ * section 1 lists the same step per token).
+ *
+ * For every sequence i with L = seq_lens[i] > 0, the token goes to position
+ * L-1: slot (L-1) % block_size of physical block
+ * block_tables[i][(L-1) / block_size], for all num_kv_heads heads, K into
+ * k_pool and V into v_pool. The copy is bit-exact; nothing else in the pools
+ * is written. Rows with L <= 0, or whose target block id is outside
+ * [0, num_blocks), or whose logical block is >= max_blocks_per_seq, are skipped.
+ */
+PKV_API int pkv_kv_cache_append(const void* k_new, const void* v_new,
+                        void* k_pool, void* v_pool,
+                        const int32_t* block_tables, int max_blocks_per_seq,
+                        const int32_t* seq_lens,
+                        int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                        int num_blocks, pkv_dtype dtype, void* stream);
+
+/*
+ * Copy whole blocks, K and V ([summary] section "블록 공유" and blog.aqudi.me
+ * "벤치마크가 다가 아니야! vLLM으로 보는 LLM 추론 최적화" section 3: a block
+ * shared by several sequences is copied only when one of them must write to
+ * it, i.e. copy-on-write).
+ *
+ * For each pair (src, dst) of block_mapping, block dst of k_pool (and of
+ * v_pool) becomes a bit-exact image of block src: all num_kv_heads heads,
+ * all block_size slots. Destinations must be distinct and must not be sources
+ * in the same call (the pairs run concurrently). Pairs with an id outside
+ * [0, num_blocks) are skipped. num_pairs == 0 enqueues nothing.
+ */
+PKV_API int pkv_copy_blocks(void* k_pool, void* v_pool,
+                    const int32_t* block_mapping, int num_pairs,
+                    int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                    pkv_dtype dtype, void* stream);
+
+/*
+ * Bytes of workspace pkv_paged_attention_decode needs for the given sizes and
+ * partition_size (0 when it needs none: partition_size == 0, or every
+ * sequence fits one partition). Returns 0 for invalid sizes as well.
+ */
+PKV_API size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, int head_dim,
+                                          int max_seq_len, int partition_size);
+
+/*
+ * Single-query decode attention through block tables ([summary] sections
+ * "자기회귀 생성과 KV 캐시" and "PagedAttention의 설계").
+ *
+ * For each sequence i (L = seq_lens[i]) and query head h, with kv head
+ * g = h / (num_heads / num_kv_heads):
+ *   out[i][h] = sum_{t < L} softmax_t(scale * q[i][h] . K_i[t][g]) * V_i[t][g]
+ * where K_i[t], V_i[t] are read from slot t % block_size of physical block
+ * block_tables[i][t / block_size]. The softmax is one normalisation over all
+ * L tokens, not a per-block one. Rows with L == 0 are written as zeros.
+ * Slots at or past L are never used (they may hold any bits, NaN included).
+ *
+ * out_dtype selects the output element type (PKV_F32 keeps the fp32
+ * accumulation; F16/BF16 round to nearest even). Arithmetic is fp32
+ * regardless of the input type.
+ *
+ * max_seq_len must bound every seq_lens entry (it sizes the launch) and must
+ * not exceed max_blocks_per_seq * block_size.
+ *
+ * partition_size == 0: one pass per (sequence, kv head). Otherwise a positive
+ * multiple of 64: the tokens of each sequence are cut into partitions of that
+ * many tokens, each handled independently, and merged by a log-sum-exp
+ * reduce; `workspace` (16-byte aligned, at least
+ * pkv_paged_attention_workspace_size(...) bytes, contents ignored and
+ * overwritten) holds the partial results. Work enqueued on `stream` by
+ * different calls must not share a workspace unless ordered by the stream.
+ */
+PKV_API int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype,
+                               const void* q,
+                               const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* seq_lens, int max_seq_len,
+                               int num_seqs, int num_heads, int num_kv_heads,
+                               int head_dim, int block_size, int num_blocks,
+                               float scale, int partition_size,
+                               void* workspace, size_t workspace_bytes,
+                               pkv_dtype dtype, void* stream);
+
+/* Static, NUL-terminated description of a pkv_status value. */
+PKV_API const char* pkv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

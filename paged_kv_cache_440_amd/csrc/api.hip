@@ -1,0 +1,168 @@
+// C-ABI entry points: argument validation, then one launch (or two) on the
+// caller's stream. Declarations and contracts are in include/pkv.h.
+
+#include <math.h>
+
+#include "pkv_internal.hpp"
+
+namespace {
+
+bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
+int dtype_bytes(int d) { return d == PKV_F32 ? 4 : 2; }
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+// log2 of a supported block size (a power of two in [8, 256]), else -1
+int block_log2(int bs) {
+    for (int s = 3; s <= 8; ++s)
+        if (bs == (1 << s)) return s;
+    return -1;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Partition count the launch must cover, or -1 if the sizes overflow.
+long long parts_for(int max_seq_len, int partition_size) {
+    if (partition_size <= 0 || max_seq_len <= partition_size) return 1;
+    return ((long long)max_seq_len + partition_size - 1) / partition_size;
+}
+
+size_t workspace_bytes_for(long long rows, int head_dim, long long parts) {
+    if (parts <= 1) return 0;
+    return (size_t)(rows * parts) * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+    switch (status) {
+        case PKV_OK: return "ok";
+        case PKV_ERR_INVALID: return "invalid argument";
+        case PKV_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, head grouping or dtype";
+        case PKV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case PKV_ERR_HIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+int pkv_kv_cache_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                        const int32_t* block_tables, int max_blocks_per_seq,
+                        const int32_t* seq_lens, int num_seqs, int num_kv_heads, int head_dim,
+                        int block_size, int num_blocks, pkv_dtype dtype, void* stream) {
+    if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks <= 0 || max_blocks_per_seq <= 0 || !valid_dtype(dtype))
+        return PKV_ERR_INVALID;
+    if (!supported_head_dim(head_dim) || block_log2(block_size) < 0) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PKV_OK;
+    if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !seq_lens)
+        return PKV_ERR_INVALID;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PKV_ERR_INVALID;
+    if ((long long)num_seqs * max_blocks_per_seq > INT32_MAX) return PKV_ERR_INVALID;
+    pkv::AppendParams a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = num_kv_heads;
+    a.row_bytes = head_dim * dtype_bytes(dtype);
+    a.log2_bs = block_log2(block_size);
+    a.num_blocks = num_blocks;
+    return pkv::launch_append(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapping, int num_pairs,
+                    int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                    pkv_dtype dtype, void* stream) {
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks <= 0 || !valid_dtype(dtype))
+        return PKV_ERR_INVALID;
+    if (!supported_head_dim(head_dim) || block_log2(block_size) < 0) return PKV_ERR_UNSUPPORTED;
+    if (num_pairs == 0) return PKV_OK;
+    if (!k_pool || !v_pool || !block_mapping) return PKV_ERR_INVALID;
+    if (!aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_INVALID;
+    const long long block_bytes = (long long)num_kv_heads * block_size * head_dim * dtype_bytes(dtype);
+    const long long chunks = (block_bytes / 16 + 1023) / 1024;
+    if (chunks * num_pairs * 2 > INT32_MAX) return PKV_ERR_INVALID;
+    pkv::CopyParams a{};
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.mapping = block_mapping;
+    a.num_pairs = num_pairs;
+    a.block_bytes = block_bytes;
+    a.num_blocks = num_blocks;
+    return pkv::launch_copy_blocks(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, int head_dim,
+                                          int max_seq_len, int partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || partition_size < 0)
+        return 0;
+    return workspace_bytes_for((long long)num_seqs * num_heads, head_dim,
+                               parts_for(max_seq_len, partition_size));
+}
+
+int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
+                               const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* seq_lens, int max_seq_len, int num_seqs,
+                               int num_heads, int num_kv_heads, int head_dim, int block_size,
+                               int num_blocks, float scale, int partition_size, void* workspace,
+                               size_t workspace_bytes, pkv_dtype dtype, void* stream) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
+        partition_size < 0 || !valid_dtype(dtype) || !valid_dtype(out_dtype) || !isfinite(scale))
+        return PKV_ERR_INVALID;
+    if (num_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
+    if (partition_size % 64 != 0) return PKV_ERR_INVALID;
+    const int group = num_heads / num_kv_heads;
+    if (!supported_head_dim(head_dim) || block_log2(block_size) < 0 ||
+        !(group == 1 || group == 2 || group == 4 || group == 8))
+        return PKV_ERR_UNSUPPORTED;
+    if ((long long)max_seq_len > (long long)max_blocks_per_seq * block_size)
+        return PKV_ERR_INVALID;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens) return PKV_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_INVALID;
+    if ((long long)num_seqs * max_blocks_per_seq > INT32_MAX) return PKV_ERR_INVALID;
+
+    const long long parts = parts_for(max_seq_len, partition_size);
+    const long long items = parts * num_seqs * num_kv_heads;
+    if (items > INT32_MAX - 64 || (long long)num_seqs * num_heads * head_dim > INT32_MAX)
+        return PKV_ERR_INVALID;
+    const size_t need = workspace_bytes_for((long long)num_seqs * num_heads, head_dim, parts);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return PKV_ERR_WORKSPACE;
+
+    pkv::AttnParams a{};
+    a.out = out;
+    a.out_dtype = out_dtype;
+    a.ws_acc = reinterpret_cast<float*>(workspace);
+    a.ws_ml = need ? a.ws_acc + (size_t)num_seqs * num_heads * parts * head_dim : nullptr;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = num_kv_heads;
+    a.group = group;
+    a.head_dim = head_dim;
+    a.log2_bs = block_log2(block_size);
+    a.num_blocks = num_blocks;
+    a.scale = scale;
+    a.part_tokens = parts > 1 ? partition_size : 0;
+    a.max_parts = (int)parts;
+    a.max_tokens = max_seq_len;
+    a.num_items = (int)items;
+    a.dtype = dtype;
+    return pkv::launch_paged_attention(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // extern "C"

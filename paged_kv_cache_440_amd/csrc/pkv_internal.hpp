@@ -1,0 +1,66 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pkv.h"
+
+namespace pkv {
+
+// Everything one attention launch needs, validated by the host layer.
+struct AttnParams {
+    void* out;
+    int out_dtype;
+    float* ws_acc;                 // [B][H][max_parts][D] unnormalised partial sums
+    float* ws_ml;                  // [B][H][max_parts][2] (running max in log2 units, sum)
+    const void* q;
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* block_tables;
+    const int32_t* seq_lens;
+    int max_blocks;                // row stride of block_tables
+    int num_seqs;
+    int num_kv_heads;
+    int group;                     // query heads per kv head
+    int head_dim;
+    int log2_bs;
+    int num_blocks;
+    float scale;
+    int part_tokens;               // 0: one pass per sequence
+    int max_parts;                 // partitions per sequence the launch covers
+    int max_tokens;                // lengths are clamped to this
+    int num_items;                 // max_parts * num_seqs * num_kv_heads
+    int dtype;
+};
+
+struct AppendParams {
+    const void* k_new;
+    const void* v_new;
+    void* k_pool;
+    void* v_pool;
+    const int32_t* block_tables;
+    const int32_t* seq_lens;
+    int max_blocks;
+    int num_seqs;
+    int num_kv_heads;
+    int row_bytes;                 // head_dim * element bytes
+    int log2_bs;
+    int num_blocks;
+};
+
+struct CopyParams {
+    void* k_pool;
+    void* v_pool;
+    const int32_t* mapping;
+    int num_pairs;
+    long long block_bytes;         // num_kv_heads * block_size * row bytes
+    int num_blocks;
+};
+
+hipError_t launch_paged_attention(const AttnParams& a, hipStream_t stream);
+hipError_t launch_append(const AppendParams& a, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyParams& a, hipStream_t stream);
+
+}  // namespace pkv

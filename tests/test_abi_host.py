@@ -1,0 +1,153 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before enqueuing anything. None
+of these calls reaches the GPU (every call here fails validation or is a
+no-op), so they run without one."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from paged_kv_cache_440_amd import _lib
+from paged_kv_cache_440_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = 0x10000           # an aligned non-null address; never dereferenced here
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"PKV_API\s+[\w\s\*]*?\b(pkv_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        pytest.skip("libpkv.so not built")
+    return _lib.library()
+
+
+def test_header_declares_the_three_operations():
+    names = declared_symbols()
+    for n in ("pkv_kv_cache_append", "pkv_copy_blocks", "pkv_paged_attention_decode",
+              "pkv_paged_attention_workspace_size", "pkv_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(declared_symbols()) <= exported
+    # nothing else of ours leaks out of the library
+    assert not [s for s in exported if "pkv" in s and s not in declared_symbols()]
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert _lib.status_string(code) and _lib.status_string(code) != "unknown status"
+    assert _lib.status_string(42) == "unknown status"
+
+
+def attn(lib, **kw):
+    args = dict(out=FAKE, out_dtype=0, q=FAKE, k=FAKE, v=FAKE, tables=FAKE, max_blocks=8,
+                lens=FAKE, max_seq_len=100, B=2, H=4, Hkv=4, D=128, bs=16, nb=32,
+                scale=0.1, part=0, ws=0, ws_bytes=0, dtype=1)
+    args.update(kw)
+    a = args
+    return lib.pkv_paged_attention_decode(a["out"], a["out_dtype"], a["q"], a["k"], a["v"],
+                                          a["tables"], a["max_blocks"], a["lens"],
+                                          a["max_seq_len"], a["B"], a["H"], a["Hkv"], a["D"],
+                                          a["bs"], a["nb"], a["scale"], a["part"], a["ws"],
+                                          a["ws_bytes"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), INVALID),
+    (dict(H=6, Hkv=4), INVALID),            # heads not a multiple of kv heads
+    (dict(H=12, Hkv=4), UNSUPPORTED),       # group 3
+    (dict(H=64, Hkv=4), UNSUPPORTED),       # group 16
+    (dict(D=96), UNSUPPORTED),
+    (dict(bs=12), UNSUPPORTED),
+    (dict(bs=4), UNSUPPORTED),
+    (dict(bs=512), UNSUPPORTED),
+    (dict(dtype=3), INVALID),
+    (dict(out_dtype=7), INVALID),
+    (dict(part=100), INVALID),              # not a multiple of 64
+    (dict(part=-64), INVALID),
+    (dict(max_seq_len=8 * 16 + 1), INVALID),  # beyond the table's capacity
+    (dict(scale=float("nan")), INVALID),
+    (dict(q=0), INVALID),
+    (dict(k=0), INVALID),
+    (dict(tables=0), INVALID),
+    (dict(lens=0), INVALID),
+    (dict(out=0), INVALID),
+    (dict(q=FAKE + 4), INVALID),            # misaligned
+    (dict(part=64, ws=0), WORKSPACE),       # 100 tokens in 64-token partitions need a workspace
+    (dict(part=64, ws=FAKE, ws_bytes=16), WORKSPACE),
+    (dict(part=64, ws=FAKE + 8, ws_bytes=1 << 20), WORKSPACE),
+    (dict(B=0), OK),                        # nothing to do, nothing enqueued
+])
+def test_attention_validation(lib, kw, status):
+    assert attn(lib, **kw) == status
+
+
+def test_workspace_size_formula(lib):
+    f = _lib.paged_attention_workspace_size
+    assert f(64, 40, 128, 2048, 0) == 0
+    assert f(64, 40, 128, 512, 512) == 0
+    assert f(64, 40, 128, 2048, 512) == 64 * 40 * 4 * (128 + 2) * 4
+    assert f(64, 40, 128, 2049, 512) == 64 * 40 * 5 * (128 + 2) * 4
+    assert f(16, 64, 128, 32768, 512) == 16 * 64 * 64 * 130 * 4
+    assert f(-1, 40, 128, 2048, 512) == 0
+
+
+def append(lib, **kw):
+    a = dict(kn=FAKE, vn=FAKE, kp=FAKE, vp=FAKE, tables=FAKE, max_blocks=4, lens=FAKE, B=3,
+             Hkv=2, D=64, bs=16, nb=10, dtype=0)
+    a.update(kw)
+    return lib.pkv_kv_cache_append(a["kn"], a["vn"], a["kp"], a["vp"], a["tables"],
+                                   a["max_blocks"], a["lens"], a["B"], a["Hkv"], a["D"], a["bs"],
+                                   a["nb"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-2), INVALID), (dict(Hkv=0), INVALID), (dict(nb=0), INVALID),
+    (dict(max_blocks=0), INVALID), (dict(dtype=5), INVALID), (dict(D=80), UNSUPPORTED),
+    (dict(bs=24), UNSUPPORTED), (dict(kn=0), INVALID), (dict(vp=0), INVALID),
+    (dict(tables=0), INVALID), (dict(lens=0), INVALID), (dict(kp=FAKE + 2), INVALID),
+    (dict(B=0), OK),
+])
+def test_append_validation(lib, kw, status):
+    assert append(lib, **kw) == status
+
+
+def copy(lib, **kw):
+    a = dict(kp=FAKE, vp=FAKE, mapping=FAKE, n=3, Hkv=2, D=64, bs=16, nb=10, dtype=2)
+    a.update(kw)
+    return lib.pkv_copy_blocks(a["kp"], a["vp"], a["mapping"], a["n"], a["Hkv"], a["D"], a["bs"],
+                               a["nb"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), INVALID), (dict(Hkv=-1), INVALID), (dict(nb=0), INVALID),
+    (dict(dtype=-1), INVALID), (dict(D=32), UNSUPPORTED), (dict(bs=3), UNSUPPORTED),
+    (dict(kp=0), INVALID), (dict(mapping=0), INVALID), (dict(vp=FAKE + 1), INVALID),
+    (dict(n=0, mapping=0), OK),
+])
+def test_copy_validation(lib, kw, status):
+    assert copy(lib, **kw) == status
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        _lib.library()
