@@ -31,20 +31,23 @@ __device__ __forceinline__ float hi_to_f32(BF16, uint32_t w) { return u2f(w & 0x
 
 // -- dot product of one 16-byte piece of q and of k, fp32 accumulation ------
 // fp16 / bf16: v_dot2 (two exact products added into an fp32 accumulator).
+// The packed pairs are taken BY VALUE before the bit cast: a bit cast applied
+// directly to a vector-subscript lvalue (q[i]) was compiled as element 0.
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t x) { return __builtin_bit_cast(f16x2, x); }
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t x) { return __builtin_bit_cast(bf16x2, x); }
+
 __device__ __forceinline__ float dot16(F16, const u32x4& q, const u32x4& k) {
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q[i]),
-                                     __builtin_bit_cast(f16x2, k[i]), acc, false);
+        acc = __builtin_amdgcn_fdot2(as_f16x2(q[i]), as_f16x2(k[i]), acc, false);
     return acc;
 }
 __device__ __forceinline__ float dot16(BF16, const u32x4& q, const u32x4& k) {
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[i]),
-                                              __builtin_bit_cast(bf16x2, k[i]), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q[i]), as_bf16x2(k[i]), acc, false);
     return acc;
 }
 __device__ __forceinline__ float dot16(F32, const u32x4& q, const u32x4& k) {
