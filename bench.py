@@ -57,6 +57,11 @@ def measured_traffic(workload: str, partition: int, achieved_bytes: float):
     return rec.get("bytes_per_launch")
 
 
+def pkv_balanced() -> int:
+    from paged_kv_cache_440_amd._lib import PARTITION_BALANCED
+    return PARTITION_BALANCED
+
+
 def cpu_baseline(w):
     """The oracle, as it stands, on the host: one decode step (append, then
     attention) over the whole batch, single-threaded float64 numpy."""
@@ -92,7 +97,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="opt13b_fp16")
     ap.add_argument("--block-size", type=int, default=None)
-    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--partition", type=int, default=None,
+                    help="0: one pass per sequence; a multiple of 64: fixed partitions; "
+                         "-1: balanced (default; 512 for the shared-prefix workloads, where "
+                         "neighbouring sequences share blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -105,6 +113,8 @@ def main():
     import paged_kv_cache_440_amd as pkv
     from paged_kv_cache_440_amd import workloads as wl
 
+    if args.partition is None:
+        args.partition = 512 if args.workload.startswith("shared_prefix") else pkv_balanced()
     kw = {}
     if args.block_size is not None:
         kw["block_size"] = args.block_size
@@ -123,8 +133,8 @@ def main():
     lens = torch.from_numpy(w.seq_lens).to(dev)
     pairs = torch.from_numpy(np.ascontiguousarray(w.copy_pairs, np.int32)).to(dev)
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    need = pkv.paged_attention_workspace_size(w.num_seqs, w.num_heads, w.head_dim, w.max_seq_len,
-                                              args.partition)
+    need = pkv.paged_attention_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                              w.max_seq_len, args.partition)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     max_len = w.max_seq_len
     stream = torch.cuda.current_stream()
@@ -162,12 +172,31 @@ def main():
     torch.cuda.synchronize()
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
+    # practical read ceiling: the probe streams both pools once (contiguous
+    # 16-byte loads, no compute), timed the same way on the same stream
+    pool_bytes = 2 * kp.numel() * kp.element_size()
+    sink = torch.empty(pkv.library().pkv_probe_read_sink_words(kp.numel() * kp.element_size()),
+                       dtype=torch.int32, device=dev)
+    for _ in range(3):
+        pkv.probe_read(kp, sink, stream=stream)
+        pkv.probe_read(vp, sink, stream=stream)
+    rd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(20)]
+    for a, b in rd:
+        a.record(stream)
+        pkv.probe_read(kp, sink, stream=stream)
+        pkv.probe_read(vp, sink, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    read_ceiling = pool_bytes / (float(np.mean([a.elapsed_time(b) for a, b in rd])) * 1e-3) / 1e9
+
     kv_bytes = w.kv_bytes()
     achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
     tokens_per_s = w.num_seqs / (ms_per_step * 1e-3)
     log(f"[bench] step {ms_per_step * 1e3:.1f} us, attention {attn_ms * 1e3:.1f} us, "
         f"{achieved:.0f} GB/s of KV = {100 * achieved / PEAK_HBM_GBPS:.1f}% of 8 TB/s, "
-        f"{tokens_per_s:.0f} tokens/s")
+        f"{tokens_per_s:.0f} tokens/s; read probe {read_ceiling:.0f} GB/s "
+        f"({100 * achieved / read_ceiling:.1f}% of it)")
 
     traffic = measured_traffic(w.name, args.partition, kv_bytes)
     cpu = None
@@ -204,6 +233,8 @@ def main():
         "attention_us": attn_ms * 1e3,
         "kv_gbps": achieved,
         "kv_frac_of_peak": achieved / PEAK_HBM_GBPS,
+        "read_probe_gbps": read_ceiling,
+        "kv_frac_of_read_probe": achieved / read_ceiling,
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,

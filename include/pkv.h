@@ -41,7 +41,8 @@
  * Errors.  Every entry point returns a pkv_status. Host-checkable problems
  *   return a negative status before anything is enqueued; PKV_ERR_HIP means the
  *   HIP runtime rejected a launch. No C++ exception crosses this interface.
- * Threads.  No mutable global state: calls are reentrant.
+ * Threads.  Calls are reentrant. The only global state is a per-device cache
+ *   of the compute-unit count, filled on first use and thread-safe.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -105,13 +106,18 @@ PKV_API int pkv_copy_blocks(void* k_pool, void* v_pool,
                     int num_kv_heads, int head_dim, int block_size, int num_blocks,
                     pkv_dtype dtype, void* stream);
 
+/* partition_size value that selects the balanced schedule (see below). */
+#define PKV_PARTITION_BALANCED (-1)
+
 /*
  * Bytes of workspace pkv_paged_attention_decode needs for the given sizes and
  * partition_size (0 when it needs none: partition_size == 0, or every
- * sequence fits one partition). Returns 0 for invalid sizes as well.
+ * sequence fits one partition). Returns 0 for invalid sizes as well. For
+ * PKV_PARTITION_BALANCED the size depends only on head_dim and the head
+ * grouping: 2 * 4096 * (num_heads / num_kv_heads) * (head_dim + 2) * 4 bytes.
  */
-PKV_API size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, int head_dim,
-                                          int max_seq_len, int partition_size);
+PKV_API size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                          int head_dim, int max_seq_len, int partition_size);
 
 /*
  * Single-query decode attention through block tables ([summary] sections
@@ -132,10 +138,24 @@ PKV_API size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, i
  * max_seq_len must bound every seq_lens entry (it sizes the launch) and must
  * not exceed max_blocks_per_seq * block_size.
  *
- * partition_size == 0: one pass per (sequence, kv head). Otherwise a positive
- * multiple of 64: the tokens of each sequence are cut into partitions of that
- * many tokens, each handled independently, and merged by a log-sum-exp
- * reduce; `workspace` (16-byte aligned, at least
+ * partition_size selects how the tokens are split over the GPU's waves; the
+ * result is the same attention up to floating-point summation order:
+ *   0                       one pass per (sequence, kv head);
+ *   a positive multiple of 64
+ *                           each sequence is cut into partitions of that many
+ *                           tokens, handled independently and merged by a
+ *                           log-sum-exp reduce. Sequences next to each other
+ *                           in the batch are processed side by side, so
+ *                           blocks they share (parallel sampling) are read
+ *                           once from HBM and then from cache;
+ *   PKV_PARTITION_BALANCED  a fixed set of persistent waves (8 per compute
+ *                           unit, at most 4096) each takes an equal share of
+ *                           all tokens of the batch, whatever the lengths;
+ *                           pieces of a sequence split between waves are
+ *                           merged by a log-sum-exp reduce. The split points
+ *                           depend on the lengths of the whole batch, so a
+ *                           row's rounding can change when other rows change.
+ * When a split is possible, `workspace` (16-byte aligned, at least
  * pkv_paged_attention_workspace_size(...) bytes, contents ignored and
  * overwritten) holds the partial results. Work enqueued on `stream` by
  * different calls must not share a workspace unless ordered by the stream.

@@ -12,8 +12,11 @@ _API = (
     "paged_attention_decode",
     "paged_attention_workspace_size",
     "status_string",
+    "probe_read",
+    "probe_copy",
     "library",
     "DTYPE_CODES",
+    "PARTITION_BALANCED",
     "PkvError",
 )
 

@@ -43,13 +43,19 @@ def library() -> ctypes.CDLL:
     lib.pkv_kv_cache_append.restype = I
     lib.pkv_copy_blocks.argtypes = [P, P, P, I, I, I, I, I, I, P]
     lib.pkv_copy_blocks.restype = I
-    lib.pkv_paged_attention_workspace_size.argtypes = [I, I, I, I, I]
+    lib.pkv_paged_attention_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.pkv_paged_attention_workspace_size.restype = Z
     lib.pkv_paged_attention_decode.argtypes = [P, I, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I,
                                                P, Z, I, P]
     lib.pkv_paged_attention_decode.restype = I
     lib.pkv_status_string.argtypes = [I]
     lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_probe_read.argtypes = [P, Z, P, P]
+    lib.pkv_probe_read.restype = I
+    lib.pkv_probe_read_sink_words.argtypes = [Z]
+    lib.pkv_probe_read_sink_words.restype = Z
+    lib.pkv_probe_copy.argtypes = [P, P, Z, P]
+    lib.pkv_probe_copy.restype = I
     _lib = lib
     return lib
 
@@ -120,18 +126,25 @@ def copy_blocks(k_pool, v_pool, block_mapping, stream=None) -> None:
         _stream(stream)))
 
 
-def paged_attention_workspace_size(num_seqs, num_heads, head_dim, max_seq_len,
+PARTITION_BALANCED = -1     # PKV_PARTITION_BALANCED
+
+
+def paged_attention_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len,
                                    partition_size) -> int:
     """pkv_paged_attention_workspace_size, in bytes."""
     return int(library().pkv_paged_attention_workspace_size(
-        int(num_seqs), int(num_heads), int(head_dim), int(max_seq_len), int(partition_size)))
+        int(num_seqs), int(num_heads), int(num_kv_heads), int(head_dim), int(max_seq_len),
+        int(partition_size)))
 
 
 def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len, scale,
-                           partition_size=512, workspace=None, stream=None) -> torch.Tensor:
+                           partition_size=PARTITION_BALANCED, workspace=None,
+                           stream=None) -> torch.Tensor:
     """pkv_paged_attention_decode into `out` [B][H][D] (float32, float16 or
-    bfloat16). `workspace` (a uint8 device tensor) is allocated here when the
-    call needs one and none is given."""
+    bfloat16). partition_size: 0 (one pass per sequence), a multiple of 64
+    (fixed partitions) or PARTITION_BALANCED (the default). `workspace` (a
+    uint8 device tensor) is allocated here when the call needs one and none
+    is given."""
     nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
     if q.dim() != 3 or q.shape[2] != d or q.dtype != k_pool.dtype:
         raise ValueError("q must be [num_seqs][num_heads][head_dim] in the pool's dtype")
@@ -140,7 +153,7 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, max_s
         raise ValueError("out must be [num_seqs][num_heads][head_dim], float32/float16/bfloat16")
     if block_tables.dim() != 2 or block_tables.shape[0] != b or seq_lens.shape != (b,):
         raise ValueError("block_tables must be [num_seqs][max_blocks], seq_lens [num_seqs]")
-    need = paged_attention_workspace_size(b, h, d, max_seq_len, partition_size)
+    need = paged_attention_workspace_size(b, h, hkv, d, max_seq_len, partition_size)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else 0
@@ -152,3 +165,31 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, max_s
         b, h, hkv, d, bs, nb, float(scale), int(partition_size), ws_ptr, ws_bytes, code,
         _stream(stream)))
     return out
+
+
+# ----------------------------------------------------------- measurement probes
+# (include/pkv_probe.h: reference points for the memory system, not attention)
+
+def probe_read(src: torch.Tensor, sink: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """pkv_probe_read: stream every byte of `src` once. Returns the sink
+    (uint32 as int32 tensor), allocated here when not given."""
+    nbytes = src.numel() * src.element_size()
+    words = int(library().pkv_probe_read_sink_words(nbytes))
+    if words == 0:
+        raise ValueError("src must hold a positive multiple of 16 bytes")
+    if sink is None:
+        sink = torch.empty(words, dtype=torch.int32, device=src.device)
+    if sink.numel() < words:
+        raise ValueError(f"sink must hold {words} words")
+    _check("pkv_probe_read", library().pkv_probe_read(
+        _dev(src, "src"), nbytes, _dev(sink, "sink", torch.int32), _stream(stream)))
+    return sink
+
+
+def probe_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    """pkv_probe_copy: dst <- src, byte for byte (same byte size)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst and src must have the same byte size")
+    _check("pkv_probe_copy", library().pkv_probe_copy(
+        _dev(dst, "dst"), _dev(src, "src"), nbytes, _stream(stream)))

@@ -3,6 +3,8 @@
 
 #include <math.h>
 
+#include <atomic>
+
 #include "pkv_internal.hpp"
 
 namespace {
@@ -29,6 +31,26 @@ long long parts_for(int max_seq_len, int partition_size) {
 size_t workspace_bytes_for(long long rows, int head_dim, long long parts) {
     if (parts <= 1) return 0;
     return (size_t)(rows * parts) * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+size_t balanced_workspace_bytes(int group, int head_dim) {
+    return (size_t)2 * pkv::kMaxBalancedWaves * group * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+// Compute units of the current device, queried once per device.
+int compute_units() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return -1;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 }  // namespace
@@ -99,10 +121,13 @@ int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapping, in
     return pkv::launch_copy_blocks(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
-size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, int head_dim,
-                                          int max_seq_len, int partition_size) {
-    if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || partition_size < 0)
+size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                          int head_dim, int max_seq_len, int partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+        head_dim <= 0 || max_seq_len < 0 || partition_size < PKV_PARTITION_BALANCED)
         return 0;
+    if (partition_size == PKV_PARTITION_BALANCED)
+        return num_seqs > 0 ? balanced_workspace_bytes(num_heads / num_kv_heads, head_dim) : 0;
     return workspace_bytes_for((long long)num_seqs * num_heads, head_dim,
                                parts_for(max_seq_len, partition_size));
 }
@@ -116,10 +141,11 @@ int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
                                size_t workspace_bytes, pkv_dtype dtype, void* stream) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
-        partition_size < 0 || !valid_dtype(dtype) || !valid_dtype(out_dtype) || !isfinite(scale))
+        partition_size < PKV_PARTITION_BALANCED || !valid_dtype(dtype) ||
+        !valid_dtype(out_dtype) || !isfinite(scale))
         return PKV_ERR_INVALID;
     if (num_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
-    if (partition_size % 64 != 0) return PKV_ERR_INVALID;
+    if (partition_size > 0 && partition_size % 64 != 0) return PKV_ERR_INVALID;
     const int group = num_heads / num_kv_heads;
     if (!supported_head_dim(head_dim) || block_log2(block_size) < 0 ||
         !(group == 1 || group == 2 || group == 4 || group == 8))
@@ -130,20 +156,29 @@ int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
     if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens) return PKV_ERR_INVALID;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_INVALID;
     if ((long long)num_seqs * max_blocks_per_seq > INT32_MAX) return PKV_ERR_INVALID;
+    if ((long long)num_seqs * num_heads * head_dim > INT32_MAX) return PKV_ERR_INVALID;
 
-    const long long parts = parts_for(max_seq_len, partition_size);
-    const long long items = parts * num_seqs * num_kv_heads;
-    if (items > INT32_MAX - 64 || (long long)num_seqs * num_heads * head_dim > INT32_MAX)
-        return PKV_ERR_INVALID;
-    const size_t need = workspace_bytes_for((long long)num_seqs * num_heads, head_dim, parts);
+    const bool balanced = partition_size == PKV_PARTITION_BALANCED;
+    const long long parts = balanced ? 1 : parts_for(max_seq_len, partition_size);
+    long long items = parts * num_seqs * num_kv_heads;
+    if (items > INT32_MAX - 64) return PKV_ERR_INVALID;
+    const size_t need = balanced ? balanced_workspace_bytes(group, head_dim)
+                                 : workspace_bytes_for((long long)num_seqs * num_heads, head_dim, parts);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return PKV_ERR_WORKSPACE;
+    if (balanced) {
+        // the launch turns this into the persistent wave count
+        const int cus = compute_units();
+        if (cus <= 0) return PKV_ERR_HIP;
+        items = cus;
+    }
+    const size_t rows = need / ((size_t)(head_dim + 2) * sizeof(float));
 
     pkv::AttnParams a{};
     a.out = out;
     a.out_dtype = out_dtype;
     a.ws_acc = reinterpret_cast<float*>(workspace);
-    a.ws_ml = need ? a.ws_acc + (size_t)num_seqs * num_heads * parts * head_dim : nullptr;
+    a.ws_ml = need ? a.ws_acc + rows * head_dim : nullptr;
     a.q = q;
     a.k_pool = k_pool;
     a.v_pool = v_pool;
@@ -157,10 +192,11 @@ int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
     a.log2_bs = block_log2(block_size);
     a.num_blocks = num_blocks;
     a.scale = scale;
-    a.part_tokens = parts > 1 ? partition_size : 0;
+    a.part_tokens = (!balanced && parts > 1) ? partition_size : 0;
     a.max_parts = (int)parts;
     a.max_tokens = max_seq_len;
     a.num_items = (int)items;
+    a.balanced = balanced ? 1 : 0;
     a.dtype = dtype;
     return pkv::launch_paged_attention(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

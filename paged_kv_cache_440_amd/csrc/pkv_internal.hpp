@@ -13,8 +13,10 @@ namespace pkv {
 struct AttnParams {
     void* out;
     int out_dtype;
-    float* ws_acc;                 // [B][H][max_parts][D] unnormalised partial sums
-    float* ws_ml;                  // [B][H][max_parts][2] (running max in log2 units, sum)
+    float* ws_acc;                 // unnormalised partial sums, D floats per row:
+                                   // [B][H][max_parts] rows (fixed partitions) or
+                                   // [2 * kMaxBalancedWaves][G] rows (balanced)
+    float* ws_ml;                  // per row: running max in log2 units, sum
     const void* q;
     const void* k_pool;
     const void* v_pool;
@@ -31,9 +33,21 @@ struct AttnParams {
     int part_tokens;               // 0: one pass per sequence
     int max_parts;                 // partitions per sequence the launch covers
     int max_tokens;                // lengths are clamped to this
-    int num_items;                 // max_parts * num_seqs * num_kv_heads
+    int num_items;                 // waves launched: max_parts * num_seqs * num_kv_heads;
+                                   // balanced: the compute-unit count on entry to the
+                                   // launcher, the persistent wave count in the kernels
+    int balanced;                  // 1: balanced schedule (see attention.hip)
     int dtype;
 };
+
+// Persistent waves of the balanced schedule: kBalancedWavesPerCU per compute
+// unit (fewer if fewer fit), at most kMaxBalancedWaves (which sizes the
+// workspace).
+#ifndef PKV_BAL_WAVES_PER_CU
+#define PKV_BAL_WAVES_PER_CU 8
+#endif
+constexpr int kBalancedWavesPerCU = PKV_BAL_WAVES_PER_CU;
+constexpr int kMaxBalancedWaves = 4096;
 
 struct AppendParams {
     const void* k_new;

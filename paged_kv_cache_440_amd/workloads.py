@@ -124,9 +124,17 @@ def _draw_into(out: torch.Tensor, seed_seq: np.random.SeedSequence, dist: str) -
 
     if nchunks == 1:
         work(0)
-    else:
+        return
+    # one torch thread per worker: the conversions run inside the pool's
+    # threads, and torch's own intra-op threads on top of them oversubscribe
+    # the cores many times over
+    prev = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
         with ThreadPoolExecutor(_workers()) as ex:
             list(ex.map(work, range(nchunks)))
+    finally:
+        torch.set_num_threads(prev)
 
 
 def _small_draw(rng: np.random.Generator, shape, dtype, dist: str) -> torch.Tensor:

@@ -82,7 +82,7 @@ class Device:
                             self.lens)
         return w
 
-    def attention(self, partition_size=512, out_dtype=torch.float32, workspace=None):
+    def attention(self, partition_size=-1, out_dtype=torch.float32, workspace=None):
         w = self.w
         out = torch.empty(self.q.shape, dtype=out_dtype, device=self.q.device)
         pkv.paged_attention_decode(out, self.q, self.k_pool, self.v_pool, self.tables, self.lens,

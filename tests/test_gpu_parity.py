@@ -13,6 +13,7 @@ import pytest
 import torch
 
 from paged_kv_cache_440_amd import workloads as wl
+from paged_kv_cache_440_amd import PARTITION_BALANCED as BAL
 from tests.gpu_support import (TOL, Device, bits, expected_attention, expected_pools, max_err,
                                poison_unwritten_slots)
 
@@ -63,7 +64,7 @@ def test_copy_and_append_bit_exact(name):
     assert np.array_equal(bits(d.v_pool), vb)
 
 
-@pytest.mark.parametrize("partition", [0, 64, 512])
+@pytest.mark.parametrize("partition", [0, 64, 512, BAL])
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_attention_matches_oracle(name, partition):
     w = _small(name)
@@ -87,14 +88,15 @@ FULL = {
 }
 
 
+@pytest.mark.parametrize("partition", [512, BAL])
 @pytest.mark.parametrize("name", list(FULL))
-def test_full_size_matches_oracle(name):
-    """Full-size workloads, partitions of 512 tokens (the timed launch
-    configuration): pools bit-exact, every output within tolerance."""
+def test_full_size_matches_oracle(name, partition):
+    """Full-size workloads in both timed launch configurations (balanced, and
+    partitions of 512 tokens): pools bit-exact, every output within tolerance."""
     w = FULL[name]()
     d = Device(w)
     d.copy_and_append()
-    out = d.attention(partition_size=512)
+    out = d.attention(partition_size=partition)
     kb, vb = expected_pools(w)
     assert np.array_equal(bits(d.k_pool), kb) and np.array_equal(bits(d.v_pool), vb)
     del d
@@ -104,16 +106,17 @@ def test_full_size_matches_oracle(name):
 
 # ------------------------------------------------ invariants (bit-exact)
 
-def _run(w, partition=512):
+def _run(w, partition=BAL):
     d = Device(w)
     d.copy_and_append()
     return d.attention(partition_size=partition).cpu()
 
 
+@pytest.mark.parametrize("partition", [512, BAL])
 @pytest.mark.parametrize("name", ["tiny_fp32", "opt13b_fp16", "long_gqa_bf16_bs16"])
-def test_block_relabelling_is_bit_exact(name):
+def test_block_relabelling_is_bit_exact(name, partition):
     w = _small(name)
-    ref = _run(w)
+    ref = _run(w, partition)
     perm = np.random.default_rng(99).permutation(w.num_blocks)
     inv = np.argsort(perm)
     w2 = _small(name)
@@ -121,19 +124,20 @@ def test_block_relabelling_is_bit_exact(name):
     w2.v_pool = w2.v_pool[torch.from_numpy(perm)].contiguous()
     w2.block_tables = np.where(w2.block_tables >= 0, inv[np.maximum(w2.block_tables, 0)],
                                -1).astype(np.int32)
-    assert torch.equal(bits_t(_run(w2)), bits_t(ref))
+    assert torch.equal(bits_t(_run(w2, partition)), bits_t(ref))
 
 
 def bits_t(t):
     return t.view(torch.int32)
 
 
+@pytest.mark.parametrize("partition", [512, BAL])
 @pytest.mark.parametrize("name", ["tiny_fp32", "opt13b_fp16", "llama13b_bf16"])
-def test_contiguous_tables_give_identical_bits(name):
+def test_contiguous_tables_give_identical_bits(name, partition):
     """Each sequence's blocks copied, in logical order, to consecutive
     physical blocks (the layout of contiguous attention)."""
     w = _small(name)
-    ref = _run(w)
+    ref = _run(w, partition)
     w2 = _small(name)
     order = []
     tables = np.full_like(w2.block_tables, -1)
@@ -146,15 +150,16 @@ def test_contiguous_tables_give_identical_bits(name):
     w2.v_pool = w2.v_pool[idx].contiguous()
     w2.num_blocks = len(order)
     w2.block_tables = tables
-    assert torch.equal(bits_t(_run(w2)), bits_t(ref))
+    assert torch.equal(bits_t(_run(w2, partition)), bits_t(ref))
 
 
+@pytest.mark.parametrize("partition", [512, BAL])
 @pytest.mark.parametrize("name", ["shared_prefix_fp16", "shared_prefix_cow_fp16"])
-def test_shared_prefix_equals_private_copies(name):
+def test_shared_prefix_equals_private_copies(name, partition):
     """Aliased prefix blocks vs every sample holding its own copy: the same
     logical history, so identical output bits."""
     w = _small(name, poison=False)
-    ref = _run(w)
+    ref = _run(w, partition)
     w2 = _small(name, poison=False)
     full = w2.info["prefix_len"] // w2.block_size
     extra = []
@@ -171,10 +176,10 @@ def test_shared_prefix_equals_private_copies(name):
     w2.num_blocks = nxt
     w2.block_tables = tables
     assert len(set(tables[:, :full].ravel().tolist())) == w2.num_seqs * full
-    assert torch.equal(bits_t(_run(w2)), bits_t(ref))
+    assert torch.equal(bits_t(_run(w2, partition)), bits_t(ref))
 
 
-@pytest.mark.parametrize("partition", [0, 64])
+@pytest.mark.parametrize("partition", [0, 64, BAL])
 def test_runs_are_deterministic(partition):
     w = _small("llama13b_bf16")
     a = _run(w, partition)
@@ -265,7 +270,7 @@ def test_lengths_on_block_and_partition_boundaries():
     d.copy_and_append()
     kb, vb = expected_pools(w)
     ref = expected_attention(w, kb, vb)
-    for part in (0, 64, 512):
+    for part in (0, 64, 512, BAL):
         out = d.attention(partition_size=part)
         assert max_err(out, ref) <= TOL[w.dtype], part
 
@@ -280,4 +285,33 @@ def test_single_pass_over_more_than_64_blocks():
     d = Device(w)
     d.copy_and_append()
     out = d.attention(partition_size=0)
+    assert max_err(out, expected_attention(w, *expected_pools(w))) <= TOL[w.dtype]
+
+
+def test_balanced_runs_cross_many_segments():
+    """Balanced schedule with many short sequences, empty rows and a few long
+    ones: waves' runs start and end inside segments, and some runs hold many
+    whole segments."""
+    rng = np.random.default_rng(11)
+    lens = rng.integers(1, 40, size=150).tolist() + [0, 0, 3000, 777, 0, 4100, 1]
+    w = wl.build_independent("ragged", lens, dtype=torch.bfloat16, num_heads=8, num_kv_heads=2,
+                             head_dim=128, block_size=32, dist="normal", seed=12)
+    poison_unwritten_slots(w)
+    d = Device(w)
+    d.copy_and_append()
+    out = d.attention(partition_size=BAL)
+    ref = expected_attention(w, *expected_pools(w))
+    assert max_err(out, ref) <= TOL[w.dtype]
+    assert (out.cpu()[np.asarray(lens) == 0] == 0).all()
+
+
+def test_balanced_one_segment_over_many_waves():
+    """One long sequence and one kv head: the segment is cut into one run per
+    wave (32 tokens each) and merged from about a thousand records."""
+    w = wl.build_independent("one_long", [32768 - 5], dtype=torch.float16, num_heads=1,
+                             num_kv_heads=1, head_dim=64, block_size=64, dist="normal", seed=13)
+    poison_unwritten_slots(w)
+    d = Device(w)
+    d.copy_and_append()
+    out = d.attention(partition_size=BAL)
     assert max_err(out, expected_attention(w, *expected_pools(w))) <= TOL[w.dtype]
