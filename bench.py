@@ -90,6 +90,29 @@ def cpu_baseline(w):
                       f"attention step, float64 numpy, one thread, {dt:.1f} s wall"}
 
 
+def copy_probe(mib: int, reps: int) -> None:
+    """pkv_probe_copy over `mib` MiB, `reps` times: each dispatch reads and
+    writes exactly mib MiB, the reference for scaling FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    import paged_kv_cache_440_amd as pkv
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        pkv.probe_copy(dst, src, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    assert torch.equal(dst[:4096], src[:4096])
+    print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "dispatches": reps,
+                      "us_per_dispatch": us, "gbps_read_plus_write": 2 * n / us / 1e3}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +125,9 @@ def main():
                          "-1: balanced (default; 512 for the shared-prefix workloads, where "
                          "neighbouring sequences share blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run the plain copy probe over buffers of this many MiB "
+                         "(a transfer of known size for scaling traffic counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -112,6 +138,10 @@ def main():
     import torch
     import paged_kv_cache_440_amd as pkv
     from paged_kv_cache_440_amd import workloads as wl
+
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, args.steps)
+        return
 
     if args.partition is None:
         args.partition = 512 if args.workload.startswith("shared_prefix") else pkv_balanced()
