@@ -1,4 +1,5 @@
-// Paged single-query decode attention for gfx950.
+// Paged single-query decode attention for gfx950: schedules, reduce kernels
+// and dispatch.
 //
 // What is computed (supersilo.blog vLLM/PagedAttention summary, sections
 // "자기회귀 생성과 KV 캐시" and "PagedAttention의 설계"): for every sequence
@@ -8,8 +9,10 @@
 //
 // A segment is (sequence i, kv head g): the L_i tokens of one kv head, read
 // for the G query heads that share it. One wave64 walks a contiguous token
-// range of one segment at a time; workgroups hold kWaves independent waves
-// (no LDS, no barriers). Three schedules decide the ranges:
+// range of one segment at a time (a "walker": attn_vec.hpp on the vector
+// units, attn_mfma.hpp on the matrix cores for grouped-query attention);
+// workgroups hold kWaves independent waves (no LDS, no barriers). Three
+// schedules decide the ranges:
 //   single pass      one wave per segment (partition_size 0);
 //   fixed partitions one wave per (segment, partition of part_len tokens),
 //                    numbered g fastest, then i, then the partition; the
@@ -20,302 +23,28 @@
 //                    into 32-token units and laid end to end in (i, g) order,
 //                    are split into W equal runs, one per wave, so every wave
 //                    streams the same number of bytes whatever the lengths.
-// Partial results of split segments are merged by a log-sum-exp reduce.
-//
-// Lane layout inside a wave (for one 16-byte piece per lane and load)
-//   A token row of one kv head is D * eb bytes = LPT 16-byte pieces. Lane l
-//   holds piece (l % LPT) of token (l / LPT) of a TPL-token group, so one
-//   wave-wide 16-byte load reads TPL whole rows: 1 KB of consecutive bytes in
-//   one physical block (block_size is a multiple of TPL). A chunk is NLOAD
-//   such groups (CHUNK tokens); the next chunk's K and V are loaded before
-//   the current one is consumed.
-//
-// Softmax
-//   Scores are kept in the log2 domain (scale * log2(e) folded in). The lanes
-//   of token class c = l / LPT see tokens c, c + TPL, c + 2 TPL, ... of the
-//   range and keep their own running max m, sum l and unnormalised
-//   accumulator acc (online rescaling by exp2(m_old - m_new) whenever m
-//   grows). At the end of the range the TPL classes are merged with the
-//   log-sum-exp rule; the reduce kernel merges the ranges of a split segment
-//   the same way. Every merge and reduction order depends only on logical
-//   token positions and on the lengths of the batch, so relabelling physical
-//   blocks or aliasing them changes no output bit.
-//
-// Masking
-//   Only the last chunk of a range can hold tokens at or past its end; there
-//   scores are replaced by -inf and values by 0 through selects, so stale
-//   slot contents (NaN included) never reach the result.
+// Partial results of split segments are merged by a log-sum-exp reduce. Every
+// merge and reduction order depends only on logical token positions and on
+// the lengths of the batch, so relabelling physical blocks or aliasing them
+// changes no output bit.
 
 #include <atomic>
 
-#include "pkv_device.hpp"
-#include "pkv_internal.hpp"
+#include "attn_common.hpp"
+#include "attn_mfma.hpp"
+#include "attn_vec.hpp"
 
 namespace pkv {
 
 namespace {
 
-#ifndef PKV_ATTN_WAVES
-#define PKV_ATTN_WAVES 4
-#endif
-#ifndef PKV_ATTN_NLOAD
-#define PKV_ATTN_NLOAD 4
-#endif
-constexpr int kWaves = PKV_ATTN_WAVES;          // independent waves per workgroup
-constexpr float kLog2e = 1.4426950408889634f;
-
-template <typename S, int D>
-struct Geo {
-    static constexpr int EB = S::bytes;
-    static constexpr int ROW = D * EB;          // bytes of one token row of one kv head
-    static constexpr int LPT = ROW / 16;        // lanes per token row
-    static constexpr int TPL = 64 / LPT;        // tokens per wave-wide load
-    static constexpr int NLOAD = PKV_ATTN_NLOAD;  // loads of K (and of V) per chunk
-    static constexpr int CHUNK = TPL * NLOAD;   // tokens per chunk
-    static constexpr int EPL = 16 / EB;         // elements per lane per load
-    static_assert(LPT >= 8 && LPT <= 32, "row must span 8..32 lanes");
-};
-
-template <typename S, int D, int G>
-struct Attn {
-    using Gm = Geo<S, D>;
-    static constexpr int LPT = Gm::LPT, TPL = Gm::TPL, NLOAD = Gm::NLOAD;
-    static constexpr int CHUNK = Gm::CHUNK, EPL = Gm::EPL;
-
-    // per-lane running state for G query heads
-    float m[G], l[G], acc[G][EPL];
-    u32x4 qv[G];
-
-    // block table window: lane j holds the physical id of logical block wb + j
-    int wb, tv;
-
-    const char* kbase;
-    const char* vbase;
-    const int* trow;
-    size_t head_stride_bytes;   // bytes from one physical block to the next
-    size_t kvhead_off;          // bytes of kv head g inside a block
-    int log2_bs, bs_mask, nblk_valid, max_phys;
-    int lane, tok, piece;
-    int t_end, last_group;
-
-    // Load the table entries of logical blocks wb .. wb + 63 (one per lane).
-    // Called only between pipelined walks: a load issued inside the walk
-    // would make every later table lookup wait for all loads in flight.
-    __device__ __forceinline__ void load_window(int first_block) {
-        wb = first_block;
-        tv = (wb + lane < nblk_valid) ? trow[wb + lane] : 0;
-    }
-
-    // physical block of logical block blk (wave-uniform, inside the window)
-    __device__ __forceinline__ uint32_t phys(int blk) {
-        uint32_t p = (uint32_t)__builtin_amdgcn_readlane(tv, blk - wb);
-        return p < (uint32_t)max_phys ? p : (uint32_t)(max_phys - 1);
-    }
-
-    __device__ __forceinline__ void load_chunk(int c0, u32x4 (&kr)[NLOAD], u32x4 (&vr)[NLOAD]) {
-#pragma unroll
-        for (int j = 0; j < NLOAD; ++j) {
-            int tg = c0 + j * TPL;
-            tg = tg < last_group ? tg : last_group;   // a group past the end re-reads the last one
-            const uint32_t p = phys(tg >> log2_bs);
-            const size_t blk_off = (size_t)p * head_stride_bytes + kvhead_off;
-            const uint32_t off = (uint32_t)(((tg & bs_mask) + tok) * Gm::ROW + piece * 16);
-            kr[j] = load16(kbase + blk_off + off);
-            vr[j] = load16(vbase + blk_off + off);
-        }
-    }
-
-    template <bool TAIL>
-    __device__ __forceinline__ void consume(int c0, const u32x4 (&kr)[NLOAD],
-                                            const u32x4 (&vr)[NLOAD], float scale_log2) {
-        bool valid[NLOAD];
-#pragma unroll
-        for (int j = 0; j < NLOAD; ++j) valid[j] = !TAIL || (c0 + j * TPL + tok < t_end);
-
-        float vf[NLOAD][EPL];
-#pragma unroll
-        for (int j = 0; j < NLOAD; ++j) {
-            Piece<S>::widen(vr[j], vf[j]);
-            if constexpr (TAIL) {
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) vf[j][e] = valid[j] ? vf[j][e] : 0.f;
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float s[NLOAD];
-#pragma unroll
-            for (int j = 0; j < NLOAD; ++j) {
-                s[j] = group_sum<LPT>(dot16(S{}, qv[h], kr[j])) * scale_log2;
-                if constexpr (TAIL) s[j] = valid[j] ? s[j] : -__builtin_inff();
-            }
-            float mx = m[h];
-#pragma unroll
-            for (int j = 0; j < NLOAD; ++j) mx = __builtin_fmaxf(mx, s[j]);
-            // Outside the tail every token is valid, so mx is finite. In the tail a
-            // class may have seen no valid token at all: then m = mx = -inf, every
-            // p is 0 and alpha (1) only multiplies zeros.
-            const float alpha = (TAIL && mx == -__builtin_inff()) ? 1.f : fast_exp2(m[h] - mx);
-            float p[NLOAD], ps = 0.f;
-#pragma unroll
-            for (int j = 0; j < NLOAD; ++j) {
-                p[j] = (TAIL && !valid[j]) ? 0.f : fast_exp2(s[j] - mx);
-                ps += p[j];
-            }
-            l[h] = l[h] * alpha + ps;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                float a = acc[h][e] * alpha;
-#pragma unroll
-                for (int j = 0; j < NLOAD; ++j) a = __builtin_fmaf(p[j], vf[j][e], a);
-                acc[h][e] = a;
-            }
-            m[h] = mx;
-        }
-    }
-
-    // -- one range of one segment --------------------------------------------
-
-    // Point the state at segment (seq, g) of length L and reset it.
-    __device__ __forceinline__ void begin(const AttnParams& a, int seq, int g, int L) {
-        log2_bs = a.log2_bs;
-        bs_mask = (1 << a.log2_bs) - 1;
-        nblk_valid = (L + bs_mask) >> a.log2_bs;
-        max_phys = a.num_blocks;
-        trow = a.block_tables + (size_t)seq * a.max_blocks;
-        head_stride_bytes = (size_t)a.num_kv_heads * ((size_t)Gm::ROW << a.log2_bs);
-        kvhead_off = (size_t)g * ((size_t)Gm::ROW << a.log2_bs);
-        kbase = reinterpret_cast<const char*>(a.k_pool);
-        vbase = reinterpret_cast<const char*>(a.v_pool);
-        const char* qrow = reinterpret_cast<const char*>(a.q) +
-                           ((size_t)seq * a.num_kv_heads * G + (size_t)g * G) * Gm::ROW + piece * 16;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            qv[h] = load16(qrow + (size_t)h * Gm::ROW);
-            m[h] = -__builtin_inff();
-            l[h] = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-        }
-    }
-
-    // Consume tokens [t_begin, t_stop) of the segment (t_begin a multiple of
-    // 32). The walk goes one table window (64 blocks) at a time; inside a
-    // window it is software-pipelined. Window ends fall on block boundaries,
-    // which are multiples of CHUNK past t_begin, so no chunk crosses one.
-    __device__ __forceinline__ void walk(int t_begin, int t_stop, float scale_log2) {
-        u32x4 k0[NLOAD], v0[NLOAD], k1[NLOAD], v1[NLOAD];
-        for (int w0 = t_begin; w0 < t_stop;) {
-            const int first_block = w0 >> log2_bs;
-            const int win_end = (first_block + 64) << log2_bs;
-            const int w_end = win_end < t_stop ? win_end : t_stop;
-            load_window(first_block);
-            t_end = w_end;
-            last_group = ((w_end - 1) / TPL) * TPL;
-            int c = w0;
-            load_chunk(c, k0, v0);
-            for (;;) {
-                const int n1 = c + CHUNK;
-                if (n1 >= w_end) { consume<true>(c, k0, v0, scale_log2); break; }
-                load_chunk(n1, k1, v1);
-                consume<false>(c, k0, v0, scale_log2);
-                const int n2 = n1 + CHUNK;
-                if (n2 >= w_end) { consume<true>(n1, k1, v1, scale_log2); break; }
-                load_chunk(n2, k0, v0);
-                consume<false>(n1, k1, v1, scale_log2);
-                c = n2;
-            }
-            w0 = w_end;
-        }
-    }
-
-    // Merge the TPL token classes (lanes LPT apart) of head h with the
-    // log-sum-exp rule: returns the range's max and sum, and leaves the merged
-    // unnormalised accumulator in acc[h] (valid on every lane of a class).
-    __device__ __forceinline__ void merge_classes(int h, float& mall, float& lsum) {
-        mall = strided_max<LPT>(m[h]);
-        const float w = (m[h] == -__builtin_inff()) ? 0.f : fast_exp2(m[h] - mall);
-        lsum = strided_sum<LPT>(l[h] * w);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = strided_sum<LPT>(acc[h][e] * w);
-    }
-};
-
-__device__ __forceinline__ void store_out(void* out, int out_dtype, size_t idx, float v) {
-    if (out_dtype == PKV_F32) {
-        reinterpret_cast<float*>(out)[idx] = v;
-    } else if (out_dtype == PKV_F16) {
-        reinterpret_cast<_Float16*>(out)[idx] = (_Float16)v;
-    } else {
-        reinterpret_cast<__bf16*>(out)[idx] = (__bf16)v;
-    }
-}
-
-__device__ __forceinline__ int clamp_len(const AttnParams& a, int L) {
-    L = L < 0 ? 0 : L;
-    return L < a.max_tokens ? L : a.max_tokens;
-}
-
-// Write the finished segment (seq, g): out = acc / l for its G heads.
-template <typename S, int D, int G>
-__device__ __forceinline__ void write_final(Attn<S, D, G>& st, const AttnParams& a, int seq, int g) {
-    constexpr int EPL = Attn<S, D, G>::EPL;
-    const size_t row0 = (size_t)seq * a.num_kv_heads * G + (size_t)g * G;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float mall, lsum;
-        st.merge_classes(h, mall, lsum);
-        const float inv = 1.0f / lsum;
-        if (st.tok == 0) {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                store_out(a.out, a.out_dtype, (row0 + h) * D + st.piece * EPL + e,
-                             st.acc[h][e] * inv);
-        }
-    }
-}
-
-// Write a partial result of G heads: unnormalised acc to rows
-// ws_acc[row0 + h], (max, sum) to ws_ml[row0 + h].
-template <typename S, int D, int G>
-__device__ __forceinline__ void write_partial(Attn<S, D, G>& st, const AttnParams& a,
-                                              size_t row0, size_t row_stride) {
-    constexpr int EPL = Attn<S, D, G>::EPL;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float mall, lsum;
-        st.merge_classes(h, mall, lsum);
-        const size_t row = row0 + (size_t)h * row_stride;
-        if (st.tok == 0) {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) a.ws_acc[row * D + st.piece * EPL + e] = st.acc[h][e];
-        }
-        if (st.lane == 0) {
-            a.ws_ml[2 * row] = mall;
-            a.ws_ml[2 * row + 1] = lsum;
-        }
-    }
-}
-
-template <typename S, int D, int G>
-__device__ __forceinline__ void write_zero_rows(const AttnParams& a, int seq, int g, int lane) {
-    constexpr int LPT = Geo<S, D>::LPT, EPL = Geo<S, D>::EPL;
-    if (lane >= LPT) return;
-    const size_t row0 = (size_t)seq * a.num_kv_heads * G + (size_t)g * G;
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-            store_out(a.out, a.out_dtype, (row0 + h) * D + lane * EPL + e, 0.f);
-}
-
 // ---------------------------------------------------------------------------
 // Single pass and fixed partitions: one wave per (segment, partition).
 // Partial rows: ws_acc[((seq * H + h) * max_parts + part)], the same for ws_ml.
-template <typename S, int D, int G>
+template <class Walker>
 __global__ __launch_bounds__(64 * kWaves)
 void paged_decode_kernel(const AttnParams a) {
-    using A = Attn<S, D, G>;
+    constexpr int D = Walker::D, G = Walker::G;
     const int lane = threadIdx.x & 63;
     // the wave index is uniform; say so, so that item-derived values live in SGPRs
     const int item = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -327,7 +56,7 @@ void paged_decode_kernel(const AttnParams a) {
 
     const int L = clamp_len(a, a.seq_lens[seq]);
     if (L == 0) {                                   // padding row: zero output
-        if (part == 0) write_zero_rows<S, D, G>(a, seq, g, lane);
+        if (part == 0) write_zero_rows<D, G>(a, seq, g, lane);
         return;
     }
     const int part_len = a.part_tokens > 0 ? a.part_tokens : L;
@@ -336,17 +65,15 @@ void paged_decode_kernel(const AttnParams a) {
     const int t_begin = part * part_len;
     const int t_stop = (t_begin + part_len < L) ? t_begin + part_len : L;
 
-    A st;
-    st.lane = lane;
-    st.tok = lane / A::LPT;
-    st.piece = lane % A::LPT;
+    Walker st;
+    st.init(lane);
     st.begin(a, seq, g, L);
     st.walk(t_begin, t_stop, a.scale * kLog2e);
     if (nparts == 1) {
-        write_final(st, a, seq, g);
+        st.write_final(a, seq, g);
     } else {
         const size_t row0 = ((size_t)seq * a.num_kv_heads * G + (size_t)g * G) * a.max_parts + part;
-        write_partial(st, a, row0, (size_t)a.max_parts);
+        st.write_partial(a, row0, (size_t)a.max_parts);
     }
 }
 
@@ -429,10 +156,10 @@ __device__ __forceinline__ long long units_before(const AttnParams& a, int end) 
     return total * a.num_kv_heads;
 }
 
-template <typename S, int D, int G>
+template <class Walker>
 __global__ __launch_bounds__(64 * kWaves)
 void paged_decode_balanced_kernel(const AttnParams a) {
-    using A = Attn<S, D, G>;
+    constexpr int G = Walker::G;
     const int lane = threadIdx.x & 63;
     const int w = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w >= a.num_items) return;
@@ -461,10 +188,8 @@ void paged_decode_balanced_kernel(const AttnParams a) {
         base += __shfl(incl, 63, 64);
     }
 
-    A st;
-    st.lane = lane;
-    st.tok = lane / A::LPT;
-    st.piece = lane % A::LPT;
+    Walker st;
+    st.init(lane);
     const float scale_log2 = a.scale * kLog2e;
     long long u = u0;
     while (u < u1 && seq < a.num_seqs) {
@@ -480,10 +205,10 @@ void paged_decode_balanced_kernel(const AttnParams a) {
         st.begin(a, seq, g, L);
         st.walk(k0 * kUnit, t_stop, scale_log2);
         if (k0 == 0 && k1 == nu) {
-            write_final(st, a, seq, g);
+            st.write_final(a, seq, g);
         } else {
             const size_t rec = 2 * (size_t)w + (k0 == 0 ? 1 : 0);
-            write_partial(st, a, rec * G, 1);
+            st.write_partial(a, rec * G, 1);
         }
         u = seg0 + k1;
         if (g == a.num_kv_heads - 1 && u == seg1) {
@@ -545,16 +270,16 @@ void balanced_reduce_kernel(const AttnParams a) {
         store_out(a.out, a.out_dtype, (size_t)item * D + lane + 64 * e, o[e] * inv);
 }
 
-// Waves of the balanced kernel instance that fit on one compute unit at once
+// Waves of a balanced kernel instance that fit on one compute unit at once
 // (register-limited), queried once per instance.
-template <typename S, int D, int G>
+template <class Walker>
 int balanced_resident_waves_per_cu() {
     static std::atomic<int> cached{0};
     int v = cached.load(std::memory_order_relaxed);
     if (v > 0) return v;
     int groups = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &groups, reinterpret_cast<const void*>(&paged_decode_balanced_kernel<S, D, G>),
+            &groups, reinterpret_cast<const void*>(&paged_decode_balanced_kernel<Walker>),
             64 * kWaves, 0) != hipSuccess || groups <= 0)
         return -1;
     v = groups * kWaves;
@@ -562,14 +287,15 @@ int balanced_resident_waves_per_cu() {
     return v;
 }
 
-template <typename S, int D, int G>
-hipError_t launch_typed(const AttnParams& a_in, hipStream_t stream) {
+template <class Walker>
+hipError_t launch_walker(const AttnParams& a_in, hipStream_t stream) {
+    constexpr int D = Walker::D, G = Walker::G;
     AttnParams a = a_in;
     if (a.balanced) {
         // a.num_items holds the compute-unit count; launch at most as many
         // persistent waves as are resident together, so that all of them
         // start at once and finish together
-        const int resident = balanced_resident_waves_per_cu<S, D, G>();
+        const int resident = balanced_resident_waves_per_cu<Walker>();
         if (resident <= 0) return hipErrorInvalidValue;
         const int per_cu = resident < kBalancedWavesPerCU ? resident : kBalancedWavesPerCU;
         const long long w = (long long)a.num_items * per_cu;
@@ -578,20 +304,29 @@ hipError_t launch_typed(const AttnParams& a_in, hipStream_t stream) {
     const int blocks = (a.num_items + kWaves - 1) / kWaves;
     const int rblocks = (a.num_seqs * a.num_kv_heads * G + kWaves - 1) / kWaves;
     if (a.balanced) {
-        hipLaunchKernelGGL((paged_decode_balanced_kernel<S, D, G>), dim3(blocks),
-                           dim3(64 * kWaves), 0, stream, a);
+        hipLaunchKernelGGL((paged_decode_balanced_kernel<Walker>), dim3(blocks), dim3(64 * kWaves),
+                           0, stream, a);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL((balanced_reduce_kernel<D>), dim3(rblocks), dim3(64 * kWaves), 0,
                            stream, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((paged_decode_kernel<S, D, G>), dim3(blocks), dim3(64 * kWaves), 0,
-                       stream, a);
+    hipLaunchKernelGGL((paged_decode_kernel<Walker>), dim3(blocks), dim3(64 * kWaves), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.max_parts <= 1) return err;
     hipLaunchKernelGGL((lse_reduce_kernel<D>), dim3(rblocks), dim3(64 * kWaves), 0, stream, a);
     return hipGetLastError();
+}
+
+// Matrix cores for 16-bit K/V with head_dim 128 and 4 or 8 query heads per
+// kv head; the vector walker otherwise.
+template <typename S, int D, int G>
+hipError_t launch_typed(const AttnParams& a, hipStream_t stream) {
+    if constexpr (S::bytes == 2 && D == 128 && (G == 4 || G == 8))
+        return launch_walker<MfmaWalker<S, G>>(a, stream);
+    else
+        return launch_walker<VecWalker<S, D, G>>(a, stream);
 }
 
 template <typename S, int D>

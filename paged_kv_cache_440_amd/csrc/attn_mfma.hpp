@@ -1,0 +1,281 @@
+// Matrix-core walker for paged decode attention (gfx950), for grouped-query
+// attention: 4 or 8 query heads share each kv head, 16-bit K/V, head_dim 128.
+// With G query heads per kv head every K/V byte feeds 2G flops; on the vector
+// units that is ALU-bound for G = 8, so both contractions of a 32-token chunk
+// run as v_mfma_f32_16x16x32_{bf16,f16} (fp32 accumulation):
+//
+//   S^T = K . Q^T     M = 16 tokens (two tiles), N = 16 query heads (G real,
+//                     the rest zero), K = 128 dims in four steps of 32.
+//   O^T += V^T . P^T  M = 16 dims (eight tiles), N = 16 query heads,
+//                     K = the chunk's 32 tokens.
+//
+// Operand layouts (16x16x32): lane l, with n = l % 16 and q = l / 16, holds
+// row n of A and column n of B for the 8 k-slots of group q; the 16x16
+// result holds rows 4q .. 4q+3 of column n. The order of the k-slots inside
+// a contraction is free as long as A and B agree, and the rows of V^T may be
+// any permutation of the dims as long as the output is written accordingly:
+//   * QK, step s: k-slots of group q are dims 32s + 8q .. +7, i.e. 16 bytes
+//     at byte 64s + 16q of a token row -- K rows (A) and q rows (B) load
+//     straight from memory;
+//   * the S^T result gives lane (n, q) head n's scores of tokens 4q + i
+//     (tile 0) and 16 + 4q + i (tile 1), i = 0..3. These eight tokens, in
+//     that order, are the k-slots of group q of PV, so P^T (B) is the
+//     lane's own softmax weights, no data movement;
+//   * V^T (A) row n of dim tile c is dim 8n + c. Lane (n, q) loads the 16
+//     bytes at dims 8n .. 8n+7 of each of its eight tokens (each wave load
+//     covers four whole 256-byte rows) and transposes that 8x8 block of
+//     16-bit values in registers: element c of the eight pieces forms the
+//     operand of tile c;
+//   * O^T tile c, row 4q + i, column n is head n, dim 8(4q + i) + c: lane
+//     (n, q) ends with dims 32q .. 32q+31 of head n.
+// The softmax of head n lives in the four lanes n, n+16, n+32, n+48: the
+// chunk max is combined across them (permlane swaps), each keeps a partial
+// sum, and the sums are added once at the end. P enters the matrix core as a
+// 16-bit high part plus a 16-bit residual, two products per tile, so the
+// weights keep about 16 significant bits.
+//
+// Masking: tokens at or past the range end (tail chunk only) get score -inf
+// and their V pieces are zeroed by select before the products.
+#pragma once
+
+#include "attn_common.hpp"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(BF16, const u32x4& a, const u32x4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x32(F16, const u32x4& a, const u32x4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// fp32 -> 16-bit (round to nearest even), as the low bits of a dword
+__device__ __forceinline__ uint32_t to16(BF16, float x) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
+__device__ __forceinline__ uint32_t to16(F16, float x) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ __forceinline__ float from16(BF16, uint32_t h) { return u2f(h << 16); }
+__device__ __forceinline__ float from16(F16, uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+template <typename S, int G_>
+struct MfmaWalker {
+    static constexpr int D = 128, G = G_;
+    static constexpr int ROW = 256;             // bytes of one token row of one kv head
+    static constexpr int CHUNK = 32;            // tokens per chunk
+    static_assert(S::bytes == 2 && G_ <= 16, "16-bit K/V, at most 16 query heads");
+
+    f32x4 acc[8];       // O^T tiles: acc[c][i] = head n, dim 32q + 8i + c (unnormalised)
+    float m, l;         // head n: running max (log2 units), this lane's partial sum
+    u32x4 qb[4];        // B operand of Q^T for the four k-steps
+
+    int wb, tv;         // table window: lane j holds the physical id of block wb + j
+    const char* kbase;
+    const char* vbase;
+    const int* trow;
+    size_t head_stride_bytes;
+    size_t kvhead_off;
+    int log2_bs, bs_mask, nblk_valid, max_phys;
+    int lane, n, q;
+    int t_end;
+
+    __device__ __forceinline__ void init(int lane_id) {
+        lane = lane_id;
+        n = lane_id & 15;
+        q = lane_id >> 4;
+    }
+
+    __device__ __forceinline__ void begin(const AttnParams& a, int seq, int g, int L) {
+        log2_bs = a.log2_bs;
+        bs_mask = (1 << a.log2_bs) - 1;
+        nblk_valid = (L + bs_mask) >> a.log2_bs;
+        max_phys = a.num_blocks;
+        trow = a.block_tables + (size_t)seq * a.max_blocks;
+        head_stride_bytes = (size_t)a.num_kv_heads * ((size_t)ROW << a.log2_bs);
+        kvhead_off = (size_t)g * ((size_t)ROW << a.log2_bs);
+        kbase = reinterpret_cast<const char*>(a.k_pool);
+        vbase = reinterpret_cast<const char*>(a.v_pool);
+        const char* qrow = reinterpret_cast<const char*>(a.q) +
+                           ((size_t)seq * a.num_kv_heads * G + (size_t)g * G + n) * ROW + 16 * q;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            qb[s] = n < G ? load16(qrow + 64 * s) : u32x4{0u, 0u, 0u, 0u};
+        m = -__builtin_inff();
+        l = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    __device__ __forceinline__ void load_window(int first_block) {
+        wb = first_block;
+        tv = (wb + lane < nblk_valid) ? trow[wb + lane] : 0;
+    }
+
+    // physical block of window block blk (per lane, 0 <= blk < 64)
+    __device__ __forceinline__ uint32_t phys(int blk) {
+        const uint32_t p = (uint32_t)__builtin_amdgcn_ds_bpermute(blk << 2, tv);
+        return p < (uint32_t)max_phys ? p : (uint32_t)(max_phys - 1);
+    }
+
+    // K: kt[t][s] = row (c0 + 16t + n), bytes 64s + 16q .. +15.
+    __device__ __forceinline__ void load_k(int c0, u32x4 (&kt)[2][4]) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int tok = c0 + 16 * t + n;
+            const char* p = kbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes +
+                            kvhead_off + (uint32_t)((tok & bs_mask) * ROW + 16 * q);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) kt[t][s] = load16(p + 64 * s);
+        }
+    }
+
+    // V: vt[4h + j] = row (c0 + 16h + 4q + j), bytes 16n .. 16n+15. Four
+    // aligned consecutive tokens never straddle a block (bs >= 8).
+    __device__ __forceinline__ void load_v(int c0, u32x4 (&vt)[8]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int tok = c0 + 16 * h + 4 * q;
+            const char* p = vbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes +
+                            kvhead_off + (uint32_t)((tok & bs_mask) * ROW + 16 * n);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vt[4 * h + j] = load16(p + ROW * j);
+        }
+    }
+
+    // Scores of the chunk: k-slot j of group q is token 16 (j / 4) + 4q + j % 4.
+    __device__ __forceinline__ void scores(const u32x4 (&kt)[2][4], float scale_log2,
+                                           float (&sc)[8]) {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            s0 = mfma_16x16x32(S{}, kt[0][s], qb[s], s0);
+            s1 = mfma_16x16x32(S{}, kt[1][s], qb[s], s1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sc[i] = s0[i] * scale_log2;
+            sc[4 + i] = s1[i] * scale_log2;
+        }
+    }
+
+    template <bool TAIL>
+    __device__ __forceinline__ void softmax_pv(int c0, float (&sc)[8], u32x4 (&vt)[8]) {
+        if constexpr (TAIL) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const bool valid = c0 + 16 * (j >> 2) + 4 * q + (j & 3) < t_end;
+                sc[j] = valid ? sc[j] : -__builtin_inff();
+#pragma unroll
+                for (int w = 0; w < 4; ++w) vt[j][w] = valid ? vt[j][w] : 0u;
+            }
+        }
+        float mx = sc[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = __builtin_fmaxf(mx, sc[j]);
+        mx = strided_max<16>(mx);
+        // Token c0 is always valid (q = 0, j = 0), so mx is finite.
+        const float m_new = __builtin_fmaxf(m, mx);
+        const float alpha = fast_exp2(m - m_new);
+        float p[8], ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = fast_exp2(sc[j] - m_new);
+            ps += p[j];
+        }
+        l = l * alpha + ps;
+        m = m_new;
+        // P^T as a 16-bit high part and the 16-bit residual
+        u32x4 bhi, blo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t h0 = to16(S{}, p[2 * w]), h1 = to16(S{}, p[2 * w + 1]);
+            const uint32_t r0 = to16(S{}, p[2 * w] - from16(S{}, h0));
+            const uint32_t r1 = to16(S{}, p[2 * w + 1] - from16(S{}, h1));
+            bhi[w] = h0 | (h1 << 16);
+            blo[w] = r0 | (r1 << 16);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            // V^T tile c: element c of the eight V pieces, token order as k-slots
+            u32x4 av;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t x = vt[2 * w][c >> 1], y = vt[2 * w + 1][c >> 1];
+                av[w] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+            }
+            f32x4 o = acc[c] * alpha;
+            o = mfma_16x16x32(S{}, av, bhi, o);
+            acc[c] = mfma_16x16x32(S{}, av, blo, o);
+        }
+    }
+
+    // One buffer each for K and V: the next chunk's K is requested as soon as
+    // the scores have consumed this chunk's K, the next V as soon as the
+    // products have consumed this V, so about one chunk stays in flight per
+    // wave with half the registers of a double buffer (two waves per SIMD).
+    __device__ __forceinline__ void walk(int t_begin, int t_stop, float scale_log2) {
+        u32x4 kt[2][4], vt[8];
+        float sc[8];
+        for (int w0 = t_begin; w0 < t_stop;) {
+            const int first_block = w0 >> log2_bs;
+            const int win_end = (first_block + 64) << log2_bs;
+            const int w_end = win_end < t_stop ? win_end : t_stop;
+            load_window(first_block);
+            t_end = w_end;
+            int c = w0;
+            load_k(c, kt);
+            load_v(c, vt);
+            for (;;) {
+                const int nx = c + CHUNK;
+                scores(kt, scale_log2, sc);
+                if (nx >= w_end) { softmax_pv<true>(c, sc, vt); break; }
+                load_k(nx, kt);
+                softmax_pv<false>(c, sc, vt);
+                load_v(nx, vt);
+                c = nx;
+            }
+            w0 = w_end;
+        }
+    }
+
+    __device__ __forceinline__ float total_sum() { return strided_sum<16>(l); }
+
+    __device__ __forceinline__ void write_final(const AttnParams& a, int seq, int g) {
+        const float inv = 1.0f / total_sum();
+        if (n >= G) return;
+        const size_t base = ((size_t)seq * a.num_kv_heads * G + (size_t)g * G + n) * D + 32 * q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) store_out(a.out, a.out_dtype, base + 8 * i + c, acc[c][i] * inv);
+    }
+
+    __device__ __forceinline__ void write_partial(const AttnParams& a, size_t row0,
+                                                  size_t row_stride) {
+        const float lsum = total_sum();
+        if (n >= G) return;
+        const size_t row = row0 + (size_t)n * row_stride;
+        float* dst = a.ws_acc + row * D + 32 * q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) dst[8 * i + c] = acc[c][i];
+        if (q == 0) {
+            a.ws_ml[2 * row] = m;
+            a.ws_ml[2 * row + 1] = lsum;
+        }
+    }
+};
+
+}  // namespace
+}  // namespace pkv

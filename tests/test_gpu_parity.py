@@ -315,3 +315,29 @@ def test_balanced_one_segment_over_many_waves():
     d.copy_and_append()
     out = d.attention(partition_size=BAL)
     assert max_err(out, expected_attention(w, *expected_pools(w))) <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("partition", [0, 64, BAL])
+@pytest.mark.parametrize("dtype,head_dim,group,block_size", [
+    (torch.bfloat16, 128, 8, 16),      # matrix-core walker
+    (torch.float16, 128, 8, 8),        # matrix-core walker, fp16, 8-token blocks
+    (torch.float16, 128, 4, 32),       # matrix-core walker, 4 query heads per kv head
+    (torch.bfloat16, 128, 2, 16),      # vector walker
+    (torch.float16, 64, 8, 16),        # vector walker, head_dim 64
+    (torch.float32, 128, 4, 64),       # vector walker, fp32
+])
+def test_grouped_query_walkers(dtype, head_dim, group, block_size, partition):
+    """Both walkers over grouped-query shapes, with lengths that end on and
+    next to chunk and block boundaries (1, 2, 31, 32, 33, ...), where few
+    tokens carry all the softmax weight."""
+    lens = [1, 2, 3, 31, 32, 33, 63, 100, 129, 700, 1000]
+    hkv = 2
+    w = wl.build_independent("gqa", lens, dtype=dtype, num_heads=hkv * group, num_kv_heads=hkv,
+                             head_dim=head_dim, block_size=block_size, dist="normal", seed=21)
+    poison_unwritten_slots(w)
+    d = Device(w)
+    d.copy_and_append()
+    out = d.attention(partition_size=partition)
+    assert torch.isfinite(out).all()
+    ref = expected_attention(w, *expected_pools(w))
+    assert max_err(out, ref) <= TOL[w.dtype], f"max abs error {max_err(out, ref):.3e}"
