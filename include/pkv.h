@@ -114,7 +114,8 @@ PKV_API int pkv_copy_blocks(void* k_pool, void* v_pool,
  * partition_size (0 when it needs none: partition_size == 0, or every
  * sequence fits one partition). Returns 0 for invalid sizes as well. For
  * PKV_PARTITION_BALANCED the size depends only on head_dim and the head
- * grouping: 2 * 4096 * (num_heads / num_kv_heads) * (head_dim + 2) * 4 bytes.
+ * grouping: 2 * 4096 * (num_heads / num_kv_heads) * (head_dim + 2) * 4 bytes
+ * of partial records plus 2 * 4096 * 4 bytes of merge information.
  */
 PKV_API size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
                                           int head_dim, int max_seq_len, int partition_size);

@@ -33,8 +33,12 @@ size_t workspace_bytes_for(long long rows, int head_dim, long long parts) {
     return (size_t)(rows * parts) * (size_t)(head_dim + 2) * sizeof(float);
 }
 
+// Two records of `group` rows per persistent wave, then two ints of merge
+// information per wave.
+size_t balanced_record_rows(int group) { return (size_t)2 * pkv::kMaxBalancedWaves * group; }
 size_t balanced_workspace_bytes(int group, int head_dim) {
-    return (size_t)2 * pkv::kMaxBalancedWaves * group * (size_t)(head_dim + 2) * sizeof(float);
+    return balanced_record_rows(group) * (size_t)(head_dim + 2) * sizeof(float) +
+           (size_t)2 * pkv::kMaxBalancedWaves * sizeof(int);
 }
 
 // Compute units of the current device, queried once per device.
@@ -172,13 +176,15 @@ int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
         if (cus <= 0) return PKV_ERR_HIP;
         items = cus;
     }
-    const size_t rows = need / ((size_t)(head_dim + 2) * sizeof(float));
+    const size_t rows = balanced ? balanced_record_rows(group)
+                                 : need / ((size_t)(head_dim + 2) * sizeof(float));
 
     pkv::AttnParams a{};
     a.out = out;
     a.out_dtype = out_dtype;
     a.ws_acc = reinterpret_cast<float*>(workspace);
     a.ws_ml = need ? a.ws_acc + rows * head_dim : nullptr;
+    a.ws_info = balanced ? reinterpret_cast<int*>(a.ws_ml + 2 * rows) : nullptr;
     a.q = q;
     a.k_pool = k_pool;
     a.v_pool = v_pool;

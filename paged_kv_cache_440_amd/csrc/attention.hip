@@ -164,11 +164,19 @@ void paged_decode_balanced_kernel(const AttnParams a) {
     const int w = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w >= a.num_items) return;
     const int W = a.num_items;
+    // padding sequences (length 0) own no units: wave w zeroes the rows of
+    // sequences w, w + W, ...
+    for (int i = w; i < a.num_seqs; i += W)
+        if (clamp_len(a, a.seq_lens[i]) == 0)
+            for (int g = 0; g < a.num_kv_heads; ++g) write_zero_rows<Walker::D, G>(a, i, g, lane);
     const long long total = units_before(a, a.num_seqs);
     const long long q = (total + W - 1) / W;
     const long long u0 = (long long)w * q;
     const long long u1 = (u0 + q < total) ? u0 + q : total;
-    if (u0 >= u1) return;
+    if (u0 >= u1) {
+        if (lane == 0) a.ws_info[2 * w] = -1;    // holds no piece of any segment
+        return;
+    }
 
     // the sequence whose segments hold unit u0, and the units before it
     long long base = 0;
@@ -186,6 +194,19 @@ void paged_decode_balanced_kernel(const AttnParams a) {
             break;
         }
         base += __shfl(incl, 63, 64);
+    }
+
+    // Tell the merge kernel whether this wave ends a split segment: the one
+    // holding unit u0, if it started in an earlier wave and ends in this run.
+    {
+        const int nu = units_of(clamp_len(a, a.seq_lens[seq]));
+        const int g = (int)((u0 - base) / nu);
+        const long long seg0 = base + (long long)g * nu;
+        const bool ends_split = seg0 < u0 && seg0 + nu <= u1;
+        if (lane == 0) {
+            a.ws_info[2 * w] = ends_split ? seq * a.num_kv_heads + g : -1;
+            a.ws_info[2 * w + 1] = (int)(seg0 / q);
+        }
     }
 
     Walker st;
@@ -218,56 +239,45 @@ void paged_decode_balanced_kernel(const AttnParams a) {
     }
 }
 
-// Finish the balanced schedule: one wave per (sequence, query head). Rows
-// of empty sequences are zeroed; rows of segments cut by run boundaries are
-// merged from their records with the log-sum-exp rule.
-template <int D>
+// Finish the balanced schedule. Wave (w, h) merges query head h of the split
+// segment that ends in wave w's run, if any (ws_info[2w] = seq * Hkv + g,
+// ws_info[2w + 1] = wf, the first wave holding a piece). Wave wf wrote
+// record 2 wf + 1, waves wf+1 .. w record 2 v. The records are folded in
+// order with the log-sum-exp rule, keeping a running max:
+//   M' = max(M, m_r),  o' = o e^(M - M') + acc_r e^(m_r - M'),
+//   l' = l e^(M - M') + l_r e^(m_r - M'),  out = o / l  (base-2 exponentials).
+// Lane l owns dims l, l + 64, ...; several records are in flight at once.
+template <int D, int G>
 __global__ __launch_bounds__(64 * kWaves)
 void balanced_reduce_kernel(const AttnParams a) {
     const int lane = threadIdx.x & 63;
-    const int num_heads = a.num_kv_heads * a.group;
     const int item = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (item >= a.num_seqs * num_heads) return;
-    const int seq = item / num_heads;
-    const int h = item % num_heads;
-    const int g = h / a.group;
+    if (item >= a.num_items * G) return;
+    const int w = item / G, h = item % G;
+    const int seg = a.ws_info[2 * w];
+    if (seg < 0) return;
+    const int wf = a.ws_info[2 * w + 1];
     constexpr int PER = D / 64;
-    const int nu = units_of(clamp_len(a, a.seq_lens[seq]));
-    if (nu == 0) {
+    float mrun = -__builtin_inff(), lsum = 0.f, o[PER];
 #pragma unroll
-        for (int e = 0; e < PER; ++e)
-            store_out(a.out, a.out_dtype, (size_t)item * D + lane + 64 * e, 0.f);
-        return;
-    }
-    const int W = a.num_items;
-    const long long total = units_before(a, a.num_seqs);
-    const long long q = (total + W - 1) / W;
-    const long long seg0 = units_before(a, seq) + (long long)g * nu;
-    const long long wf = seg0 / q;
-    const long long wl = (seg0 + nu - 1) / q;
-    if (wf == wl) return;                        // finished by one wave
-    const int hh = h % a.group;
-    float mmax = -__builtin_inff();
-    for (long long wv = wf; wv <= wl; ++wv) {
-        const size_t rec = 2 * (size_t)wv + (wv == wf ? 1 : 0);
-        mmax = __builtin_fmaxf(mmax, a.ws_ml[2 * (rec * a.group + hh)]);
-    }
-    float o[PER], lsum = 0.f;
+    for (int k = 0; k < PER; ++k) o[k] = 0.f;
+#pragma unroll 8
+    for (int v = wf; v <= w; ++v) {
+        const size_t row = (2 * (size_t)v + (v == wf ? 1 : 0)) * G + h;
+        const float mr = a.ws_ml[2 * row];
+        const float mnew = __builtin_fmaxf(mrun, mr);
+        const float keep = (mrun == -__builtin_inff()) ? 0.f : fast_exp2(mrun - mnew);
+        const float take = (mr == -__builtin_inff()) ? 0.f : fast_exp2(mr - mnew);
+        lsum = __builtin_fmaf(take, a.ws_ml[2 * row + 1], lsum * keep);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = 0.f;
-    for (long long wv = wf; wv <= wl; ++wv) {
-        const size_t row = (2 * (size_t)wv + (wv == wf ? 1 : 0)) * a.group + hh;
-        const float mp = a.ws_ml[2 * row];
-        const float wgt = (mp == -__builtin_inff()) ? 0.f : fast_exp2(mp - mmax);
-        lsum = __builtin_fmaf(wgt, a.ws_ml[2 * row + 1], lsum);
-        const float* acc = a.ws_acc + row * D;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(wgt, acc[lane + 64 * e], o[e]);
+        for (int k = 0; k < PER; ++k)
+            o[k] = __builtin_fmaf(take, a.ws_acc[row * D + lane + 64 * k], o[k] * keep);
+        mrun = mnew;
     }
+    const size_t out0 = ((size_t)seg * G + h) * D;   // row (seq, g * G + h)
     const float inv = 1.0f / lsum;
 #pragma unroll
-    for (int e = 0; e < PER; ++e)
-        store_out(a.out, a.out_dtype, (size_t)item * D + lane + 64 * e, o[e] * inv);
+    for (int k = 0; k < PER; ++k) store_out(a.out, a.out_dtype, out0 + lane + 64 * k, o[k] * inv);
 }
 
 // Waves of a balanced kernel instance that fit on one compute unit at once
@@ -308,7 +318,8 @@ hipError_t launch_walker(const AttnParams& a_in, hipStream_t stream) {
                            0, stream, a);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL((balanced_reduce_kernel<D>), dim3(rblocks), dim3(64 * kWaves), 0,
+        hipLaunchKernelGGL((balanced_reduce_kernel<D, G>),
+                           dim3((a.num_items * G + kWaves - 1) / kWaves), dim3(64 * kWaves), 0,
                            stream, a);
         return hipGetLastError();
     }

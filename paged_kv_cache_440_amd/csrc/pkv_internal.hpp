@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/pkv.h"
+#include "pkv.h"
 
 namespace pkv {
 
@@ -17,6 +17,8 @@ struct AttnParams {
                                    // [B][H][max_parts] rows (fixed partitions) or
                                    // [2 * kMaxBalancedWaves][G] rows (balanced)
     float* ws_ml;                  // per row: running max in log2 units, sum
+    int* ws_info;                  // balanced: 2 ints per persistent wave (split
+                                   // segment ending in its run, first wave holding it)
     const void* q;
     const void* k_pool;
     const void* v_pool;

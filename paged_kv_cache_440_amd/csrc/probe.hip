@@ -2,7 +2,7 @@
 // read-only stream that gives the practical HBM read ceiling, and a plain
 // copy of known size for scaling traffic counters.
 
-#include "../../include/pkv_probe.h"
+#include "pkv_probe.h"
 #include "pkv_device.hpp"
 
 namespace pkv {

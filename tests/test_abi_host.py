@@ -111,10 +111,11 @@ def test_workspace_size_formula(lib):
     assert f(64, 40, 40, 128, 2049, 512) == 64 * 40 * 5 * (128 + 2) * 4
     assert f(16, 64, 8, 128, 32768, 512) == 16 * 64 * 64 * 130 * 4
     assert f(-1, 40, 40, 128, 2048, 512) == 0
-    # balanced: two records of G rows per persistent wave, at most 4096 waves
-    assert f(64, 40, 40, 128, 2048, -1) == 2 * 4096 * 1 * 130 * 4
-    assert f(16, 64, 8, 128, 32768, -1) == 2 * 4096 * 8 * 130 * 4
-    assert f(1, 4, 4, 64, 1, -1) == 2 * 4096 * 1 * 66 * 4
+    # balanced: two records of G rows per persistent wave (at most 4096
+    # waves), then two ints of merge information per wave
+    assert f(64, 40, 40, 128, 2048, -1) == 2 * 4096 * 1 * 130 * 4 + 2 * 4096 * 4
+    assert f(16, 64, 8, 128, 32768, -1) == 2 * 4096 * 8 * 130 * 4 + 2 * 4096 * 4
+    assert f(1, 4, 4, 64, 1, -1) == 2 * 4096 * 1 * 66 * 4 + 2 * 4096 * 4
     assert f(0, 4, 4, 64, 1, -1) == 0
     assert f(64, 40, 40, 128, 2048, -2) == 0
     assert f(64, 40, 0, 128, 2048, -1) == 0
