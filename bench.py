@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode attention tokens/s + achieved KV HBM GB/s (% of MI355X peak)"
 PEAK_HBM_GBPS = 8000.0
-DTYPE_NAMES = {"torch.float32": "f32", "torch.float16": "f16", "torch.bfloat16": "bf16"}
+DTYPE_NAMES = {"torch.float32": "f32", "torch.float16": "f16", "torch.bfloat16": "bf16",
+               "torch.uint8": "fp8_e4m3"}
 
 
 def log(*a):
@@ -57,6 +58,24 @@ def measured_traffic(workload: str, partition: int, achieved_bytes: float):
     return rec.get("bytes_per_launch")
 
 
+# The schedule each workload is timed with: the faster of the balanced
+# schedule and 512-token partitions as measured on MI355X. Balanced wins when
+# sequences are long and their lengths spread (few segments per persistent
+# wave); fixed partitions win for many short sequences, for sequences that
+# share prefix blocks (neighbours run side by side and hit the cache) and for
+# the FP8 vector walker.
+DEFAULT_SCHEDULE = {
+    "opt13b_fp16": "balanced",
+    "long_gqa_bf16": "balanced",
+    "long_gqa_fp8": "balanced",
+    "llama13b_bf16": 512,
+    "shared_prefix_fp16": 512,
+    "shared_prefix_cow_fp16": 512,
+    "opt13b_fp8": 512,
+    "tiny_fp32": 512,
+}
+
+
 def pkv_balanced() -> int:
     from paged_kv_cache_440_amd._lib import PARTITION_BALANCED
     return PARTITION_BALANCED
@@ -67,10 +86,12 @@ def cpu_baseline(w):
     attention) over the whole batch, single-threaded float64 numpy."""
     import torch
     from threadpoolctl import threadpool_limits
-    from oracle import paged_decode_attention, pool_after_append
+    from oracle import (fp8_dequantize_pool, paged_decode_attention, pool_after_append,
+                        pool_after_append_fp8)
 
     def bits(t):
-        return t.contiguous().view(torch.int16 if t.element_size() == 2 else torch.int32).numpy()
+        ints = {1: torch.uint8, 2: torch.int16, 4: torch.int32}
+        return t.contiguous().view(ints[t.element_size()]).numpy()
 
     def widen(a):
         t = torch.from_numpy(a).view(w.dtype)
@@ -80,10 +101,17 @@ def cpu_baseline(w):
     kb, vb = bits(w.k_pool), bits(w.v_pool)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        k2, v2 = pool_after_append(kb, vb, bits(w.k_new), bits(w.v_new), w.block_tables,
-                                   w.seq_lens, w.block_size)
-        paged_decode_attention(q, widen(k2), widen(v2), w.block_tables, w.seq_lens,
-                               w.block_size, w.scale)
+        if w.fp8:
+            ks, vs = w.k_scales.numpy(), w.v_scales.numpy()
+            k2, v2 = pool_after_append_fp8(kb, vb, w.k_new.float().numpy(),
+                                           w.v_new.float().numpy(), ks, vs, w.block_tables,
+                                           w.seq_lens, w.block_size)
+            kf, vf = fp8_dequantize_pool(k2, ks), fp8_dequantize_pool(v2, vs)
+        else:
+            k2, v2 = pool_after_append(kb, vb, bits(w.k_new), bits(w.v_new), w.block_tables,
+                                       w.seq_lens, w.block_size)
+            kf, vf = widen(k2), widen(v2)
+        paged_decode_attention(q, kf, vf, w.block_tables, w.seq_lens, w.block_size, w.scale)
         dt = time.perf_counter() - t0
     return {"value": w.num_seqs / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"the whole batch ({w.num_seqs} sequences, all heads): one append + "
@@ -122,8 +150,7 @@ def main():
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition", type=int, default=None,
                     help="0: one pass per sequence; a multiple of 64: fixed partitions; "
-                         "-1: balanced (default; 512 for the shared-prefix workloads, where "
-                         "neighbouring sequences share blocks)")
+                         "-1: balanced (default: the workload's entry in DEFAULT_SCHEDULE)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run the plain copy probe over buffers of this many MiB "
@@ -144,7 +171,9 @@ def main():
         return
 
     if args.partition is None:
-        args.partition = 512 if args.workload.startswith("shared_prefix") else pkv_balanced()
+        args.partition = DEFAULT_SCHEDULE.get(args.workload, 512)
+        if args.partition == "balanced":
+            args.partition = pkv_balanced()
     kw = {}
     if args.block_size is not None:
         kw["block_size"] = args.block_size
@@ -169,13 +198,27 @@ def main():
     max_len = w.max_seq_len
     stream = torch.cuda.current_stream()
 
-    def attention():
-        pkv.paged_attention_decode(out, q, kp, vp, tables, lens, max_len, w.scale,
-                                   partition_size=args.partition, workspace=ws, stream=stream)
+    if w.fp8:
+        ks, vs = w.k_scales.to(dev), w.v_scales.to(dev)
+
+        def attention():
+            pkv.paged_attention_decode_fp8(out, q, kp, vp, ks, vs, tables, lens, max_len, w.scale,
+                                           partition_size=args.partition, workspace=ws,
+                                           stream=stream)
+
+        def append():
+            pkv.kv_cache_append_fp8(k_new, v_new, kp, vp, ks, vs, tables, lens, stream=stream)
+    else:
+        def attention():
+            pkv.paged_attention_decode(out, q, kp, vp, tables, lens, max_len, w.scale,
+                                       partition_size=args.partition, workspace=ws, stream=stream)
+
+        def append():
+            pkv.kv_cache_append(k_new, v_new, kp, vp, tables, lens, stream=stream)
 
     def step(ev=None):
         pkv.copy_blocks(kp, vp, pairs, stream=stream)
-        pkv.kv_cache_append(k_new, v_new, kp, vp, tables, lens, stream=stream)
+        append()
         if ev is not None:
             ev[0].record(stream)
         attention()
@@ -246,7 +289,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": DTYPE_NAMES[str(w.dtype)],
+        "dtype": DTYPE_NAMES[str(w.k_pool.dtype)],
         "data": "synthetic",
         "config": {
             "workload": w.name,

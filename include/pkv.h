@@ -28,9 +28,15 @@
  *   q, out           [num_seqs][num_heads][head_dim]
  *   k_new, v_new     [num_seqs][num_kv_heads][head_dim]
  *   block_mapping    int32 [num_pairs][2] = (source block, destination block)
- * Element types.  pkv_dtype; all of q, k_new, v_new, k_pool, v_pool share one.
- * Supported shapes.  head_dim 64 or 128; block_size a power of two in [8, 256];
- *   num_heads / num_kv_heads in {1, 2, 4, 8}.
+ * Element types.  pkv_dtype. In pkv_kv_cache_append and
+ *   pkv_paged_attention_decode all of q, k_new, v_new, k_pool, v_pool share
+ *   one of F32, F16, BF16. PKV_FP8_E4M3 is a pool storage type: pools of
+ *   8-bit codes with one float scale per kv head for K and for V, written by
+ *   pkv_kv_cache_append_fp8 and read by pkv_paged_attention_decode_fp8;
+ *   pkv_copy_blocks copies any pool type (scales are per head, not per
+ *   block, so a block copy needs nothing else).
+ * Supported shapes.  head_dim 64 or 128 (128 for FP8 pools); block_size a
+ *   power of two in [8, 256]; num_heads / num_kv_heads in {1, 2, 4, 8}.
  * Device-resident values (table entries, seq_lens, block_mapping) are the
  *   caller's contract and are not read by the host. The kernels never access
  *   memory outside the buffers described above: a table entry outside
@@ -60,7 +66,7 @@
 extern "C" {
 #endif
 
-typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 } pkv_dtype;
 
 typedef enum {
     PKV_OK = 0,
@@ -171,6 +177,49 @@ PKV_API int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype,
                                float scale, int partition_size,
                                void* workspace, size_t workspace_bytes,
                                pkv_dtype dtype, void* stream);
+
+/*
+ * FP8 KV cache (blog.aqudi.me "벤치마크가 다가 아니야! vLLM으로 보는 LLM 추론
+ * 최적화", section 4: lowering the precision of the KV cache saves memory
+ * and bandwidth). Storage is OCP FP8 E4M3: a code s eeee mmm stands for
+ * (-1)^s 2^(e-7) (1 + m/8), or (-1)^s 2^-6 m/8 when e = 0; s 1111 111 is
+ * NaN; the largest finite magnitude is 448. A stored code c of kv head g
+ * means value(c) * k_scales[g] in k_pool (v_scales[g] in v_pool).
+ *
+ * pkv_kv_cache_append_fp8: as pkv_kv_cache_append, but k_new / v_new
+ * ([num_seqs][num_kv_heads][head_dim], new_dtype F32, F16 or BF16) are
+ * quantised into the uint8 pools: each element x of head g becomes the
+ * E4M3 code nearest to float32(x) / k_scales[g] (IEEE float32 division;
+ * ties to the even code; magnitudes beyond 448 saturate to 448; NaN stays
+ * NaN). k_scales / v_scales are device float arrays [num_kv_heads], read by
+ * the kernel. head_dim must be 128.
+ */
+PKV_API int pkv_kv_cache_append_fp8(const void* k_new, const void* v_new, pkv_dtype new_dtype,
+                            void* k_pool, void* v_pool,
+                            const float* k_scales, const float* v_scales,
+                            const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* seq_lens,
+                            int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                            int num_blocks, void* stream);
+
+/*
+ * pkv_paged_attention_decode_fp8: as pkv_paged_attention_decode, over uint8
+ * E4M3 pools with per-head scales: K_i[t][g] = value(code) * k_scales[g],
+ * V_i[t][g] = value(code) * v_scales[g]. q has q_dtype (F32, F16 or BF16);
+ * arithmetic is fp32 as in the 16-bit path. head_dim must be 128; with more
+ * than one query head per kv head q must be F16 or BF16. The workspace is sized by
+ * pkv_paged_attention_workspace_size exactly as for the 16-bit path.
+ */
+PKV_API int pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype,
+                               const void* q, pkv_dtype q_dtype,
+                               const void* k_pool, const void* v_pool,
+                               const float* k_scales, const float* v_scales,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* seq_lens, int max_seq_len,
+                               int num_seqs, int num_heads, int num_kv_heads,
+                               int head_dim, int block_size, int num_blocks,
+                               float scale, int partition_size,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated description of a pkv_status value. */
 PKV_API const char* pkv_status_string(int status);

@@ -13,3 +13,10 @@ from .paged_attention import (  # noqa: F401
     pool_after_append,
     pool_after_copy,
 )
+from .fp8 import (  # noqa: F401
+    decode as fp8_decode,
+    encode as fp8_encode,
+    quantize as fp8_quantize,
+    pool_after_append_fp8,
+    dequantize_pool as fp8_dequantize_pool,
+)

@@ -8,6 +8,9 @@ names below load it on first use, and fail loudly if it was not built.
 
 _API = (
     "kv_cache_append",
+    "kv_cache_append_fp8",
+    "paged_attention_decode_fp8",
+    "FP8_E4M3",
     "copy_blocks",
     "paged_attention_decode",
     "paged_attention_workspace_size",

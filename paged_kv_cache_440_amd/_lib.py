@@ -16,6 +16,8 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+FP8_E4M3 = 3            # PKV_FP8_E4M3: pools of uint8 E4M3 codes with per-head scales
+POOL_CODES = {**DTYPE_CODES, torch.uint8: FP8_E4M3}
 STATUS = {0: "PKV_OK", -1: "PKV_ERR_INVALID", -2: "PKV_ERR_UNSUPPORTED",
           -3: "PKV_ERR_WORKSPACE", -4: "PKV_ERR_HIP"}
 
@@ -48,6 +50,11 @@ def library() -> ctypes.CDLL:
     lib.pkv_paged_attention_decode.argtypes = [P, I, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I,
                                                P, Z, I, P]
     lib.pkv_paged_attention_decode.restype = I
+    lib.pkv_kv_cache_append_fp8.argtypes = [P, P, I, P, P, P, P, P, I, P, I, I, I, I, I, P]
+    lib.pkv_kv_cache_append_fp8.restype = I
+    lib.pkv_paged_attention_decode_fp8.argtypes = [P, I, P, I, P, P, P, P, P, I, P, I, I, I, I, I,
+                                                   I, I, F, I, P, Z, P]
+    lib.pkv_paged_attention_decode_fp8.restype = I
     lib.pkv_status_string.argtypes = [I]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_probe_read.argtypes = [P, Z, P, P]
@@ -90,16 +97,25 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
 def _pool_geometry(k_pool: torch.Tensor, v_pool: torch.Tensor):
     if k_pool.dim() != 4 or k_pool.shape != v_pool.shape or k_pool.dtype != v_pool.dtype:
         raise ValueError("k_pool and v_pool must both be [num_blocks][kv_heads][block_size][head_dim]")
-    if k_pool.dtype not in DTYPE_CODES:
-        raise TypeError(f"unsupported dtype {k_pool.dtype}")
+    if k_pool.dtype not in POOL_CODES:
+        raise TypeError(f"unsupported pool dtype {k_pool.dtype}")
     num_blocks, num_kv_heads, block_size, head_dim = k_pool.shape
-    return num_blocks, num_kv_heads, block_size, head_dim, DTYPE_CODES[k_pool.dtype]
+    return num_blocks, num_kv_heads, block_size, head_dim, POOL_CODES[k_pool.dtype]
+
+
+def _scales(k_scales, v_scales, hkv):
+    for name, t in (("k_scales", k_scales), ("v_scales", v_scales)):
+        if t.shape != (hkv,):
+            raise ValueError(f"{name} must be [num_kv_heads]")
+    return _dev(k_scales, "k_scales", torch.float32), _dev(v_scales, "v_scales", torch.float32)
 
 
 def kv_cache_append(k_new, v_new, k_pool, v_pool, block_tables, seq_lens, stream=None) -> None:
     """pkv_kv_cache_append: store k_new/v_new [B][Hkv][D] at position
     seq_lens[i]-1 of each sequence (seq_lens count the new token)."""
     nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
+    if code == FP8_E4M3:
+        raise TypeError("uint8 (FP8) pools are written by kv_cache_append_fp8")
     b = block_tables.shape[0]
     if k_new.shape != (b, hkv, d) or v_new.shape != (b, hkv, d):
         raise ValueError(f"k_new/v_new must be [{b}][{hkv}][{d}]")
@@ -129,6 +145,29 @@ def copy_blocks(k_pool, v_pool, block_mapping, stream=None) -> None:
 PARTITION_BALANCED = -1     # PKV_PARTITION_BALANCED
 
 
+def kv_cache_append_fp8(k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens,
+                        stream=None) -> None:
+    """pkv_kv_cache_append_fp8: quantise k_new/v_new [B][Hkv][D] (float32,
+    float16 or bfloat16) into uint8 E4M3 pools at position seq_lens[i]-1, with
+    per-head float32 scales [Hkv]."""
+    nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
+    if code != FP8_E4M3:
+        raise TypeError("kv_cache_append_fp8 needs uint8 (FP8) pools")
+    b = block_tables.shape[0]
+    if k_new.shape != (b, hkv, d) or v_new.shape != (b, hkv, d) or k_new.dtype != v_new.dtype:
+        raise ValueError(f"k_new/v_new must be [{b}][{hkv}][{d}] of one dtype")
+    if k_new.dtype not in DTYPE_CODES:
+        raise TypeError(f"unsupported k_new dtype {k_new.dtype}")
+    if seq_lens.shape != (b,):
+        raise ValueError("seq_lens must be [num_seqs]")
+    ks, vs = _scales(k_scales, v_scales, hkv)
+    _check("pkv_kv_cache_append_fp8", library().pkv_kv_cache_append_fp8(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), DTYPE_CODES[k_new.dtype],
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), ks, vs,
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens", torch.int32), b, hkv, d, bs, nb, _stream(stream)))
+
+
 def paged_attention_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len,
                                    partition_size) -> int:
     """pkv_paged_attention_workspace_size, in bytes."""
@@ -146,6 +185,8 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, max_s
     uint8 device tensor) is allocated here when the call needs one and none
     is given."""
     nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
+    if code == FP8_E4M3:
+        raise TypeError("uint8 (FP8) pools are read by paged_attention_decode_fp8")
     if q.dim() != 3 or q.shape[2] != d or q.dtype != k_pool.dtype:
         raise ValueError("q must be [num_seqs][num_heads][head_dim] in the pool's dtype")
     b, h = q.shape[0], q.shape[1]
@@ -193,3 +234,33 @@ def probe_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
         raise ValueError("dst and src must have the same byte size")
     _check("pkv_probe_copy", library().pkv_probe_copy(
         _dev(dst, "dst"), _dev(src, "src"), nbytes, _stream(stream)))
+
+
+def paged_attention_decode_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens,
+                               max_seq_len, scale, partition_size=PARTITION_BALANCED,
+                               workspace=None, stream=None) -> torch.Tensor:
+    """pkv_paged_attention_decode_fp8 into `out` [B][H][D] over uint8 E4M3
+    pools with per-head float32 scales; q is float32, float16 or bfloat16."""
+    nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
+    if code != FP8_E4M3:
+        raise TypeError("paged_attention_decode_fp8 needs uint8 (FP8) pools")
+    if q.dim() != 3 or q.shape[2] != d or q.dtype not in DTYPE_CODES:
+        raise ValueError("q must be [num_seqs][num_heads][head_dim], float32/float16/bfloat16")
+    b, h = q.shape[0], q.shape[1]
+    if out.shape != q.shape or out.dtype not in DTYPE_CODES:
+        raise ValueError("out must be [num_seqs][num_heads][head_dim], float32/float16/bfloat16")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or seq_lens.shape != (b,):
+        raise ValueError("block_tables must be [num_seqs][max_blocks], seq_lens [num_seqs]")
+    ks, vs = _scales(k_scales, v_scales, hkv)
+    need = paged_attention_workspace_size(b, h, hkv, d, max_seq_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("pkv_paged_attention_decode_fp8", library().pkv_paged_attention_decode_fp8(
+        _dev(out, "out"), DTYPE_CODES[out.dtype], _dev(q, "q"), DTYPE_CODES[q.dtype],
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), ks, vs,
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), b, h, hkv, d, bs, nb,
+        float(scale), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+    return out

@@ -10,7 +10,8 @@
 namespace {
 
 bool valid_dtype(int d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
-int dtype_bytes(int d) { return d == PKV_F32 ? 4 : 2; }
+bool valid_pool_dtype(int d) { return valid_dtype(d) || d == PKV_FP8_E4M3; }
+int dtype_bytes(int d) { return d == PKV_F32 ? 4 : d == PKV_FP8_E4M3 ? 1 : 2; }
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
 // log2 of a supported block size (a power of two in [8, 256]), else -1
@@ -57,6 +58,76 @@ int compute_units() {
     return n;
 }
 
+// Validation and parameter setup shared by the attention entry points
+// (everything but the element types). Returns a pkv_status; on PKV_OK with
+// num_seqs > 0, `a` is ready but for dtype / q_dtype / scales.
+int prepare_attention(pkv::AttnParams& a, void* out, int out_dtype, const void* q,
+                      const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                      int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
+                      int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, float scale, int partition_size,
+                      void* workspace, size_t workspace_bytes) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
+        partition_size < PKV_PARTITION_BALANCED || !valid_dtype(out_dtype) || !isfinite(scale))
+        return PKV_ERR_INVALID;
+    if (num_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
+    if (partition_size > 0 && partition_size % 64 != 0) return PKV_ERR_INVALID;
+    const int group = num_heads / num_kv_heads;
+    if (!supported_head_dim(head_dim) || block_log2(block_size) < 0 ||
+        !(group == 1 || group == 2 || group == 4 || group == 8))
+        return PKV_ERR_UNSUPPORTED;
+    if ((long long)max_seq_len > (long long)max_blocks_per_seq * block_size)
+        return PKV_ERR_INVALID;
+    a.group = group;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens) return PKV_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_INVALID;
+    if ((long long)num_seqs * max_blocks_per_seq > INT32_MAX) return PKV_ERR_INVALID;
+    if ((long long)num_seqs * num_heads * head_dim > INT32_MAX) return PKV_ERR_INVALID;
+
+    const bool balanced = partition_size == PKV_PARTITION_BALANCED;
+    const long long parts = balanced ? 1 : parts_for(max_seq_len, partition_size);
+    long long items = parts * num_seqs * num_kv_heads;
+    if (items > INT32_MAX - 64) return PKV_ERR_INVALID;
+    const size_t need = balanced ? balanced_workspace_bytes(group, head_dim)
+                                 : workspace_bytes_for((long long)num_seqs * num_heads, head_dim, parts);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return PKV_ERR_WORKSPACE;
+    if (balanced) {
+        // the launch turns this into the persistent wave count
+        const int cus = compute_units();
+        if (cus <= 0) return PKV_ERR_HIP;
+        items = cus;
+    }
+    const size_t rows = balanced ? balanced_record_rows(group)
+                                 : need / ((size_t)(head_dim + 2) * sizeof(float));
+
+    a.out = out;
+    a.out_dtype = out_dtype;
+    a.ws_acc = reinterpret_cast<float*>(workspace);
+    a.ws_ml = need ? a.ws_acc + rows * head_dim : nullptr;
+    a.ws_info = balanced ? reinterpret_cast<int*>(a.ws_ml + 2 * rows) : nullptr;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.log2_bs = block_log2(block_size);
+    a.num_blocks = num_blocks;
+    a.scale = scale;
+    a.part_tokens = (!balanced && parts > 1) ? partition_size : 0;
+    a.max_parts = (int)parts;
+    a.max_tokens = max_seq_len;
+    a.num_items = (int)items;
+    a.balanced = balanced ? 1 : 0;
+    return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,8 +148,9 @@ int pkv_kv_cache_append(const void* k_new, const void* v_new, void* k_pool, void
                         const int32_t* seq_lens, int num_seqs, int num_kv_heads, int head_dim,
                         int block_size, int num_blocks, pkv_dtype dtype, void* stream) {
     if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-        num_blocks <= 0 || max_blocks_per_seq <= 0 || !valid_dtype(dtype))
+        num_blocks <= 0 || max_blocks_per_seq <= 0 || !valid_pool_dtype(dtype))
         return PKV_ERR_INVALID;
+    if (dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;   // see pkv_kv_cache_append_fp8
     if (!supported_head_dim(head_dim) || block_log2(block_size) < 0) return PKV_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PKV_OK;
     if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !seq_lens)
@@ -102,11 +174,47 @@ int pkv_kv_cache_append(const void* k_new, const void* v_new, void* k_pool, void
     return pkv::launch_append(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int pkv_kv_cache_append_fp8(const void* k_new, const void* v_new, pkv_dtype new_dtype,
+                            void* k_pool, void* v_pool, const float* k_scales,
+                            const float* v_scales, const int32_t* block_tables,
+                            int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs,
+                            int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                            void* stream) {
+    if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks <= 0 || max_blocks_per_seq <= 0 || !valid_dtype(new_dtype))
+        return PKV_ERR_INVALID;
+    if (head_dim != 128 || block_log2(block_size) < 0) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PKV_OK;
+    if (!k_new || !v_new || !k_pool || !v_pool || !k_scales || !v_scales || !block_tables ||
+        !seq_lens)
+        return PKV_ERR_INVALID;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PKV_ERR_INVALID;
+    if ((long long)num_seqs * max_blocks_per_seq > INT32_MAX) return PKV_ERR_INVALID;
+    pkv::AppendFp8Params a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.new_dtype = new_dtype;
+    a.k_pool = reinterpret_cast<uint8_t*>(k_pool);
+    a.v_pool = reinterpret_cast<uint8_t*>(v_pool);
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.log2_bs = block_log2(block_size);
+    a.num_blocks = num_blocks;
+    return pkv::launch_append_fp8(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapping, int num_pairs,
                     int num_kv_heads, int head_dim, int block_size, int num_blocks,
                     pkv_dtype dtype, void* stream) {
     if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-        num_blocks <= 0 || !valid_dtype(dtype))
+        num_blocks <= 0 || !valid_pool_dtype(dtype))
         return PKV_ERR_INVALID;
     if (!supported_head_dim(head_dim) || block_log2(block_size) < 0) return PKV_ERR_UNSUPPORTED;
     if (num_pairs == 0) return PKV_OK;
@@ -143,68 +251,44 @@ int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
                                int num_heads, int num_kv_heads, int head_dim, int block_size,
                                int num_blocks, float scale, int partition_size, void* workspace,
                                size_t workspace_bytes, pkv_dtype dtype, void* stream) {
-    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
-        partition_size < PKV_PARTITION_BALANCED || !valid_dtype(dtype) ||
-        !valid_dtype(out_dtype) || !isfinite(scale))
-        return PKV_ERR_INVALID;
-    if (num_heads % num_kv_heads != 0) return PKV_ERR_INVALID;
-    if (partition_size > 0 && partition_size % 64 != 0) return PKV_ERR_INVALID;
-    const int group = num_heads / num_kv_heads;
-    if (!supported_head_dim(head_dim) || block_log2(block_size) < 0 ||
-        !(group == 1 || group == 2 || group == 4 || group == 8))
-        return PKV_ERR_UNSUPPORTED;
-    if ((long long)max_seq_len > (long long)max_blocks_per_seq * block_size)
-        return PKV_ERR_INVALID;
-    if (num_seqs == 0) return PKV_OK;
-    if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens) return PKV_ERR_INVALID;
-    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_INVALID;
-    if ((long long)num_seqs * max_blocks_per_seq > INT32_MAX) return PKV_ERR_INVALID;
-    if ((long long)num_seqs * num_heads * head_dim > INT32_MAX) return PKV_ERR_INVALID;
-
-    const bool balanced = partition_size == PKV_PARTITION_BALANCED;
-    const long long parts = balanced ? 1 : parts_for(max_seq_len, partition_size);
-    long long items = parts * num_seqs * num_kv_heads;
-    if (items > INT32_MAX - 64) return PKV_ERR_INVALID;
-    const size_t need = balanced ? balanced_workspace_bytes(group, head_dim)
-                                 : workspace_bytes_for((long long)num_seqs * num_heads, head_dim, parts);
-    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
-        return PKV_ERR_WORKSPACE;
-    if (balanced) {
-        // the launch turns this into the persistent wave count
-        const int cus = compute_units();
-        if (cus <= 0) return PKV_ERR_HIP;
-        items = cus;
-    }
-    const size_t rows = balanced ? balanced_record_rows(group)
-                                 : need / ((size_t)(head_dim + 2) * sizeof(float));
-
+    if (!valid_pool_dtype(dtype)) return PKV_ERR_INVALID;
+    if (dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;   // see pkv_paged_attention_decode_fp8
     pkv::AttnParams a{};
-    a.out = out;
-    a.out_dtype = out_dtype;
-    a.ws_acc = reinterpret_cast<float*>(workspace);
-    a.ws_ml = need ? a.ws_acc + rows * head_dim : nullptr;
-    a.ws_info = balanced ? reinterpret_cast<int*>(a.ws_ml + 2 * rows) : nullptr;
-    a.q = q;
-    a.k_pool = k_pool;
-    a.v_pool = v_pool;
-    a.block_tables = block_tables;
-    a.seq_lens = seq_lens;
-    a.max_blocks = max_blocks_per_seq;
-    a.num_seqs = num_seqs;
-    a.num_kv_heads = num_kv_heads;
-    a.group = group;
-    a.head_dim = head_dim;
-    a.log2_bs = block_log2(block_size);
-    a.num_blocks = num_blocks;
-    a.scale = scale;
-    a.part_tokens = (!balanced && parts > 1) ? partition_size : 0;
-    a.max_parts = (int)parts;
-    a.max_tokens = max_seq_len;
-    a.num_items = (int)items;
-    a.balanced = balanced ? 1 : 0;
+    const int st = prepare_attention(a, out, out_dtype, q, k_pool, v_pool, block_tables,
+                                     max_blocks_per_seq, seq_lens, max_seq_len, num_seqs, num_heads,
+                                     num_kv_heads, head_dim, block_size, num_blocks, scale,
+                                     partition_size, workspace, workspace_bytes);
+    if (st != PKV_OK || num_seqs == 0) return st;
     a.dtype = dtype;
+    a.q_dtype = dtype;
     return pkv::launch_paged_attention(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype, const void* q,
+                                   pkv_dtype q_dtype, const void* k_pool, const void* v_pool,
+                                   const float* k_scales, const float* v_scales,
+                                   const int32_t* block_tables, int max_blocks_per_seq,
+                                   const int32_t* seq_lens, int max_seq_len, int num_seqs,
+                                   int num_heads, int num_kv_heads, int head_dim, int block_size,
+                                   int num_blocks, float scale, int partition_size,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(q_dtype)) return PKV_ERR_INVALID;
+    pkv::AttnParams a{};
+    const int st = prepare_attention(a, out, out_dtype, q, k_pool, v_pool, block_tables,
+                                     max_blocks_per_seq, seq_lens, max_seq_len, num_seqs, num_heads,
+                                     num_kv_heads, head_dim, block_size, num_blocks, scale,
+                                     partition_size, workspace, workspace_bytes);
+    if (st != PKV_OK) return st;
+    if (head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (q_dtype == PKV_F32 && a.group > 1) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PKV_OK;
+    if (!k_scales || !v_scales) return PKV_ERR_INVALID;
+    a.dtype = PKV_FP8_E4M3;
+    a.q_dtype = q_dtype;
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    return pkv::launch_paged_attention_fp8(a, (hipStream_t)stream) == hipSuccess ? PKV_OK
+                                                                                 : PKV_ERR_HIP;
 }
 
 }  // extern "C"

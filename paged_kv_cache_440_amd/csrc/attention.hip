@@ -31,6 +31,7 @@
 #include <atomic>
 
 #include "attn_common.hpp"
+#include "attn_fp8.hpp"
 #include "attn_mfma.hpp"
 #include "attn_vec.hpp"
 
@@ -43,6 +44,7 @@ namespace {
 // Partial rows: ws_acc[((seq * H + h) * max_parts + part)], the same for ws_ml.
 template <class Walker>
 __global__ __launch_bounds__(64 * kWaves)
+__attribute__((amdgpu_waves_per_eu(Walker::kMinWavesPerSimd)))
 void paged_decode_kernel(const AttnParams a) {
     constexpr int D = Walker::D, G = Walker::G;
     const int lane = threadIdx.x & 63;
@@ -158,6 +160,7 @@ __device__ __forceinline__ long long units_before(const AttnParams& a, int end) 
 
 template <class Walker>
 __global__ __launch_bounds__(64 * kWaves)
+__attribute__((amdgpu_waves_per_eu(Walker::kMinWavesPerSimd)))
 void paged_decode_balanced_kernel(const AttnParams a) {
     constexpr int G = Walker::G;
     const int lane = threadIdx.x & 63;
@@ -360,7 +363,41 @@ hipError_t launch_dim(const AttnParams& a, hipStream_t stream) {
     }
 }
 
+// FP8 pools: the vector walker for one query head per kv head, the matrix
+// cores for 2, 4 or 8 (q in fp16 / bf16; the entry point rejects fp32 q
+// there). head_dim is 128.
+template <typename Q, int G>
+hipError_t launch_fp8_typed(const AttnParams& a, hipStream_t stream) {
+    if constexpr (G == 1)
+        return launch_walker<Fp8VecWalker<Q, G>>(a, stream);
+    else if constexpr (Q::bytes == 2)
+        return launch_walker<Fp8MfmaWalker<Q, G>>(a, stream);
+    else
+        return hipErrorInvalidValue;
+}
+
+template <typename Q>
+hipError_t launch_fp8_group(const AttnParams& a, hipStream_t stream) {
+    switch (a.group) {
+        case 1: return launch_fp8_typed<Q, 1>(a, stream);
+        case 2: return launch_fp8_typed<Q, 2>(a, stream);
+        case 4: return launch_fp8_typed<Q, 4>(a, stream);
+        case 8: return launch_fp8_typed<Q, 8>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_paged_attention_fp8(const AttnParams& a, hipStream_t stream) {
+    if (a.head_dim != 128) return hipErrorInvalidValue;
+    switch (a.q_dtype) {
+        case PKV_F32: return launch_fp8_group<F32>(a, stream);
+        case PKV_F16: return launch_fp8_group<F16>(a, stream);
+        case PKV_BF16: return launch_fp8_group<BF16>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_paged_attention(const AttnParams& a, hipStream_t stream) {
     switch (a.dtype) {

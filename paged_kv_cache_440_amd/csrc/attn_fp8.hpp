@@ -1,0 +1,493 @@
+// Walkers for FP8 (OCP E4M3) pools: K/V are 8-bit codes times a per-kv-head
+// scale (blog.aqudi.me "벤치마크가 다가 아니야! vLLM으로 보는 LLM 추론
+// 최적화", section 4: a lower-precision KV cache halves the bytes decode
+// streams). Codes are widened in registers with v_cvt_pk_f32_fp8 (exact: every
+// E4M3 value is a float32); the K scale is folded into the score scale and
+// the V scale into the output. head_dim 128: a token row of one kv head is
+// 128 bytes.
+#pragma once
+
+#include "attn_common.hpp"
+#include "attn_mfma.hpp"
+
+namespace pkv {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// the four E4M3 codes of a dword as float32, in byte order
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    f[0] = lo[0];
+    f[1] = lo[1];
+    f[2] = hi[0];
+    f[3] = hi[1];
+}
+
+// q elements [first, first + n) of one row as float32
+template <typename Q>
+__device__ __forceinline__ float q_elem(const char* row, int i);
+template <> __device__ __forceinline__ float q_elem<F32>(const char* row, int i) {
+    return reinterpret_cast<const float*>(row)[i];
+}
+template <> __device__ __forceinline__ float q_elem<F16>(const char* row, int i) {
+    return (float)reinterpret_cast<const _Float16*>(row)[i];
+}
+template <> __device__ __forceinline__ float q_elem<BF16>(const char* row, int i) {
+    return (float)reinterpret_cast<const __bf16*>(row)[i];
+}
+
+// ---------------------------------------------------------------------------
+// Vector walker (one query head per kv head). Lane l holds 16-byte piece
+// l % 8 (16 codes, dims 16 (l % 8) ..) of token l / 8 of an 8-token group;
+// one wave load covers 8 whole rows (1 KB). q is widened once per segment
+// to float32 and pre-multiplied by scale * log2(e) * k_scale, so a score is
+// one 16-term FMA chain plus a 3-step DPP row sum. Softmax bookkeeping is
+// that of the 16-bit vector walker (token classes merged at the end).
+template <typename Q, int G_>
+struct Fp8VecWalker {
+    static constexpr int D = 128, G = G_;
+    static constexpr int ROW = 128, LPT = 8, TPL = 8, NLOAD = 4, CHUNK = TPL * NLOAD, EPL = 16;
+    static constexpr int kMinWavesPerSimd = 2;
+
+    float qf[G][EPL];
+    float m[G], l[G], acc[G][EPL];
+    float vscale;
+
+    int wb, tv;
+    const char* kbase;
+    const char* vbase;
+    const int* trow;
+    size_t head_stride_bytes, kvhead_off;
+    int log2_bs, bs_mask, nblk_valid, max_phys;
+    int lane, tok, piece;
+    int t_end, last_group;
+
+    __device__ __forceinline__ void init(int lane_id) {
+        lane = lane_id;
+        tok = lane_id / LPT;
+        piece = lane_id % LPT;
+    }
+
+    __device__ __forceinline__ void begin(const AttnParams& a, int seq, int g, int L) {
+        log2_bs = a.log2_bs;
+        bs_mask = (1 << a.log2_bs) - 1;
+        nblk_valid = (L + bs_mask) >> a.log2_bs;
+        max_phys = a.num_blocks;
+        trow = a.block_tables + (size_t)seq * a.max_blocks;
+        head_stride_bytes = (size_t)a.num_kv_heads * ((size_t)ROW << a.log2_bs);
+        kvhead_off = (size_t)g * ((size_t)ROW << a.log2_bs);
+        kbase = reinterpret_cast<const char*>(a.k_pool);
+        vbase = reinterpret_cast<const char*>(a.v_pool);
+        vscale = a.v_scales[g];
+        const float qmul = a.scale * kLog2e * a.k_scales[g];
+        const char* q0 = reinterpret_cast<const char*>(a.q) +
+                         ((size_t)seq * a.num_kv_heads * G + (size_t)g * G) * D * Q::bytes;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+                qf[h][e] = q_elem<Q>(q0 + (size_t)h * D * Q::bytes, piece * EPL + e) * qmul;
+            m[h] = -__builtin_inff();
+            l[h] = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+        }
+    }
+
+    __device__ __forceinline__ void load_window(int first_block) {
+        wb = first_block;
+        tv = (wb + lane < nblk_valid) ? trow[wb + lane] : 0;
+    }
+
+    __device__ __forceinline__ uint32_t phys(int blk) {
+        uint32_t p = (uint32_t)__builtin_amdgcn_readlane(tv, blk - wb);
+        return p < (uint32_t)max_phys ? p : (uint32_t)(max_phys - 1);
+    }
+
+    __device__ __forceinline__ void load_chunk(int c0, u32x4 (&kr)[NLOAD], u32x4 (&vr)[NLOAD]) {
+#pragma unroll
+        for (int j = 0; j < NLOAD; ++j) {
+            int tg = c0 + j * TPL;
+            tg = tg < last_group ? tg : last_group;
+            const uint32_t p = phys(tg >> log2_bs);
+            const size_t blk_off = (size_t)p * head_stride_bytes + kvhead_off;
+            const uint32_t off = (uint32_t)(((tg & bs_mask) + tok) * ROW + piece * 16);
+            kr[j] = load16(kbase + blk_off + off);
+            vr[j] = load16(vbase + blk_off + off);
+        }
+    }
+
+    template <bool TAIL>
+    __device__ __forceinline__ void consume(int c0, const u32x4 (&kr)[NLOAD],
+                                            const u32x4 (&vr)[NLOAD], float) {
+        bool valid[NLOAD];
+#pragma unroll
+        for (int j = 0; j < NLOAD; ++j) valid[j] = !TAIL || (c0 + j * TPL + tok < t_end);
+        // scores, one K piece widened at a time
+        float s[G][NLOAD];
+#pragma unroll
+        for (int j = 0; j < NLOAD; ++j) {
+            float kf[EPL];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) fp8x4_to_f32(kr[j][w], kf + 4 * w);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float d = qf[h][0] * kf[0];
+#pragma unroll
+                for (int e = 1; e < EPL; ++e) d = __builtin_fmaf(qf[h][e], kf[e], d);
+                d = group_sum<LPT>(d);
+                s[h][j] = (TAIL && !valid[j]) ? -__builtin_inff() : d;
+            }
+        }
+        // online softmax update, then the V pieces one at a time
+        float p[G][NLOAD];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float mx = m[h];
+#pragma unroll
+            for (int j = 0; j < NLOAD; ++j) mx = __builtin_fmaxf(mx, s[h][j]);
+            const float alpha = (TAIL && mx == -__builtin_inff()) ? 1.f : fast_exp2(m[h] - mx);
+            float ps = 0.f;
+#pragma unroll
+            for (int j = 0; j < NLOAD; ++j) {
+                p[h][j] = (TAIL && !valid[j]) ? 0.f : fast_exp2(s[h][j] - mx);
+                ps += p[h][j];
+            }
+            l[h] = l[h] * alpha + ps;
+            m[h] = mx;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+        }
+#pragma unroll
+        for (int j = 0; j < NLOAD; ++j) {
+            float vf[EPL];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) fp8x4_to_f32(vr[j][w], vf + 4 * w);
+            if constexpr (TAIL) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) vf[e] = valid[j] ? vf[e] : 0.f;
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[h][e] = __builtin_fmaf(p[h][j], vf[e], acc[h][e]);
+        }
+    }
+
+    __device__ __forceinline__ void walk(int t_begin, int t_stop, float scale_log2) {
+        u32x4 k0[NLOAD], v0[NLOAD], k1[NLOAD], v1[NLOAD];
+        for (int w0 = t_begin; w0 < t_stop;) {
+            const int first_block = w0 >> log2_bs;
+            const int win_end = (first_block + 64) << log2_bs;
+            const int w_end = win_end < t_stop ? win_end : t_stop;
+            load_window(first_block);
+            t_end = w_end;
+            last_group = ((w_end - 1) / TPL) * TPL;
+            int c = w0;
+            load_chunk(c, k0, v0);
+            for (;;) {
+                const int n1 = c + CHUNK;
+                if (n1 >= w_end) { consume<true>(c, k0, v0, scale_log2); break; }
+                load_chunk(n1, k1, v1);
+                consume<false>(c, k0, v0, scale_log2);
+                const int n2 = n1 + CHUNK;
+                if (n2 >= w_end) { consume<true>(n1, k1, v1, scale_log2); break; }
+                load_chunk(n2, k0, v0);
+                consume<false>(n1, k1, v1, scale_log2);
+                c = n2;
+            }
+            w0 = w_end;
+        }
+    }
+
+    // classes merged with the log-sum-exp rule; acc[h] ends scaled to values
+    __device__ __forceinline__ void merge_classes(int h, float& mall, float& lsum) {
+        mall = strided_max<LPT>(m[h]);
+        const float w = (m[h] == -__builtin_inff()) ? 0.f : fast_exp2(m[h] - mall);
+        lsum = strided_sum<LPT>(l[h] * w);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = strided_sum<LPT>(acc[h][e] * w) * vscale;
+    }
+
+    __device__ __forceinline__ void write_final(const AttnParams& a, int seq, int g) {
+        const size_t row0 = (size_t)seq * a.num_kv_heads * G + (size_t)g * G;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float mall, lsum;
+            merge_classes(h, mall, lsum);
+            const float inv = 1.0f / lsum;
+            if (tok == 0) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e)
+                    store_out(a.out, a.out_dtype, (row0 + h) * D + piece * EPL + e, acc[h][e] * inv);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void write_partial(const AttnParams& a, size_t row0,
+                                                  size_t row_stride) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float mall, lsum;
+            merge_classes(h, mall, lsum);
+            const size_t row = row0 + (size_t)h * row_stride;
+            if (tok == 0) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) a.ws_acc[row * D + piece * EPL + e] = acc[h][e];
+            }
+            if (lane == 0) {
+                a.ws_ml[2 * row] = mall;
+                a.ws_ml[2 * row + 1] = lsum;
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Matrix-core walker (2, 4 or 8 query heads per kv head, q in fp16 or bf16).
+// Same contractions and layouts as MfmaWalker<F16> (attn_mfma.hpp); the
+// codes are widened to fp16 (exact) on the way into the operands, and q is
+// converted to fp16 once per segment.
+//   K, step s of group q: dims 16q + 8s' .. (s = 2h + s', h = 0, 1 picks
+//     bytes 16q or 64 + 16q of the row): one 16-byte load gives two steps.
+//   V: lane (n, q) loads the 8 codes of dims 8n .. 8n+7 of each of its
+//     tokens (an 8-byte load); tile c takes code c of the eight tokens.
+template <typename Q, int G_>
+struct Fp8MfmaWalker {
+    static constexpr int D = 128, G = G_;
+    static constexpr int ROW = 128;
+    static constexpr int CHUNK = 32;
+    static constexpr int kMinWavesPerSimd = 2;
+    static_assert(Q::bytes == 2 && G_ <= 16, "16-bit q, at most 16 query heads");
+
+    f32x4 acc[8];
+    float m, l, vscale, kfac;
+    u32x4 qb[4];        // fp16 B operand of Q^T for the four k-steps
+
+    int wb, tv;
+    const char* kbase;
+    const char* vbase;
+    const int* trow;
+    size_t head_stride_bytes, kvhead_off;
+    int log2_bs, bs_mask, nblk_valid, max_phys;
+    int lane, n, q;
+    int t_end;
+
+    __device__ __forceinline__ void init(int lane_id) {
+        lane = lane_id;
+        n = lane_id & 15;
+        q = lane_id >> 4;
+    }
+
+    __device__ __forceinline__ void begin(const AttnParams& a, int seq, int g, int L) {
+        log2_bs = a.log2_bs;
+        bs_mask = (1 << a.log2_bs) - 1;
+        nblk_valid = (L + bs_mask) >> a.log2_bs;
+        max_phys = a.num_blocks;
+        trow = a.block_tables + (size_t)seq * a.max_blocks;
+        head_stride_bytes = (size_t)a.num_kv_heads * ((size_t)ROW << a.log2_bs);
+        kvhead_off = (size_t)g * ((size_t)ROW << a.log2_bs);
+        kbase = reinterpret_cast<const char*>(a.k_pool);
+        vbase = reinterpret_cast<const char*>(a.v_pool);
+        vscale = a.v_scales[g];
+        kfac = a.k_scales[g];
+        const char* qrow = reinterpret_cast<const char*>(a.q) +
+                           ((size_t)seq * a.num_kv_heads * G + (size_t)g * G + n) * D * Q::bytes;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            // step s = 2h + s2: dims 64h + 16q + 8 s2 .. +7
+            const int d0 = 64 * (s >> 1) + 16 * q + 8 * (s & 1);
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (n < G) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x0 = q_elem<Q>(qrow, d0 + 2 * i), x1 = q_elem<Q>(qrow, d0 + 2 * i + 1);
+                    w[i] = to16(F16{}, x0) | (to16(F16{}, x1) << 16);
+                }
+            }
+            qb[s] = w;
+        }
+        m = -__builtin_inff();
+        l = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    __device__ __forceinline__ void load_window(int first_block) {
+        wb = first_block;
+        tv = (wb + lane < nblk_valid) ? trow[wb + lane] : 0;
+    }
+
+    __device__ __forceinline__ uint32_t phys(int blk) {
+        const uint32_t p = (uint32_t)__builtin_amdgcn_ds_bpermute(blk << 2, tv);
+        return p < (uint32_t)max_phys ? p : (uint32_t)(max_phys - 1);
+    }
+
+    // K: kt[t][h] = row (c0 + 16t + n), bytes 64h + 16q .. +15
+    __device__ __forceinline__ void load_k(int c0, u32x4 (&kt)[2][2]) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int tok = c0 + 16 * t + n;
+            const char* p = kbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes +
+                            kvhead_off + (uint32_t)((tok & bs_mask) * ROW + 16 * q);
+            kt[t][0] = load16(p);
+            kt[t][1] = load16(p + 64);
+        }
+    }
+
+    // V: vt[4h + j] = row (c0 + 16h + 4q + j), bytes 8n .. 8n+7
+    __device__ __forceinline__ void load_v(int c0, u32x2 (&vt)[8]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int tok = c0 + 16 * h + 4 * q;
+            const char* p = vbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes +
+                            kvhead_off + (uint32_t)((tok & bs_mask) * ROW + 8 * n);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vt[4 * h + j] = *reinterpret_cast<const u32x2*>(p + ROW * j);
+        }
+    }
+
+    // 8 codes (two dwords) -> the fp16 A operand of one k-step
+    __device__ __forceinline__ u32x4 codes_to_f16(uint32_t w0, uint32_t w1) {
+        float f[8];
+        fp8x4_to_f32(w0, f);
+        fp8x4_to_f32(w1, f + 4);
+        u32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = to16(F16{}, f[2 * i]) | (to16(F16{}, f[2 * i + 1]) << 16);
+        return r;
+    }
+
+    __device__ __forceinline__ void scores(const u32x4 (&kt)[2][2], float scale_log2,
+                                           float (&sc)[8]) {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int s = 2 * h + s2;
+                s0 = mfma_16x16x32(F16{}, codes_to_f16(kt[0][h][2 * s2], kt[0][h][2 * s2 + 1]),
+                                   qb[s], s0);
+                s1 = mfma_16x16x32(F16{}, codes_to_f16(kt[1][h][2 * s2], kt[1][h][2 * s2 + 1]),
+                                   qb[s], s1);
+            }
+        }
+        const float f = scale_log2 * kfac;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sc[i] = s0[i] * f;
+            sc[4 + i] = s1[i] * f;
+        }
+    }
+
+    template <bool TAIL>
+    __device__ __forceinline__ void softmax_pv(int c0, float (&sc)[8], u32x2 (&vt)[8]) {
+        if constexpr (TAIL) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const bool valid = c0 + 16 * (j >> 2) + 4 * q + (j & 3) < t_end;
+                sc[j] = valid ? sc[j] : -__builtin_inff();
+                vt[j][0] = valid ? vt[j][0] : 0u;
+                vt[j][1] = valid ? vt[j][1] : 0u;
+            }
+        }
+        float mx = sc[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = __builtin_fmaxf(mx, sc[j]);
+        mx = strided_max<16>(mx);
+        const float m_new = __builtin_fmaxf(m, mx);
+        const float alpha = fast_exp2(m - m_new);
+        float p[8], ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = fast_exp2(sc[j] - m_new);
+            ps += p[j];
+        }
+        l = l * alpha + ps;
+        m = m_new;
+        u32x4 bhi, blo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t h0 = to16(F16{}, p[2 * w]), h1 = to16(F16{}, p[2 * w + 1]);
+            const uint32_t r0 = to16(F16{}, p[2 * w] - from16(F16{}, h0));
+            const uint32_t r1 = to16(F16{}, p[2 * w + 1] - from16(F16{}, h1));
+            bhi[w] = h0 | (h1 << 16);
+            blo[w] = r0 | (r1 << 16);
+        }
+        // widen the eight V pieces: vf[j][c] = code c of token j
+        float vf[8][8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            fp8x4_to_f32(vt[j][0], vf[j]);
+            fp8x4_to_f32(vt[j][1], vf[j] + 4);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            u32x4 av;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                av[w] = to16(F16{}, vf[2 * w][c]) | (to16(F16{}, vf[2 * w + 1][c]) << 16);
+            f32x4 o = acc[c] * alpha;
+            o = mfma_16x16x32(F16{}, av, bhi, o);
+            acc[c] = mfma_16x16x32(F16{}, av, blo, o);
+        }
+    }
+
+    __device__ __forceinline__ void walk(int t_begin, int t_stop, float scale_log2) {
+        u32x4 kt[2][2];
+        u32x2 vt[8];
+        float sc[8];
+        for (int w0 = t_begin; w0 < t_stop;) {
+            const int first_block = w0 >> log2_bs;
+            const int win_end = (first_block + 64) << log2_bs;
+            const int w_end = win_end < t_stop ? win_end : t_stop;
+            load_window(first_block);
+            t_end = w_end;
+            int c = w0;
+            load_k(c, kt);
+            load_v(c, vt);
+            for (;;) {
+                const int nx = c + CHUNK;
+                scores(kt, scale_log2, sc);
+                if (nx >= w_end) { softmax_pv<true>(c, sc, vt); break; }
+                load_k(nx, kt);
+                softmax_pv<false>(c, sc, vt);
+                load_v(nx, vt);
+                c = nx;
+            }
+            w0 = w_end;
+        }
+    }
+
+    __device__ __forceinline__ void write_final(const AttnParams& a, int seq, int g) {
+        const float inv = vscale / strided_sum<16>(l);
+        if (n >= G) return;
+        const size_t base = ((size_t)seq * a.num_kv_heads * G + (size_t)g * G + n) * D + 32 * q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) store_out(a.out, a.out_dtype, base + 8 * i + c, acc[c][i] * inv);
+    }
+
+    __device__ __forceinline__ void write_partial(const AttnParams& a, size_t row0,
+                                                  size_t row_stride) {
+        const float lsum = strided_sum<16>(l);
+        if (n >= G) return;
+        const size_t row = row0 + (size_t)n * row_stride;
+        float* dst = a.ws_acc + row * D + 32 * q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) dst[8 * i + c] = acc[c][i] * vscale;
+        if (q == 0) {
+            a.ws_ml[2 * row] = m;
+            a.ws_ml[2 * row + 1] = lsum;
+        }
+    }
+};
+
+}  // namespace
+}  // namespace pkv

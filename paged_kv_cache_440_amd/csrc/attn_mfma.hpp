@@ -73,6 +73,7 @@ struct MfmaWalker {
     static constexpr int D = 128, G = G_;
     static constexpr int ROW = 256;             // bytes of one token row of one kv head
     static constexpr int CHUNK = 32;            // tokens per chunk
+    static constexpr int kMinWavesPerSimd = 2;
     static_assert(S::bytes == 2 && G_ <= 16, "16-bit K/V, at most 16 query heads");
 
     f32x4 acc[8];       // O^T tiles: acc[c][i] = head n, dim 32q + 8i + c (unnormalised)
@@ -240,8 +241,10 @@ struct MfmaWalker {
                 scores(kt, scale_log2, sc);
                 if (nx >= w_end) { softmax_pv<true>(c, sc, vt); break; }
                 load_k(nx, kt);
+                __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
                 softmax_pv<false>(c, sc, vt);
                 load_v(nx, vt);
+                __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
                 c = nx;
             }
             w0 = w_end;

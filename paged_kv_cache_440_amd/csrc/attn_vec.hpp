@@ -51,6 +51,7 @@ struct VecWalker {
     using Gm = Geo<S, D_>;
     static constexpr int LPT = Gm::LPT, TPL = Gm::TPL, NLOAD = Gm::NLOAD;
     static constexpr int CHUNK = Gm::CHUNK, EPL = Gm::EPL;
+    static constexpr int kMinWavesPerSimd = 1;
 
     // per-lane running state for G query heads
     float m[G], l[G], acc[G][EPL];
@@ -194,10 +195,12 @@ struct VecWalker {
                 const int n1 = c + CHUNK;
                 if (n1 >= w_end) { consume<true>(c, k0, v0, scale_log2); break; }
                 load_chunk(n1, k1, v1);
+                __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
                 consume<false>(c, k0, v0, scale_log2);
                 const int n2 = n1 + CHUNK;
                 if (n2 >= w_end) { consume<true>(n1, k1, v1, scale_log2); break; }
                 load_chunk(n2, k0, v0);
+                __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
                 consume<false>(n1, k1, v1, scale_log2);
                 c = n2;
             }

@@ -39,7 +39,11 @@ struct AttnParams {
                                    // balanced: the compute-unit count on entry to the
                                    // launcher, the persistent wave count in the kernels
     int balanced;                  // 1: balanced schedule (see attention.hip)
-    int dtype;
+    int dtype;                     // q / K / V element type (16/32-bit path)
+    // FP8 pools: K/V are E4M3 codes times a per-kv-head scale; q has q_dtype
+    const float* k_scales;
+    const float* v_scales;
+    int q_dtype;
 };
 
 // Persistent waves of the balanced schedule: kBalancedWavesPerCU per compute
@@ -66,6 +70,25 @@ struct AppendParams {
     int num_blocks;
 };
 
+// Quantising append into FP8 E4M3 pools.
+struct AppendFp8Params {
+    const void* k_new;
+    const void* v_new;
+    int new_dtype;                 // PKV_F32 / PKV_F16 / PKV_BF16
+    uint8_t* k_pool;
+    uint8_t* v_pool;
+    const float* k_scales;         // [num_kv_heads]
+    const float* v_scales;
+    const int32_t* block_tables;
+    const int32_t* seq_lens;
+    int max_blocks;
+    int num_seqs;
+    int num_kv_heads;
+    int head_dim;
+    int log2_bs;
+    int num_blocks;
+};
+
 struct CopyParams {
     void* k_pool;
     void* v_pool;
@@ -77,6 +100,8 @@ struct CopyParams {
 
 hipError_t launch_paged_attention(const AttnParams& a, hipStream_t stream);
 hipError_t launch_append(const AppendParams& a, hipStream_t stream);
+hipError_t launch_append_fp8(const AppendFp8Params& a, hipStream_t stream);
+hipError_t launch_paged_attention_fp8(const AttnParams& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -64,6 +64,13 @@ class Workload:
     pending_v: torch.Tensor | None = None
     pending_lens: np.ndarray | None = None
     info: dict = field(default_factory=dict)
+    # FP8 pools: uint8 E4M3 codes; a code of kv head g means value * scale[g]
+    k_scales: torch.Tensor | None = None
+    v_scales: torch.Tensor | None = None
+
+    @property
+    def fp8(self) -> bool:
+        return self.k_scales is not None
 
     @property
     def num_seqs(self) -> int:
@@ -79,7 +86,8 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
-        return torch.tensor([], dtype=self.dtype).element_size()
+        """Bytes of one stored K/V element (1 for FP8 pools)."""
+        return self.k_pool.element_size()
 
     def kv_bytes(self) -> int:
         """Bytes of K and V history one decode step reads: sum_i L_i * 2*Hkv*D*eb."""
@@ -98,12 +106,15 @@ def _workers() -> int:
     return max(1, min(16, n))
 
 
-def _draw_into(out: torch.Tensor, seed_seq: np.random.SeedSequence, dist: str) -> None:
+def _draw_into(out: torch.Tensor, seed_seq: np.random.SeedSequence, dist: str,
+               fp8_scales: np.ndarray | None = None, row_elems: int = 1) -> None:
     """Fill a flat host tensor with seeded draws, chunk by chunk.
 
     Each fixed-size chunk has its own child seed, so the values do not depend
     on the number of threads. Draws are float32, rounded to the target dtype
-    to nearest-even.
+    to nearest-even. For a uint8 (FP8) tensor, element i belongs to kv head
+    (i // row_elems) % len(fp8_scales) and stores torch's float8_e4m3fn
+    conversion of draw / scale of that head.
     """
     flat = out.view(-1)
     n = flat.numel()
@@ -120,7 +131,12 @@ def _draw_into(out: torch.Tensor, seed_seq: np.random.SeedSequence, dist: str) -
             x = rng.uniform(-1.0, 1.0, hi - lo).astype(np.float32)
         else:
             raise ValueError(dist)
-        flat[lo:hi] = torch.from_numpy(x).to(out.dtype)
+        if fp8_scales is None:
+            flat[lo:hi] = torch.from_numpy(x).to(out.dtype)
+        else:
+            head = (np.arange(lo, hi, dtype=np.int64) // row_elems) % len(fp8_scales)
+            y = torch.from_numpy(x / fp8_scales[head])
+            flat[lo:hi] = y.to(torch.float8_e4m3fn).view(torch.uint8)
 
     if nchunks == 1:
         work(0)
@@ -146,16 +162,27 @@ def _small_draw(rng: np.random.Generator, shape, dtype, dist: str) -> torch.Tens
     return torch.from_numpy(x).to(dtype).reshape(shape)
 
 
+FP8_NAN = 0x7F
+
+
 def _pool(num_blocks, num_kv_heads, block_size, head_dim, dtype, seed_seq, dist,
-          used_blocks) -> torch.Tensor:
-    pool = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dtype)
-    _draw_into(pool, seed_seq, dist)
+          used_blocks, fp8_scales=None) -> torch.Tensor:
+    pool_dtype = torch.uint8 if fp8_scales is not None else dtype
+    pool = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=pool_dtype)
+    _draw_into(pool, seed_seq, dist, fp8_scales, block_size * head_dim)
     unused = np.ones(num_blocks, dtype=bool)
     unused[np.asarray(used_blocks, dtype=np.int64)] = False
     idx = torch.from_numpy(np.nonzero(unused)[0])
     if idx.numel():
-        pool[idx] = float("nan")
+        pool[idx] = FP8_NAN if fp8_scales is not None else float("nan")
     return pool
+
+
+def fp8_head_scales(num_kv_heads: int, spread: float) -> np.ndarray:
+    """Per-head scales for FP8 pools: head g gets (1 + g / Hkv) * spread / 448,
+    so N(0, 1) values of magnitude up to `spread` stay within the format."""
+    g = np.arange(num_kv_heads, dtype=np.float64)
+    return ((1.0 + g / num_kv_heads) * spread / 448.0).astype(np.float32)
 
 
 def _blocks_needed(n_tokens: int, block_size: int) -> int:
@@ -167,9 +194,11 @@ def _blocks_needed(n_tokens: int, block_size: int) -> int:
 
 def build_independent(name, seq_lens, *, dtype, num_heads, num_kv_heads, head_dim,
                       block_size, dist, seed, pool_factor=1.25, num_blocks=None,
-                      scale=None) -> Workload:
+                      scale=None, fp8_spread=None) -> Workload:
     """Sequences that share no blocks; the table rows are consecutive slices of
-    a seeded permutation of the pool ids."""
+    a seeded permutation of the pool ids. With fp8_spread, the pools hold
+    FP8 E4M3 codes under fp8_head_scales(num_kv_heads, fp8_spread); q and the
+    new tokens keep `dtype`."""
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     ss_tables, ss_k, ss_v, ss_small = np.random.SeedSequence(seed).spawn(4)
     rng_tables = np.random.default_rng(ss_tables)
@@ -187,8 +216,9 @@ def build_independent(name, seq_lens, *, dtype, num_heads, num_kv_heads, head_di
         tables[i, :n] = perm[cursor:cursor + n]
         cursor += n
     used = perm[:needed]
-    k_pool = _pool(num_blocks, num_kv_heads, block_size, head_dim, dtype, ss_k, dist, used)
-    v_pool = _pool(num_blocks, num_kv_heads, block_size, head_dim, dtype, ss_v, dist, used)
+    sc = fp8_head_scales(num_kv_heads, fp8_spread) if fp8_spread is not None else None
+    k_pool = _pool(num_blocks, num_kv_heads, block_size, head_dim, dtype, ss_k, dist, used, sc)
+    v_pool = _pool(num_blocks, num_kv_heads, block_size, head_dim, dtype, ss_v, dist, used, sc)
     rng = np.random.default_rng(ss_small)
     b = len(seq_lens)
     k_new = _small_draw(rng, (b, num_kv_heads, head_dim), dtype, dist)
@@ -198,7 +228,9 @@ def build_independent(name, seq_lens, *, dtype, num_heads, num_kv_heads, head_di
                     head_dim=head_dim, block_size=block_size,
                     scale=(1.0 / math.sqrt(head_dim)) if scale is None else scale,
                     num_blocks=num_blocks, seq_lens=seq_lens, block_tables=tables,
-                    k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new, q=q)
+                    k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new, q=q,
+                    k_scales=None if sc is None else torch.from_numpy(sc.copy()),
+                    v_scales=None if sc is None else torch.from_numpy(sc.copy()))
 
 
 # ----------------------------------------------------------------------------
@@ -221,6 +253,28 @@ def opt13b_fp16(seed=SEED_BASE + 2, num_seqs=64, len_range=(32, 2048),
     return build_independent("opt13b_fp16", lens, dtype=torch.float16, num_heads=40,
                              num_kv_heads=40, head_dim=128, block_size=block_size,
                              dist="normal", seed=seed + 100_000)
+
+
+def opt13b_fp8(seed=SEED_BASE + 6, num_seqs=64, len_range=(32, 2048), block_size=16) -> Workload:
+    """The OPT-13B layer with an FP8 E4M3 KV cache: the same shape and length
+    draw as opt13b_fp16, K/V stored as codes under per-head scales
+    (magnitudes up to 8 representable), q and new tokens in fp16."""
+    rng = np.random.default_rng(np.random.SeedSequence(SEED_BASE + 2).spawn(1)[0])
+    lens = rng.integers(len_range[0], len_range[1], size=num_seqs, endpoint=True)
+    return build_independent("opt13b_fp8", lens, dtype=torch.float16, num_heads=40,
+                             num_kv_heads=40, head_dim=128, block_size=block_size,
+                             dist="normal", seed=seed + 100_000, fp8_spread=8.0)
+
+
+def long_gqa_fp8(seed=SEED_BASE + 7, block_size=16, num_seqs=16,
+                 len_range=(16384, 32768)) -> Workload:
+    """The long-context grouped-query layer (64 query heads over 8 kv heads)
+    with an FP8 E4M3 KV cache; q and new tokens in bf16."""
+    rng = np.random.default_rng(np.random.SeedSequence(SEED_BASE + 5).spawn(1)[0])
+    lens = rng.integers(len_range[0], len_range[1], size=num_seqs, endpoint=True)
+    return build_independent(f"long_gqa_fp8_bs{block_size}", lens, dtype=torch.bfloat16,
+                             num_heads=64, num_kv_heads=8, head_dim=128, block_size=block_size,
+                             dist="normal", seed=seed + 1000 * block_size, fp8_spread=8.0)
 
 
 def llama13b_bf16(seed=SEED_BASE + 3, num_seqs=256, median=350.0, sigma=0.9,
@@ -345,6 +399,8 @@ WORKLOADS = {
     "shared_prefix_fp16": shared_prefix_fp16,
     "shared_prefix_cow_fp16": shared_prefix_cow_fp16,
     "long_gqa_bf16": long_gqa_bf16,
+    "opt13b_fp8": opt13b_fp8,
+    "long_gqa_fp8": long_gqa_fp8,
 }
 
 

@@ -12,11 +12,18 @@ import numpy as np
 import torch
 
 import paged_kv_cache_440_amd as pkv
-from oracle import paged_decode_attention, pool_after_append, pool_after_copy
+from oracle import (fp8_dequantize_pool, paged_decode_attention, pool_after_append,
+                    pool_after_append_fp8, pool_after_copy)
 
 # max-abs tolerance on attention outputs (fp32 accumulation, fp32 output)
 TOL = {torch.float32: 1e-5, torch.float16: 2e-3, torch.bfloat16: 2e-3}
-_INT = {4: torch.int32, 2: torch.int16}
+_INT = {4: torch.int32, 2: torch.int16, 1: torch.uint8}
+
+
+def tol(w) -> float:
+    """Attention tolerance of a workload: the 16-bit bound for FP8 pools (the
+    oracle reads the same dequantised values; only the arithmetic differs)."""
+    return 2e-3 if w.fp8 else TOL[w.dtype]
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
@@ -41,8 +48,10 @@ def widen(t: torch.Tensor) -> np.ndarray:
 def poison_unwritten_slots(w) -> None:
     """Fill with NaN every slot of each sequence's blocks at or past position
     L-1 (the slot the step's append will write, and everything after it),
-    so that stale contents of partially used blocks are NaN (test-side)."""
+    so that stale contents of partially used blocks are NaN (test-side).
+    FP8 pools get the NaN code 0x7F."""
     bs = w.block_size
+    nan = 0x7F if w.fp8 else float("nan")
     for i, n in enumerate(w.seq_lens):
         n = int(n)
         if n <= 0:
@@ -50,8 +59,8 @@ def poison_unwritten_slots(w) -> None:
         nb = -(-n // bs)
         for t in range(n - 1, nb * bs):
             phys = int(w.block_tables[i, t // bs])
-            w.k_pool[phys, :, t % bs] = float("nan")
-            w.v_pool[phys, :, t % bs] = float("nan")
+            w.k_pool[phys, :, t % bs] = nan
+            w.v_pool[phys, :, t % bs] = nan
 
 
 class Device:
@@ -67,27 +76,41 @@ class Device:
         self.tables = torch.from_numpy(w.block_tables).to(dev)
         self.lens = torch.from_numpy(w.seq_lens).to(dev)
         self.pairs = torch.from_numpy(np.ascontiguousarray(w.copy_pairs, dtype=np.int32)).to(dev)
+        self.k_scales = w.k_scales.to(dev) if w.fp8 else None
+        self.v_scales = w.v_scales.to(dev) if w.fp8 else None
         self.pending = []
         if w.pending_lens is not None:
             for t in range(w.pending_lens.shape[0]):
                 self.pending.append((w.pending_k[t].to(dev), w.pending_v[t].to(dev),
                                      torch.from_numpy(w.pending_lens[t]).to(dev)))
 
+    def append(self, k, v, lens):
+        if self.w.fp8:
+            pkv.kv_cache_append_fp8(k, v, self.k_pool, self.v_pool, self.k_scales, self.v_scales,
+                                    self.tables, lens)
+        else:
+            pkv.kv_cache_append(k, v, self.k_pool, self.v_pool, self.tables, lens)
+
     def copy_and_append(self):
         w = self.w
         pkv.copy_blocks(self.k_pool, self.v_pool, self.pairs)
         for k, v, lens in self.pending:
-            pkv.kv_cache_append(k, v, self.k_pool, self.v_pool, self.tables, lens)
-        pkv.kv_cache_append(self.k_new, self.v_new, self.k_pool, self.v_pool, self.tables,
-                            self.lens)
+            self.append(k, v, lens)
+        self.append(self.k_new, self.v_new, self.lens)
         return w
 
     def attention(self, partition_size=-1, out_dtype=torch.float32, workspace=None):
         w = self.w
         out = torch.empty(self.q.shape, dtype=out_dtype, device=self.q.device)
-        pkv.paged_attention_decode(out, self.q, self.k_pool, self.v_pool, self.tables, self.lens,
-                                   w.max_seq_len, w.scale, partition_size=partition_size,
-                                   workspace=workspace)
+        if w.fp8:
+            pkv.paged_attention_decode_fp8(out, self.q, self.k_pool, self.v_pool, self.k_scales,
+                                           self.v_scales, self.tables, self.lens, w.max_seq_len,
+                                           w.scale, partition_size=partition_size,
+                                           workspace=workspace)
+        else:
+            pkv.paged_attention_decode(out, self.q, self.k_pool, self.v_pool, self.tables,
+                                       self.lens, w.max_seq_len, w.scale,
+                                       partition_size=partition_size, workspace=workspace)
         return out
 
 
@@ -95,19 +118,29 @@ def expected_pools(w):
     """Oracle pools (raw bits) after the step's copies and appends."""
     kb, vb = bits(w.k_pool), bits(w.v_pool)
     kb, vb = pool_after_copy(kb, vb, w.copy_pairs)
+
+    def append(kb, vb, k, v, lens):
+        if w.fp8:
+            return pool_after_append_fp8(kb, vb, k.float().numpy(), v.float().numpy(),
+                                         w.k_scales.numpy(), w.v_scales.numpy(), w.block_tables,
+                                         lens, w.block_size)
+        return pool_after_append(kb, vb, bits(k), bits(v), w.block_tables, lens, w.block_size)
+
     if w.pending_lens is not None:
         for t in range(w.pending_lens.shape[0]):
-            kb, vb = pool_after_append(kb, vb, bits(w.pending_k[t]), bits(w.pending_v[t]),
-                                       w.block_tables, w.pending_lens[t], w.block_size)
-    kb, vb = pool_after_append(kb, vb, bits(w.k_new), bits(w.v_new), w.block_tables,
-                               w.seq_lens, w.block_size)
+            kb, vb = append(kb, vb, w.pending_k[t], w.pending_v[t], w.pending_lens[t])
+    kb, vb = append(kb, vb, w.k_new, w.v_new, w.seq_lens)
     return kb, vb
 
 
 def expected_attention(w, kb, vb, seqs=None):
     """Oracle outputs (float64) for the given sequences (default: all)."""
-    k = widen(from_bits(kb, w.dtype))
-    v = widen(from_bits(vb, w.dtype))
+    if w.fp8:
+        k = fp8_dequantize_pool(kb, w.k_scales.numpy())
+        v = fp8_dequantize_pool(vb, w.v_scales.numpy())
+    else:
+        k = widen(from_bits(kb, w.dtype))
+        v = widen(from_bits(vb, w.dtype))
     q = widen(w.q)
     idx = np.arange(w.num_seqs) if seqs is None else np.asarray(seqs)
     return paged_decode_attention(q[idx], k, v, w.block_tables[idx], w.seq_lens[idx],

@@ -79,7 +79,8 @@ def attn(lib, **kw):
     (dict(bs=12), UNSUPPORTED),
     (dict(bs=4), UNSUPPORTED),
     (dict(bs=512), UNSUPPORTED),
-    (dict(dtype=3), INVALID),
+    (dict(dtype=3), UNSUPPORTED),            # FP8 pools go through the _fp8 entry point
+    (dict(dtype=4), INVALID),
     (dict(out_dtype=7), INVALID),
     (dict(part=100), INVALID),              # not a multiple of 64
     (dict(part=-64), INVALID),
@@ -133,7 +134,8 @@ def append(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=-2), INVALID), (dict(Hkv=0), INVALID), (dict(nb=0), INVALID),
-    (dict(max_blocks=0), INVALID), (dict(dtype=5), INVALID), (dict(D=80), UNSUPPORTED),
+    (dict(max_blocks=0), INVALID), (dict(dtype=5), INVALID), (dict(dtype=3), UNSUPPORTED),
+    (dict(D=80), UNSUPPORTED),
     (dict(bs=24), UNSUPPORTED), (dict(kn=0), INVALID), (dict(vp=0), INVALID),
     (dict(tables=0), INVALID), (dict(lens=0), INVALID), (dict(kp=FAKE + 2), INVALID),
     (dict(B=0), OK),
@@ -184,3 +186,59 @@ def test_probe_validation(lib):
     assert words(16) == 1
     assert words(256 * 8 * 16) == 1 and words(256 * 8 * 16 + 16) == 2
     assert words(1 << 34) == 256 * 32                                  # capped grid
+
+
+def attn_fp8(lib, **kw):
+    a = dict(out=FAKE, out_dtype=0, q=FAKE, q_dtype=1, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE,
+             tables=FAKE, max_blocks=8, lens=FAKE, max_seq_len=100, B=2, H=4, Hkv=4, D=128,
+             bs=16, nb=32, scale=0.1, part=0, ws=0, ws_bytes=0)
+    a.update(kw)
+    f = lib.pkv_paged_attention_decode_fp8
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int] + \
+        [ctypes.c_void_p] * 5 + [ctypes.c_int, ctypes.c_void_p] + [ctypes.c_int] * 7 + \
+        [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    return f(a["out"], a["out_dtype"], a["q"], a["q_dtype"], a["k"], a["v"], a["ks"], a["vs"],
+             a["tables"], a["max_blocks"], a["lens"], a["max_seq_len"], a["B"], a["H"], a["Hkv"],
+             a["D"], a["bs"], a["nb"], a["scale"], a["part"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_dtype=3), INVALID),               # q is never FP8
+    (dict(q_dtype=9), INVALID),
+    (dict(D=64), UNSUPPORTED),
+    (dict(H=8, Hkv=4, q_dtype=0), UNSUPPORTED),   # fp32 q only with one q head per kv head
+    (dict(ks=0), INVALID),
+    (dict(vs=0), INVALID),
+    (dict(k=FAKE + 8), INVALID),
+    (dict(part=64, ws=0), WORKSPACE),
+    (dict(B=-1), INVALID),
+    (dict(B=0), OK),
+])
+def test_attention_fp8_validation(lib, kw, status):
+    assert attn_fp8(lib, **kw) == status
+
+
+def append_fp8(lib, **kw):
+    a = dict(kn=FAKE, vn=FAKE, new_dtype=1, kp=FAKE, vp=FAKE, ks=FAKE, vs=FAKE, tables=FAKE,
+             max_blocks=4, lens=FAKE, B=3, Hkv=2, D=128, bs=16, nb=10)
+    a.update(kw)
+    f = lib.pkv_kv_cache_append_fp8
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 5 + \
+        [ctypes.c_int, ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p]
+    return f(a["kn"], a["vn"], a["new_dtype"], a["kp"], a["vp"], a["ks"], a["vs"], a["tables"],
+             a["max_blocks"], a["lens"], a["B"], a["Hkv"], a["D"], a["bs"], a["nb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(new_dtype=3), INVALID), (dict(D=64), UNSUPPORTED), (dict(bs=12), UNSUPPORTED),
+    (dict(ks=0), INVALID), (dict(vs=0), INVALID), (dict(kp=FAKE + 1), INVALID),
+    (dict(B=-1), INVALID), (dict(B=0), OK),
+])
+def test_append_fp8_validation(lib, kw, status):
+    assert append_fp8(lib, **kw) == status
+
+
+def test_copy_blocks_accepts_fp8_pools(lib):
+    # a zero-pair call validates the arguments and enqueues nothing
+    assert copy(lib, dtype=3, n=0, mapping=0) == OK
+    assert copy(lib, dtype=3, D=32) == UNSUPPORTED

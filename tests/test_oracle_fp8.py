@@ -1,0 +1,110 @@
+"""Pins for the oracle's FP8 (OCP E4M3) quantisation, against facts that do
+not come from the oracle: fixed values of the format, torch's independent
+float8_e4m3fn conversion, brute force and round trips."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8_decode, fp8_encode, fp8_quantize, pool_after_append_fp8
+from oracle.fp8 import _encode_one
+
+ALL = np.arange(256, dtype=np.uint8)
+
+
+def torch_decode(codes):
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def torch_encode(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def test_fixed_values_of_the_format():
+    v = fp8_decode(ALL)
+    assert v[0x00] == 0.0 and not np.signbit(v[0x00])
+    assert v[0x80] == 0.0 and np.signbit(v[0x80])
+    assert v[0x01] == 2.0 ** -9                  # smallest subnormal
+    assert v[0x07] == 7 * 2.0 ** -9              # largest subnormal
+    assert v[0x08] == 2.0 ** -6                  # smallest normal
+    assert v[0x38] == 1.0
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.isfinite(v).sum() == 254
+    assert np.all(np.diff(v[:0x7F]) > 0)         # codes 0..126 increase
+
+
+def test_decode_matches_torch_for_every_code():
+    ours, ref = fp8_decode(ALL), torch_decode(ALL)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+    assert np.array_equal(np.signbit(ours[ok]), np.signbit(ref[ok]))
+
+
+def test_encode_matches_torch_in_range():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 0.05, 1.0, 30.0, 150.0)])
+    x = x[np.abs(x) <= 464].astype(np.float32)
+    assert np.array_equal(fp8_encode(x), torch_encode(x))
+
+
+def test_midpoints_round_to_the_even_code():
+    v = fp8_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)     # exact in float32
+    codes = fp8_encode(mids)
+    lower = np.arange(0x7E)
+    want = np.where(lower % 2 == 0, lower, lower + 1)
+    assert np.array_equal(codes, want.astype(np.uint8))
+    assert np.array_equal(codes, torch_encode(mids))
+    assert np.array_equal(fp8_encode(-mids), (want | 0x80).astype(np.uint8))
+
+
+def test_round_trip_of_every_finite_code():
+    finite = ALL[np.isfinite(fp8_decode(ALL))]
+    assert np.array_equal(fp8_encode(fp8_decode(finite)), finite)
+
+
+def test_saturation_signed_zero_and_nan():
+    assert fp8_encode(np.float32(1e6)) == 0x7E and fp8_encode(np.float32(-1e6)) == 0xFE
+    assert fp8_encode(np.float32(470.0)) == 0x7E       # torch gives NaN here; we saturate
+    assert fp8_encode(np.float32(0.0)) == 0x00 and fp8_encode(np.float32(-0.0)) == 0x80
+    assert fp8_encode(np.float32(np.nan)) == 0x7F
+    assert fp8_encode(np.float32(2.0 ** -10)) == 0x00   # half the smallest subnormal: tie to even
+    assert fp8_encode(np.float32(3 * 2.0 ** -10)) == 0x02
+
+
+def test_vectorised_encode_equals_brute_force():
+    rng = np.random.default_rng(2)
+    x = np.concatenate([rng.standard_normal(400) * s for s in (1e-3, 0.1, 5.0, 200.0, 1000.0)])
+    x = x.astype(np.float32)
+    brute = np.array([_encode_one(float(y)) for y in x], dtype=np.uint8)
+    assert np.array_equal(fp8_encode(x), brute)
+
+
+def test_quantize_divides_in_float32():
+    x = np.array([1.0, -3.0, 0.3], dtype=np.float32)
+    s = np.float32(1.0 / 56)
+    y = x / s
+    assert y.dtype == np.float32
+    assert np.array_equal(fp8_quantize(x, s), fp8_encode(y))
+
+
+def test_append_fp8_writes_only_the_new_slots():
+    rng = np.random.default_rng(3)
+    nb, hkv, bs, d = 6, 2, 16, 8
+    k = rng.integers(0, 255, (nb, hkv, bs, d)).astype(np.uint8)
+    v = rng.integers(0, 255, (nb, hkv, bs, d)).astype(np.uint8)
+    tables = np.array([[5, 1, 3], [2, -1, -1], [0, -1, -1]], dtype=np.int32)
+    lens = np.array([37, 16, 0], dtype=np.int32)
+    kn = rng.standard_normal((3, hkv, d)).astype(np.float32)
+    vn = rng.standard_normal((3, hkv, d)).astype(np.float32)
+    ks, vs = np.array([0.02, 0.03], np.float32), np.array([0.05, 0.01], np.float32)
+    k2, v2 = pool_after_append_fp8(k, v, kn, vn, ks, vs, tables, lens, bs)
+    changed = np.argwhere(np.any(k2 != k, axis=-1) | np.any(v2 != v, axis=-1))
+    allowed = {(3, g, 4) for g in range(hkv)} | {(2, g, 15) for g in range(hkv)}
+    assert {tuple(c) for c in changed} <= allowed
+    for g in range(hkv):
+        assert np.array_equal(k2[3, g, 4], torch_encode(kn[0, g] / ks[g]))
+        assert np.array_equal(v2[2, g, 15], torch_encode(vn[1, g] / vs[g]))
