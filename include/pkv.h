@@ -73,7 +73,8 @@ typedef enum {
     PKV_ERR_INVALID = -1,     /* null pointer, negative size, inconsistent arguments */
     PKV_ERR_UNSUPPORTED = -2, /* head_dim / block_size / head grouping / dtype not built */
     PKV_ERR_WORKSPACE = -3,   /* split-K workspace missing, misaligned or too small */
-    PKV_ERR_HIP = -4          /* the HIP runtime reported an error when launching */
+    PKV_ERR_HIP = -4,         /* the HIP runtime reported an error when launching */
+    PKV_ERR_NO_BLOCKS = -5    /* block manager: the pool has no free block */
 } pkv_status;
 
 /*

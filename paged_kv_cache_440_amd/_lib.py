@@ -19,7 +19,7 @@ DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 FP8_E4M3 = 3            # PKV_FP8_E4M3: pools of uint8 E4M3 codes with per-head scales
 POOL_CODES = {**DTYPE_CODES, torch.uint8: FP8_E4M3}
 STATUS = {0: "PKV_OK", -1: "PKV_ERR_INVALID", -2: "PKV_ERR_UNSUPPORTED",
-          -3: "PKV_ERR_WORKSPACE", -4: "PKV_ERR_HIP"}
+          -3: "PKV_ERR_WORKSPACE", -4: "PKV_ERR_HIP", -5: "PKV_ERR_NO_BLOCKS"}
 
 
 class PkvError(RuntimeError):

@@ -139,6 +139,7 @@ const char* pkv_status_string(int status) {
         case PKV_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, head grouping or dtype";
         case PKV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case PKV_ERR_HIP: return "HIP runtime error at launch";
+        case PKV_ERR_NO_BLOCKS: return "no free block in the pool";
         default: return "unknown status";
     }
 }

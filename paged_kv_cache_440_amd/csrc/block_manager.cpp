@@ -1,0 +1,179 @@
+// Host-side block manager for the paged KV cache (declared in
+// include/pkv_block_manager.h): on-demand block allocation from a free
+// stack, per-block reference counts for shared blocks, and copy-on-write of
+// a shared, partly filled last block when a sequence appends to it.
+
+#include "pkv_block_manager.h"
+
+#include <new>
+#include <unordered_map>
+#include <utility>
+#include <vector>
+
+struct pkv_block_manager {
+    int num_blocks;
+    int block_size;
+    std::vector<int32_t> free_stack;          // top = back()
+    std::vector<int32_t> refcount;            // per physical block
+    struct Seq {
+        std::vector<int32_t> table;           // logical -> physical
+        int len = 0;
+    };
+    std::unordered_map<int64_t, Seq> seqs;
+    std::vector<std::pair<int32_t, int32_t>> copies;   // queued (src, dst)
+};
+
+namespace {
+
+int32_t pop_free(pkv_block_manager* bm) {
+    const int32_t b = bm->free_stack.back();
+    bm->free_stack.pop_back();
+    bm->refcount[b] = 1;
+    return b;
+}
+
+void release(pkv_block_manager* bm, int32_t b) {
+    if (--bm->refcount[b] == 0) bm->free_stack.push_back(b);
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_block_manager* pkv_bm_create(int num_blocks, int block_size) {
+    if (num_blocks <= 0 || block_size <= 0) return nullptr;
+    pkv_block_manager* bm = new (std::nothrow) pkv_block_manager;
+    if (!bm) return nullptr;
+    try {
+        bm->num_blocks = num_blocks;
+        bm->block_size = block_size;
+        bm->free_stack.reserve(num_blocks);
+        for (int b = num_blocks - 1; b >= 0; --b) bm->free_stack.push_back(b);
+        bm->refcount.assign(num_blocks, 0);
+    } catch (...) {
+        delete bm;
+        return nullptr;
+    }
+    return bm;
+}
+
+void pkv_bm_destroy(pkv_block_manager* bm) { delete bm; }
+
+int pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id) {
+    if (!bm || bm->seqs.count(seq_id)) return PKV_ERR_INVALID;
+    try {
+        bm->seqs.emplace(seq_id, pkv_block_manager::Seq{});
+    } catch (...) {
+        return PKV_ERR_INVALID;
+    }
+    return PKV_OK;
+}
+
+int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child) {
+    if (!bm || parent == child || bm->seqs.count(child)) return PKV_ERR_INVALID;
+    auto it = bm->seqs.find(parent);
+    if (it == bm->seqs.end()) return PKV_ERR_INVALID;
+    try {
+        pkv_block_manager::Seq s = it->second;
+        bm->seqs.emplace(child, std::move(s));
+    } catch (...) {
+        return PKV_ERR_INVALID;
+    }
+    for (int32_t b : bm->seqs[child].table) ++bm->refcount[b];
+    return PKV_OK;
+}
+
+int pkv_bm_append_token(pkv_block_manager* bm, int64_t seq_id, int32_t* block, int32_t* offset) {
+    if (!bm) return PKV_ERR_INVALID;
+    auto it = bm->seqs.find(seq_id);
+    if (it == bm->seqs.end()) return PKV_ERR_INVALID;
+    pkv_block_manager::Seq& s = it->second;
+    const int slot = s.len % bm->block_size;
+    if (slot == 0) {
+        // the last block is full (or there is none): a fresh block
+        if (bm->free_stack.empty()) return PKV_ERR_NO_BLOCKS;
+        s.table.push_back(pop_free(bm));
+    } else {
+        const int32_t last = s.table.back();
+        if (bm->refcount[last] > 1) {
+            // shared and partly filled: this sequence gets its own copy
+            if (bm->free_stack.empty()) return PKV_ERR_NO_BLOCKS;
+            const int32_t fresh = pop_free(bm);
+            bm->copies.emplace_back(last, fresh);
+            --bm->refcount[last];
+            s.table.back() = fresh;
+        }
+    }
+    ++s.len;
+    if (block) *block = s.table.back();
+    if (offset) *offset = slot;
+    return PKV_OK;
+}
+
+int pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id) {
+    if (!bm) return PKV_ERR_INVALID;
+    auto it = bm->seqs.find(seq_id);
+    if (it == bm->seqs.end()) return PKV_ERR_INVALID;
+    for (int32_t b : it->second.table) release(bm, b);
+    bm->seqs.erase(it);
+    return PKV_OK;
+}
+
+int pkv_bm_num_free_blocks(const pkv_block_manager* bm) {
+    return bm ? (int)bm->free_stack.size() : PKV_ERR_INVALID;
+}
+
+int pkv_bm_seq_len(const pkv_block_manager* bm, int64_t seq_id) {
+    if (!bm) return PKV_ERR_INVALID;
+    auto it = bm->seqs.find(seq_id);
+    return it == bm->seqs.end() ? PKV_ERR_INVALID : it->second.len;
+}
+
+int pkv_bm_refcount(const pkv_block_manager* bm, int32_t block) {
+    if (!bm || block < 0 || block >= bm->num_blocks) return PKV_ERR_INVALID;
+    return bm->refcount[block];
+}
+
+int pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq_id, int32_t* out,
+                       int max_blocks) {
+    if (!bm) return PKV_ERR_INVALID;
+    auto it = bm->seqs.find(seq_id);
+    if (it == bm->seqs.end()) return PKV_ERR_INVALID;
+    const std::vector<int32_t>& t = it->second.table;
+    if ((int)t.size() > max_blocks) return PKV_ERR_WORKSPACE;
+    if (!t.empty() && !out) return PKV_ERR_INVALID;
+    for (size_t i = 0; i < t.size(); ++i) out[i] = t[i];
+    return (int)t.size();
+}
+
+int pkv_bm_take_copies(pkv_block_manager* bm, int32_t* pairs, int max_pairs) {
+    if (!bm || max_pairs < 0 || (max_pairs > 0 && !pairs)) return PKV_ERR_INVALID;
+    const int n = (int)bm->copies.size() < max_pairs ? (int)bm->copies.size() : max_pairs;
+    for (int i = 0; i < n; ++i) {
+        pairs[2 * i] = bm->copies[i].first;
+        pairs[2 * i + 1] = bm->copies[i].second;
+    }
+    bm->copies.erase(bm->copies.begin(), bm->copies.begin() + n);
+    return n;
+}
+
+int pkv_bm_build_batch(const pkv_block_manager* bm, const int64_t* seq_ids, int n,
+                       int32_t* tables, int max_blocks, int32_t* seq_lens) {
+    if (!bm || n < 0 || max_blocks <= 0) return PKV_ERR_INVALID;
+    if (n == 0) return PKV_OK;
+    if (!seq_ids || !tables || !seq_lens) return PKV_ERR_INVALID;
+    for (int i = 0; i < n; ++i) {            // validate everything before writing
+        auto it = bm->seqs.find(seq_ids[i]);
+        if (it == bm->seqs.end()) return PKV_ERR_INVALID;
+        if ((int)it->second.table.size() > max_blocks) return PKV_ERR_WORKSPACE;
+    }
+    for (int i = 0; i < n; ++i) {
+        const pkv_block_manager::Seq& s = bm->seqs.find(seq_ids[i])->second;
+        int32_t* row = tables + (size_t)i * max_blocks;
+        for (int j = 0; j < max_blocks; ++j) row[j] = j < (int)s.table.size() ? s.table[j] : -1;
+        seq_lens[i] = s.len;
+    }
+    return PKV_OK;
+}
+
+}  // extern "C"

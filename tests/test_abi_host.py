@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert _lib.status_string(code) and _lib.status_string(code) != "unknown status"
     assert _lib.status_string(42) == "unknown status"
 

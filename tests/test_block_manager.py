@@ -1,0 +1,83 @@
+"""The C++ block manager (through its C ABI) against the oracle: identical
+tables, lengths, reference counts, free counts and copy-on-write pairs after
+every operation of random workloads. Host only, no GPU."""
+
+import os
+
+import numpy as np
+import pytest
+
+from oracle.block_manager import BlockManagerOracle, NoFreeBlock
+from paged_kv_cache_440_amd.build import LIB_PATH
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH), reason="libpkv.so not built")
+
+
+def _same(bm, orc):
+    assert bm.num_free_blocks() == len(orc.free)
+    for s, table in orc.tables.items():
+        assert bm.block_table(s) == table
+        assert bm.seq_len(s) == orc.lens[s]
+    for b in range(bm.num_blocks):
+        assert bm.refcount(b) == orc.ref[b]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_operations_match_the_oracle(seed):
+    from paged_kv_cache_440_amd.block_manager import BlockManager
+    from paged_kv_cache_440_amd import PkvError
+    rng = np.random.default_rng(seed)
+    nb, bs = int(rng.integers(8, 80)), int(rng.choice([4, 8, 16]))
+    bm, orc = BlockManager(nb, bs), BlockManagerOracle(nb, bs)
+    live, next_id = [], 100
+    for _ in range(600):
+        op = rng.random()
+        if op < 0.08 or not live:
+            bm.add_sequence(next_id); orc.add_sequence(next_id)
+            live.append(next_id); next_id += 1
+        elif op < 0.16:
+            parent = int(rng.choice(live))
+            bm.fork(parent, next_id); orc.fork(parent, next_id)
+            live.append(next_id); next_id += 1
+        elif op < 0.24:
+            s = int(rng.choice(live))
+            bm.free_sequence(s); orc.free_sequence(s)
+            live.remove(s)
+        else:
+            s = int(rng.choice(live))
+            try:
+                want = orc.append_token(s)
+            except NoFreeBlock:
+                with pytest.raises(PkvError):
+                    bm.append_token(s)
+            else:
+                assert bm.append_token(s) == want
+        if rng.random() < 0.2:
+            assert bm.take_copies().tolist() == [list(p) for p in orc.take_copies()]
+        _same(bm, orc)
+    tables, lens = bm.build_batch(live, nb)
+    for i, s in enumerate(live):
+        t = orc.tables[s]
+        assert tables[i, :len(t)].tolist() == t and (tables[i, len(t):] == -1).all()
+        assert lens[i] == orc.lens[s]
+
+
+def test_errors_leave_the_manager_unchanged():
+    from paged_kv_cache_440_amd.block_manager import BlockManager
+    from paged_kv_cache_440_amd import PkvError
+    bm = BlockManager(2, 4)
+    bm.add_sequence(1)
+    with pytest.raises(PkvError):
+        bm.add_sequence(1)
+    with pytest.raises(PkvError):
+        bm.fork(9, 2)
+    with pytest.raises(PkvError):
+        bm.append_token(5)
+    for _ in range(8):
+        bm.append_token(1)
+    with pytest.raises(PkvError) as e:
+        bm.append_token(1)
+    assert e.value.status == -5
+    assert bm.seq_len(1) == 8 and bm.num_free_blocks() == 0
+    with pytest.raises(PkvError):
+        bm.build_batch([1], 1)            # two blocks do not fit one column
