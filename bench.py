@@ -118,6 +118,76 @@ def cpu_baseline(w):
                       f"attention step, float64 numpy, one thread, {dt:.1f} s wall"}
 
 
+def block_manager_bench(steps: int, warmup: int) -> None:
+    """Host bookkeeping of one decode step of the shared-prefix workload:
+    reserve a slot for each of 256 samples (copy-on-write of the shared
+    partial block on the first step), collect the copy pairs and build the
+    launch's block tables. The C++ manager (one call each) against the
+    oracle's plain Python manager on the same operations."""
+    from paged_kv_cache_440_amd.block_manager import BlockManager
+    from oracle.block_manager import BlockManagerOracle
+
+    prompts, samples, prefix, bs = 32, 8, 1032, 16
+    steps = max(1, min(steps, 200))
+    nb = prompts * (prefix // bs + 1) + prompts * samples * (2 + (steps + 1) // bs + 1)
+    ids = [p * samples + s + 1 for p in range(prompts) for s in range(samples)]
+    max_blocks = (prefix + steps + 2 * bs) // bs + 1
+
+    def setup(mgr):
+        for p in range(prompts):
+            root = -(p + 1)
+            mgr.add_sequence(root)
+            for _ in range(prefix):
+                mgr.append_token(root)
+            for s in range(samples):
+                mgr.fork(root, p * samples + s + 1)
+            mgr.free_sequence(root)
+
+    def run(step_fn, n):
+        t0 = time.perf_counter()
+        for _ in range(n):
+            step_fn()
+        return (time.perf_counter() - t0) / n
+
+    bm = BlockManager(nb, bs)
+    setup(bm)
+    ids_np = np.asarray(ids, dtype=np.int64)
+
+    def cxx_step():
+        bm.append_batch(ids_np)
+        bm.take_copies()
+        bm.build_batch(ids_np, max_blocks)
+
+    for _ in range(min(warmup, 5)):
+        cxx_step()
+    cxx = run(cxx_step, steps)
+
+    orc = BlockManagerOracle(nb, bs)
+    setup(orc)
+
+    def oracle_step():
+        for s in ids:
+            orc.append_token(s)
+        orc.take_copies()
+        tables = np.full((len(ids), max_blocks), -1, dtype=np.int32)
+        for i, s in enumerate(ids):
+            tables[i, :len(orc.tables[s])] = orc.tables[s]
+        np.array([orc.lens[s] for s in ids], dtype=np.int32)
+
+    for _ in range(min(warmup, 5)):
+        oracle_step()
+    ora = run(oracle_step, steps)
+    print(json.dumps({
+        "metric": "block manager decode-step bookkeeping (steps/s)", "value": 1.0 / cxx,
+        "unit": "steps/s", "us_per_step": cxx * 1e6, "sequences": len(ids), "steps": steps,
+        "higher_is_better": True, "data": "synthetic",
+        "config": {"workload": "shared_prefix_fp16 bookkeeping", "prompts": prompts,
+                   "samples": samples, "prefix": prefix, "block_size": bs},
+        "cpu_baseline": {"value": 1.0 / ora, "unit": "steps/s", "cores": 1, "kind": "oracle",
+                         "sample": f"the same {steps} steps in the Python oracle manager"},
+    }), flush=True)
+
+
 def copy_probe(mib: int, reps: int) -> None:
     """pkv_probe_copy over `mib` MiB, `reps` times: each dispatch reads and
     writes exactly mib MiB, the reference for scaling FETCH_SIZE/WRITE_SIZE."""
@@ -152,11 +222,18 @@ def main():
                     help="0: one pass per sequence; a multiple of 64: fixed partitions; "
                          "-1: balanced (default: the workload's entry in DEFAULT_SCHEDULE)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block-manager", action="store_true",
+                    help="only time the host block manager's decode-step bookkeeping "
+                         "(parallel sampling: 32 prompts x 8 samples, 1032-token prefix) "
+                         "against the oracle's, and exit (no GPU)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run the plain copy probe over buffers of this many MiB "
                          "(a transfer of known size for scaling traffic counters) and exit")
     args = ap.parse_args()
 
+    if args.block_manager:
+        block_manager_bench(args.steps, args.warmup)
+        return
     if args.gpus != 1:
         log(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
             "this library has no multi-GPU path.")

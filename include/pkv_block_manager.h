@@ -64,6 +64,14 @@ PKV_API int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
 PKV_API int pkv_bm_append_token(pkv_block_manager* bm, int64_t seq_id, int32_t* block,
                                 int32_t* offset);
 
+/* One decode step's worth of pkv_bm_append_token: the slots of the next
+ * token of seq_ids[0..n) (distinct ids) in that order (the same result as n
+ * single calls),
+ * written to blocks[i] / offsets[i]. All or nothing: if the pool cannot
+ * supply every block the step needs, PKV_ERR_NO_BLOCKS and no change. */
+PKV_API int pkv_bm_append_batch(pkv_block_manager* bm, const int64_t* seq_ids, int n,
+                                int32_t* blocks, int32_t* offsets);
+
 /* Drop the sequence: every block's reference count goes down by one, and
  * blocks no longer referenced return to the free stack. */
 PKV_API int pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id);

@@ -27,6 +27,7 @@ def _bind():
     lib.pkv_bm_add_sequence.argtypes = [P, L]
     lib.pkv_bm_fork.argtypes = [P, L, L]
     lib.pkv_bm_append_token.argtypes = [P, L, P, P]
+    lib.pkv_bm_append_batch.argtypes = [P, P, I, P, P]
     lib.pkv_bm_free_sequence.argtypes = [P, L]
     lib.pkv_bm_num_free_blocks.argtypes = [P]
     lib.pkv_bm_seq_len.argtypes = [P, L]
@@ -34,7 +35,7 @@ def _bind():
     lib.pkv_bm_block_table.argtypes = [P, L, P, I]
     lib.pkv_bm_take_copies.argtypes = [P, P, I]
     lib.pkv_bm_build_batch.argtypes = [P, P, I, P, I, P]
-    for name in ("pkv_bm_add_sequence", "pkv_bm_fork", "pkv_bm_append_token",
+    for name in ("pkv_bm_add_sequence", "pkv_bm_fork", "pkv_bm_append_token", "pkv_bm_append_batch",
                  "pkv_bm_free_sequence", "pkv_bm_num_free_blocks", "pkv_bm_seq_len",
                  "pkv_bm_refcount", "pkv_bm_block_table", "pkv_bm_take_copies",
                  "pkv_bm_build_batch"):
@@ -78,6 +79,16 @@ class BlockManager:
         _check("pkv_bm_append_token", self._lib.pkv_bm_append_token(
             self._h, seq_id, ctypes.byref(b), ctypes.byref(o)))
         return b.value, o.value
+
+    def append_batch(self, seq_ids) -> tuple[np.ndarray, np.ndarray]:
+        """append_token for every id in order, all or nothing; returns the
+        (blocks, offsets) arrays."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        blocks = np.empty(len(ids), dtype=np.int32)
+        offsets = np.empty(len(ids), dtype=np.int32)
+        _check("pkv_bm_append_batch", self._lib.pkv_bm_append_batch(
+            self._h, ids.ctypes.data, len(ids), blocks.ctypes.data, offsets.ctypes.data))
+        return blocks, offsets
 
     def free_sequence(self, seq_id: int) -> None:
         _check("pkv_bm_free_sequence", self._lib.pkv_bm_free_sequence(self._h, seq_id))

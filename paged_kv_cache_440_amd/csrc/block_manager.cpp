@@ -110,6 +110,43 @@ int pkv_bm_append_token(pkv_block_manager* bm, int64_t seq_id, int32_t* block, i
     return PKV_OK;
 }
 
+int pkv_bm_append_batch(pkv_block_manager* bm, const int64_t* seq_ids, int n, int32_t* blocks,
+                        int32_t* offsets) {
+    if (!bm || n < 0) return PKV_ERR_INVALID;
+    if (n == 0) return PKV_OK;
+    if (!seq_ids) return PKV_ERR_INVALID;
+    // Dry run: the blocks the step needs, replaying the reference counts of
+    // shared last blocks in order (the last holder of a shared block writes
+    // in place, so only the holders before it need a copy).
+    std::unordered_map<int32_t, int32_t> ref;
+    std::unordered_map<int64_t, int> seen;
+    size_t need = 0;
+    for (int i = 0; i < n; ++i) {
+        auto it = bm->seqs.find(seq_ids[i]);
+        if (it == bm->seqs.end() || seen[seq_ids[i]]++) return PKV_ERR_INVALID;
+        const pkv_block_manager::Seq& s = it->second;
+        if (s.len % bm->block_size == 0) {
+            ++need;
+        } else {
+            const int32_t last = s.table.back();
+            auto r = ref.find(last);
+            int32_t& cnt = r == ref.end() ? (ref[last] = bm->refcount[last]) : r->second;
+            if (cnt > 1) {
+                ++need;
+                --cnt;
+            }
+        }
+    }
+    if (need > bm->free_stack.size()) return PKV_ERR_NO_BLOCKS;
+    for (int i = 0; i < n; ++i) {
+        int32_t b, o;
+        pkv_bm_append_token(bm, seq_ids[i], &b, &o);
+        if (blocks) blocks[i] = b;
+        if (offsets) offsets[i] = o;
+    }
+    return PKV_OK;
+}
+
 int pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id) {
     if (!bm) return PKV_ERR_INVALID;
     auto it = bm->seqs.find(seq_id);
