@@ -180,6 +180,43 @@ PKV_API int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype,
                                pkv_dtype dtype, void* stream);
 
 /*
+ * Several new tokens per sequence (blog.aqudi.me "벤치마크가 다가 아니야!
+ * vLLM으로 보는 LLM 추론 최적화", section 4: chunked prefill feeds a long
+ * prompt in pieces between decode steps; speculative decoding checks several
+ * proposed tokens in one pass of the large model). Sequence i of (new) length
+ * L holds its num_queries (nq) new tokens at positions L-nq .. L-1.
+ *
+ * pkv_kv_cache_append_multi: k_new, v_new [num_seqs][nq][num_kv_heads]
+ * [head_dim]; new token j goes to position L-nq+j (skipped when negative),
+ * bit-exact, as pkv_kv_cache_append does for one token. nq = 1 is that call.
+ *
+ * pkv_paged_attention_multi: q and out [num_seqs][nq][num_heads][head_dim];
+ * new token j (position p = L-nq+j) attends causally to positions 0 .. p:
+ *   out[i][j][h] = sum_{t <= p} softmax_t(scale * q[i][j][h] . K_i[t][g]) V_i[t][g]
+ * (a token with p < 0 gets a zero row). F16 / BF16 K/V and q, head_dim 128,
+ * nq * (num_heads / num_kv_heads) <= 16 (PKV_ERR_UNSUPPORTED otherwise).
+ * partition_size and the workspace work as in pkv_paged_attention_decode;
+ * size the workspace with pkv_paged_attention_workspace_size(num_seqs,
+ * num_heads * nq, num_kv_heads, head_dim, max_seq_len, partition_size).
+ */
+PKV_API int pkv_kv_cache_append_multi(const void* k_new, const void* v_new,
+                              void* k_pool, void* v_pool,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* seq_lens, int num_seqs, int num_queries,
+                              int num_kv_heads, int head_dim, int block_size,
+                              int num_blocks, pkv_dtype dtype, void* stream);
+
+PKV_API int pkv_paged_attention_multi(void* out, pkv_dtype out_dtype, const void* q,
+                              const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* seq_lens, int max_seq_len,
+                              int num_seqs, int num_queries, int num_heads, int num_kv_heads,
+                              int head_dim, int block_size, int num_blocks,
+                              float scale, int partition_size,
+                              void* workspace, size_t workspace_bytes,
+                              pkv_dtype dtype, void* stream);
+
+/*
  * FP8 KV cache (blog.aqudi.me "벤치마크가 다가 아니야! vLLM으로 보는 LLM 추론
  * 최적화", section 4: lowering the precision of the KV cache saves memory
  * and bandwidth). Storage is OCP FP8 E4M3: a code s eeee mmm stands for

@@ -10,7 +10,9 @@ from .paged_attention import (  # noqa: F401
     gather_sequence,
     dense_decode_attention,
     paged_decode_attention,
+    paged_multi_query_attention,
     pool_after_append,
+    pool_after_append_multi,
     pool_after_copy,
 )
 from .fp8 import (  # noqa: F401

@@ -151,3 +151,51 @@ def pool_after_copy(k_pool, v_pool, pairs):
         k_out[int(dst)] = k_out[int(src)]
         v_out[int(dst)] = v_out[int(src)]
     return k_out, v_out
+
+
+def paged_multi_query_attention(q, k_pool, v_pool, block_tables, seq_lens, block_size, scale):
+    """Attention of several new tokens per sequence over a paged pool.
+
+    blog.aqudi.me ("벤치마크가 다가 아니야! vLLM으로 보는 LLM 추론 최적화",
+    section 4): chunked prefill feeds a long prompt in pieces between decode
+    steps, and speculative decoding has the large model check several
+    proposed tokens in one pass; both attend several new tokens of a sequence
+    to its cached history. q: [B][nq][H][D]; seq_lens count all nq new tokens,
+    which sit at positions L-nq .. L-1, so new token j (position L-nq+j) sees
+    the tokens at positions 0 .. L-nq+j -- the causal rule of the summary
+    page's "자기회귀 생성과 KV 캐시" section, current position included. A
+    query whose position is negative (L < nq - j) gets a zero row.
+    Returns float64 [B][nq][H][D].
+    """
+    batch, nq, num_heads, head_dim = q.shape
+    out = np.zeros((batch, nq, num_heads, head_dim), dtype=np.float64)
+    for i in range(batch):
+        n = int(seq_lens[i])
+        for j in range(nq):
+            pos = n - nq + j
+            if pos < 0:
+                continue
+            k = gather_sequence(k_pool, block_tables[i], pos + 1, block_size)
+            v = gather_sequence(v_pool, block_tables[i], pos + 1, block_size)
+            out[i, j] = dense_decode_attention(q[i, j], k, v, scale)
+    return out
+
+
+def pool_after_append_multi(k_pool, v_pool, k_new, v_new, block_tables, seq_lens, block_size):
+    """The pools after each sequence stores nq new tokens: k_new, v_new
+    [B][nq][H_kv][D]; token j goes to position L-nq+j (skipped if negative).
+    Raw (bit-exact) copies, like pool_after_append."""
+    k_out = k_pool.copy()
+    v_out = v_pool.copy()
+    nq = k_new.shape[1]
+    for i in range(len(seq_lens)):
+        n = int(seq_lens[i])
+        for j in range(nq):
+            pos = n - nq + j
+            if pos < 0:
+                continue
+            logical, slot = block_and_slot(pos, block_size)
+            physical = int(block_tables[i][logical])
+            k_out[physical, :, slot, :] = k_new[i, j]
+            v_out[physical, :, slot, :] = v_new[i, j]
+    return k_out, v_out

@@ -9,6 +9,8 @@ names below load it on first use, and fail loudly if it was not built.
 _API = (
     "kv_cache_append",
     "kv_cache_append_fp8",
+    "kv_cache_append_multi",
+    "paged_attention_multi",
     "paged_attention_decode_fp8",
     "FP8_E4M3",
     "copy_blocks",

@@ -55,6 +55,11 @@ def library() -> ctypes.CDLL:
     lib.pkv_paged_attention_decode_fp8.argtypes = [P, I, P, I, P, P, P, P, P, I, P, I, I, I, I, I,
                                                    I, I, F, I, P, Z, P]
     lib.pkv_paged_attention_decode_fp8.restype = I
+    lib.pkv_kv_cache_append_multi.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, I, P]
+    lib.pkv_kv_cache_append_multi.restype = I
+    lib.pkv_paged_attention_multi.argtypes = [P, I, P, P, P, P, I, P, I, I, I, I, I, I, I, I, F,
+                                              I, P, Z, I, P]
+    lib.pkv_paged_attention_multi.restype = I
     lib.pkv_status_string.argtypes = [I]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_probe_read.argtypes = [P, Z, P, P]
@@ -263,4 +268,55 @@ def paged_attention_decode_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), b, h, hkv, d, bs, nb,
         float(scale), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def kv_cache_append_multi(k_new, v_new, k_pool, v_pool, block_tables, seq_lens,
+                          stream=None) -> None:
+    """pkv_kv_cache_append_multi: k_new/v_new [B][nq][Hkv][D]; new token j of
+    sequence i goes to position seq_lens[i] - nq + j."""
+    nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
+    if code == FP8_E4M3:
+        raise TypeError("uint8 (FP8) pools are written by kv_cache_append_fp8")
+    b = block_tables.shape[0]
+    if k_new.dim() != 4 or k_new.shape != v_new.shape or k_new.shape[0] != b or \
+            k_new.shape[2:] != (hkv, d):
+        raise ValueError(f"k_new/v_new must be [{b}][nq][{hkv}][{d}]")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+        raise TypeError("k_new/v_new must have the pool's dtype")
+    if seq_lens.shape != (b,):
+        raise ValueError("seq_lens must be [num_seqs]")
+    _check("pkv_kv_cache_append_multi", library().pkv_kv_cache_append_multi(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens", torch.int32), b, k_new.shape[1], hkv, d, bs, nb, code,
+        _stream(stream)))
+
+
+def paged_attention_multi(out, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len, scale,
+                          partition_size=PARTITION_BALANCED, workspace=None,
+                          stream=None) -> torch.Tensor:
+    """pkv_paged_attention_multi into `out` [B][nq][H][D]: new token j of
+    sequence i (position seq_lens[i] - nq + j) attends causally to the cache."""
+    nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
+    if code == FP8_E4M3:
+        raise TypeError("FP8 pools are not supported by paged_attention_multi")
+    if q.dim() != 4 or q.shape[3] != d or q.dtype != k_pool.dtype:
+        raise ValueError("q must be [num_seqs][nq][num_heads][head_dim] in the pool's dtype")
+    b, nq, h = q.shape[0], q.shape[1], q.shape[2]
+    if out.shape != q.shape or out.dtype not in DTYPE_CODES:
+        raise ValueError("out must be [num_seqs][nq][num_heads][head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or seq_lens.shape != (b,):
+        raise ValueError("block_tables must be [num_seqs][max_blocks], seq_lens [num_seqs]")
+    need = paged_attention_workspace_size(b, h * nq, hkv, d, max_seq_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("pkv_paged_attention_multi", library().pkv_paged_attention_multi(
+        _dev(out, "out"), DTYPE_CODES[out.dtype], _dev(q, "q"), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len),
+        b, nq, h, hkv, d, bs, nb, float(scale), int(partition_size), ws_ptr, ws_bytes, code,
+        _stream(stream)))
     return out

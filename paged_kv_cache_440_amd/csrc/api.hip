@@ -66,7 +66,7 @@ int prepare_attention(pkv::AttnParams& a, void* out, int out_dtype, const void* 
                       int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
                       int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                       int block_size, int num_blocks, float scale, int partition_size,
-                      void* workspace, size_t workspace_bytes) {
+                      void* workspace, size_t workspace_bytes, int num_queries = 1) {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
         partition_size < PKV_PARTITION_BALANCED || !valid_dtype(out_dtype) || !isfinite(scale))
@@ -80,18 +80,21 @@ int prepare_attention(pkv::AttnParams& a, void* out, int out_dtype, const void* 
     if ((long long)max_seq_len > (long long)max_blocks_per_seq * block_size)
         return PKV_ERR_INVALID;
     a.group = group;
+    a.num_queries = num_queries;
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens) return PKV_ERR_INVALID;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_INVALID;
     if ((long long)num_seqs * max_blocks_per_seq > INT32_MAX) return PKV_ERR_INVALID;
-    if ((long long)num_seqs * num_heads * head_dim > INT32_MAX) return PKV_ERR_INVALID;
+    if ((long long)num_seqs * num_queries * num_heads * head_dim > INT32_MAX) return PKV_ERR_INVALID;
+    const int cols = group * num_queries;       // output rows per (sequence, kv head)
 
     const bool balanced = partition_size == PKV_PARTITION_BALANCED;
     const long long parts = balanced ? 1 : parts_for(max_seq_len, partition_size);
     long long items = parts * num_seqs * num_kv_heads;
     if (items > INT32_MAX - 64) return PKV_ERR_INVALID;
-    const size_t need = balanced ? balanced_workspace_bytes(group, head_dim)
-                                 : workspace_bytes_for((long long)num_seqs * num_heads, head_dim, parts);
+    const size_t need =
+        balanced ? balanced_workspace_bytes(cols, head_dim)
+                 : workspace_bytes_for((long long)num_seqs * num_kv_heads * cols, head_dim, parts);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return PKV_ERR_WORKSPACE;
     if (balanced) {
@@ -100,7 +103,7 @@ int prepare_attention(pkv::AttnParams& a, void* out, int out_dtype, const void* 
         if (cus <= 0) return PKV_ERR_HIP;
         items = cus;
     }
-    const size_t rows = balanced ? balanced_record_rows(group)
+    const size_t rows = balanced ? balanced_record_rows(cols)
                                  : need / ((size_t)(head_dim + 2) * sizeof(float));
 
     a.out = out;
@@ -172,6 +175,41 @@ int pkv_kv_cache_append(const void* k_new, const void* v_new, void* k_pool, void
     a.row_bytes = head_dim * dtype_bytes(dtype);
     a.log2_bs = block_log2(block_size);
     a.num_blocks = num_blocks;
+    a.num_queries = 1;
+    return pkv::launch_append(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_kv_cache_append_multi(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* seq_lens, int num_seqs, int num_queries,
+                              int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                              pkv_dtype dtype, void* stream) {
+    if (num_queries <= 0 || num_seqs < 0) return PKV_ERR_INVALID;
+    if ((long long)num_seqs * num_queries > INT32_MAX) return PKV_ERR_INVALID;
+    // the scalar checks of the single-token append (no sequences: nothing enqueued)
+    const int st = pkv_kv_cache_append(k_new, v_new, k_pool, v_pool, block_tables,
+                                       max_blocks_per_seq, seq_lens, 0, num_kv_heads, head_dim,
+                                       block_size, num_blocks, dtype, nullptr);
+    if (st != PKV_OK || num_seqs == 0) return st;
+    if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !seq_lens)
+        return PKV_ERR_INVALID;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PKV_ERR_INVALID;
+    if ((long long)num_seqs * max_blocks_per_seq > INT32_MAX) return PKV_ERR_INVALID;
+    pkv::AppendParams a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = num_kv_heads;
+    a.row_bytes = head_dim * dtype_bytes(dtype);
+    a.log2_bs = block_log2(block_size);
+    a.num_blocks = num_blocks;
+    a.num_queries = num_queries;
     return pkv::launch_append(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -263,6 +301,30 @@ int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
     a.dtype = dtype;
     a.q_dtype = dtype;
     return pkv::launch_paged_attention(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_paged_attention_multi(void* out, pkv_dtype out_dtype, const void* q,
+                              const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* seq_lens, int max_seq_len, int num_seqs,
+                              int num_queries, int num_heads, int num_kv_heads, int head_dim,
+                              int block_size, int num_blocks, float scale, int partition_size,
+                              void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+                              void* stream) {
+    if (!valid_pool_dtype(dtype) || num_queries <= 0) return PKV_ERR_INVALID;
+    pkv::AttnParams a{};
+    const int st = prepare_attention(a, out, out_dtype, q, k_pool, v_pool, block_tables,
+                                     max_blocks_per_seq, seq_lens, max_seq_len, num_seqs, num_heads,
+                                     num_kv_heads, head_dim, block_size, num_blocks, scale,
+                                     partition_size, workspace, workspace_bytes, num_queries);
+    if (st != PKV_OK) return st;
+    if ((dtype != PKV_F16 && dtype != PKV_BF16) || head_dim != 128 || num_queries * a.group > 16)
+        return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PKV_OK;
+    a.dtype = dtype;
+    a.q_dtype = dtype;
+    return pkv::launch_paged_attention_multi(a, (hipStream_t)stream) == hipSuccess ? PKV_OK
+                                                                                   : PKV_ERR_HIP;
 }
 
 int pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype, const void* q,

@@ -21,7 +21,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kCopyUnroll = 4;
 
-// One thread per 16-byte piece of one (sequence, kv head) row of K or of V.
+// One thread per 16-byte piece of one (sequence, new token, kv head) row of
+// K or of V. New token j of a sequence of (new) length L goes to position
+// L - nq + j; positions below 0 are skipped.
 __global__ __launch_bounds__(kThreads)
 void append_kernel(const AppendParams a, long long total) {
     const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
@@ -31,11 +33,13 @@ void append_kernel(const AppendParams a, long long total) {
     long long r = t / pieces;
     const int g = (int)(r % a.num_kv_heads);
     r /= a.num_kv_heads;
+    const int j = (int)(r % a.num_queries);
+    r /= a.num_queries;
     const int seq = (int)(r % a.num_seqs);
     const int which = (int)(r / a.num_seqs);      // 0: K, 1: V
     const int L = a.seq_lens[seq];
-    if (L <= 0) return;
-    const int pos = L - 1;
+    const int pos = L - a.num_queries + j;
+    if (L <= 0 || pos < 0) return;
     const int blk = pos >> a.log2_bs;
     if (blk >= a.max_blocks) return;
     const int phys = a.block_tables[(size_t)seq * a.max_blocks + blk];
@@ -43,7 +47,8 @@ void append_kernel(const AppendParams a, long long total) {
     const int slot = pos & ((1 << a.log2_bs) - 1);
     const size_t row = (((size_t)phys * a.num_kv_heads + g) << a.log2_bs) + (size_t)slot;
     const size_t dst = row * a.row_bytes + (size_t)piece * 16;
-    const size_t src = ((size_t)seq * a.num_kv_heads + g) * a.row_bytes + (size_t)piece * 16;
+    const size_t src = (((size_t)seq * a.num_queries + j) * a.num_kv_heads + g) * a.row_bytes +
+                       (size_t)piece * 16;
     const char* s = reinterpret_cast<const char*>(which ? a.v_new : a.k_new);
     char* d = reinterpret_cast<char*>(which ? a.v_pool : a.k_pool);
     store16(d + dst, load16(s + src));
@@ -167,7 +172,7 @@ void copy_blocks_kernel(const CopyParams a, int chunks_per_block) {
 }  // namespace
 
 hipError_t launch_append(const AppendParams& a, hipStream_t stream) {
-    const long long total = 2LL * a.num_seqs * a.num_kv_heads * (a.row_bytes / 16);
+    const long long total = 2LL * a.num_seqs * a.num_queries * a.num_kv_heads * (a.row_bytes / 16);
     if (total == 0) return hipSuccess;
     const long long blocks = (total + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, total);

@@ -58,7 +58,7 @@ void paged_decode_kernel(const AttnParams a) {
 
     const int L = clamp_len(a, a.seq_lens[seq]);
     if (L == 0) {                                   // padding row: zero output
-        if (part == 0) write_zero_rows<D, G>(a, seq, g, lane);
+        if (part == 0) write_zero_rows<D>(a, seq, g, lane);
         return;
     }
     const int part_len = a.part_tokens > 0 ? a.part_tokens : L;
@@ -74,22 +74,25 @@ void paged_decode_kernel(const AttnParams a) {
     if (nparts == 1) {
         st.write_final(a, seq, g);
     } else {
-        const size_t row0 = ((size_t)seq * a.num_kv_heads * G + (size_t)g * G) * a.max_parts + part;
+        const int cols = a.num_queries * G;
+        const size_t row0 = ((size_t)seq * a.num_kv_heads * cols + (size_t)g * cols) * a.max_parts + part;
         st.write_partial(a, row0, (size_t)a.max_parts);
     }
 }
 
-// Merge the partitions of every (sequence, query head) that has more than one:
+// Merge the partitions of every (segment, column) that has more than one:
 //   M = max_p m_p,  out = sum_p exp2(m_p - M) acc_p / sum_p exp2(m_p - M) l_p
-// One wave per (sequence, head); lane j owns dims j, j + 64, ...
+// One wave per (sequence, kv head, column); lane j owns dims j, j + 64, ...
 template <int D>
 __global__ __launch_bounds__(64 * kWaves)
 void lse_reduce_kernel(const AttnParams a) {
     const int lane = threadIdx.x & 63;
-    const int num_heads = a.num_kv_heads * a.group;
+    const int cols = a.num_queries * a.group;
     const int item = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (item >= a.num_seqs * num_heads) return;
-    const int seq = item / num_heads;
+    if (item >= a.num_seqs * a.num_kv_heads * cols) return;
+    const int seq = item / (a.num_kv_heads * cols);
+    const int g = (item / cols) % a.num_kv_heads;
+    const int n = item % cols;
     const int L = clamp_len(a, a.seq_lens[seq]);
     const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
     if (nparts <= 1) return;
@@ -108,10 +111,10 @@ void lse_reduce_kernel(const AttnParams a) {
 #pragma unroll
         for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(w, acc[lane + 64 * e], o[e]);
     }
-    const float inv = 1.0f / lsum;
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;   // 0: a query before the start
+    const size_t orow = out_row(a, seq, g, n);
 #pragma unroll
-    for (int e = 0; e < PER; ++e)
-        store_out(a.out, a.out_dtype, (size_t)item * D + lane + 64 * e, o[e] * inv);
+    for (int e = 0; e < PER; ++e) store_out(a.out, a.out_dtype, orow * D + lane + 64 * e, o[e] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -171,7 +174,7 @@ void paged_decode_balanced_kernel(const AttnParams a) {
     // sequences w, w + W, ...
     for (int i = w; i < a.num_seqs; i += W)
         if (clamp_len(a, a.seq_lens[i]) == 0)
-            for (int g = 0; g < a.num_kv_heads; ++g) write_zero_rows<Walker::D, G>(a, i, g, lane);
+            for (int g = 0; g < a.num_kv_heads; ++g) write_zero_rows<Walker::D>(a, i, g, lane);
     const long long total = units_before(a, a.num_seqs);
     const long long q = (total + W - 1) / W;
     const long long u0 = (long long)w * q;
@@ -232,7 +235,7 @@ void paged_decode_balanced_kernel(const AttnParams a) {
             st.write_final(a, seq, g);
         } else {
             const size_t rec = 2 * (size_t)w + (k0 == 0 ? 1 : 0);
-            st.write_partial(a, rec * G, 1);
+            st.write_partial(a, rec * (a.num_queries * G), 1);
         }
         u = seg0 + k1;
         if (g == a.num_kv_heads - 1 && u == seg1) {
@@ -242,21 +245,23 @@ void paged_decode_balanced_kernel(const AttnParams a) {
     }
 }
 
-// Finish the balanced schedule. Wave (w, h) merges query head h of the split
+// Finish the balanced schedule. Wave (w, n) merges column n of the split
 // segment that ends in wave w's run, if any (ws_info[2w] = seq * Hkv + g,
 // ws_info[2w + 1] = wf, the first wave holding a piece). Wave wf wrote
-// record 2 wf + 1, waves wf+1 .. w record 2 v. The records are folded in
-// order with the log-sum-exp rule, keeping a running max:
+// record 2 wf + 1, waves wf+1 .. w record 2 v; a record holds one row per
+// column. The records are folded in order with the log-sum-exp rule,
+// keeping a running max:
 //   M' = max(M, m_r),  o' = o e^(M - M') + acc_r e^(m_r - M'),
 //   l' = l e^(M - M') + l_r e^(m_r - M'),  out = o / l  (base-2 exponentials).
 // Lane l owns dims l, l + 64, ...; several records are in flight at once.
-template <int D, int G>
+template <int D>
 __global__ __launch_bounds__(64 * kWaves)
 void balanced_reduce_kernel(const AttnParams a) {
     const int lane = threadIdx.x & 63;
+    const int cols = a.num_queries * a.group;
     const int item = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (item >= a.num_items * G) return;
-    const int w = item / G, h = item % G;
+    if (item >= a.num_items * cols) return;
+    const int w = item / cols, n = item % cols;
     const int seg = a.ws_info[2 * w];
     if (seg < 0) return;
     const int wf = a.ws_info[2 * w + 1];
@@ -266,7 +271,7 @@ void balanced_reduce_kernel(const AttnParams a) {
     for (int k = 0; k < PER; ++k) o[k] = 0.f;
 #pragma unroll 8
     for (int v = wf; v <= w; ++v) {
-        const size_t row = (2 * (size_t)v + (v == wf ? 1 : 0)) * G + h;
+        const size_t row = (2 * (size_t)v + (v == wf ? 1 : 0)) * cols + n;
         const float mr = a.ws_ml[2 * row];
         const float mnew = __builtin_fmaxf(mrun, mr);
         const float keep = (mrun == -__builtin_inff()) ? 0.f : fast_exp2(mrun - mnew);
@@ -277,10 +282,10 @@ void balanced_reduce_kernel(const AttnParams a) {
             o[k] = __builtin_fmaf(take, a.ws_acc[row * D + lane + 64 * k], o[k] * keep);
         mrun = mnew;
     }
-    const size_t out0 = ((size_t)seg * G + h) * D;   // row (seq, g * G + h)
-    const float inv = 1.0f / lsum;
+    const size_t orow = out_row(a, seg / a.num_kv_heads, seg % a.num_kv_heads, n);
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;   // 0: a query before the start
 #pragma unroll
-    for (int k = 0; k < PER; ++k) store_out(a.out, a.out_dtype, out0 + lane + 64 * k, o[k] * inv);
+    for (int k = 0; k < PER; ++k) store_out(a.out, a.out_dtype, orow * D + lane + 64 * k, o[k] * inv);
 }
 
 // Waves of a balanced kernel instance that fit on one compute unit at once
@@ -314,15 +319,16 @@ hipError_t launch_walker(const AttnParams& a_in, hipStream_t stream) {
         const long long w = (long long)a.num_items * per_cu;
         a.num_items = (int)(w < kMaxBalancedWaves ? w : kMaxBalancedWaves);
     }
+    const int cols = a.num_queries * G;
     const int blocks = (a.num_items + kWaves - 1) / kWaves;
-    const int rblocks = (a.num_seqs * a.num_kv_heads * G + kWaves - 1) / kWaves;
+    const int rblocks = (a.num_seqs * a.num_kv_heads * cols + kWaves - 1) / kWaves;
     if (a.balanced) {
         hipLaunchKernelGGL((paged_decode_balanced_kernel<Walker>), dim3(blocks), dim3(64 * kWaves),
                            0, stream, a);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL((balanced_reduce_kernel<D, G>),
-                           dim3((a.num_items * G + kWaves - 1) / kWaves), dim3(64 * kWaves), 0,
+        hipLaunchKernelGGL((balanced_reduce_kernel<D>),
+                           dim3((a.num_items * cols + kWaves - 1) / kWaves), dim3(64 * kWaves), 0,
                            stream, a);
         return hipGetLastError();
     }
@@ -387,7 +393,29 @@ hipError_t launch_fp8_group(const AttnParams& a, hipStream_t stream) {
     }
 }
 
+template <typename S>
+hipError_t launch_multi_group(const AttnParams& a, hipStream_t stream) {
+    switch (a.group) {
+        case 1: return launch_walker<MfmaWalker<S, 1>>(a, stream);
+        case 2: return launch_walker<MfmaWalker<S, 2>>(a, stream);
+        case 4: return launch_walker<MfmaWalker<S, 4>>(a, stream);
+        case 8: return launch_walker<MfmaWalker<S, 8>>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
+
+// Several new tokens per sequence: always the matrix-core walker, whose 16
+// columns hold (new token, query head) pairs with their own causal limits.
+hipError_t launch_paged_attention_multi(const AttnParams& a, hipStream_t stream) {
+    if (a.head_dim != 128 || a.num_queries * a.group > 16) return hipErrorInvalidValue;
+    switch (a.dtype) {
+        case PKV_F16: return launch_multi_group<F16>(a, stream);
+        case PKV_BF16: return launch_multi_group<BF16>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_paged_attention_fp8(const AttnParams& a, hipStream_t stream) {
     if (a.head_dim != 128) return hipErrorInvalidValue;

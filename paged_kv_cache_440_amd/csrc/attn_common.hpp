@@ -28,11 +28,19 @@ __device__ __forceinline__ int clamp_len(const AttnParams& a, int L) {
     return L < a.max_tokens ? L : a.max_tokens;
 }
 
-// Zero output rows of the G query heads of kv head g (padding sequences).
-template <int D, int G>
+// Output row of column n of segment (seq, g): query token n / G, head g*G + n % G.
+__device__ __forceinline__ size_t out_row(const AttnParams& a, int seq, int g, int n) {
+    const int G = a.group;
+    return ((size_t)seq * a.num_queries + n / G) * ((size_t)a.num_kv_heads * G) +
+           (size_t)g * G + n % G;
+}
+
+// Zero the output rows of every column of segment (seq, g) (padding sequences).
+template <int D>
 __device__ __forceinline__ void write_zero_rows(const AttnParams& a, int seq, int g, int lane) {
-    const size_t row0 = (size_t)seq * a.num_kv_heads * G + (size_t)g * G;
-    for (int idx = lane; idx < G * D; idx += 64) store_out(a.out, a.out_dtype, row0 * D + idx, 0.f);
+    const int cols = a.num_queries * a.group;
+    for (int idx = lane; idx < cols * D; idx += 64)
+        store_out(a.out, a.out_dtype, out_row(a, seq, g, idx / D) * D + idx % D, 0.f);
 }
 
 }  // namespace

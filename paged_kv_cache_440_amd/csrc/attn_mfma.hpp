@@ -75,6 +75,7 @@ struct MfmaWalker {
     static constexpr int CHUNK = 32;            // tokens per chunk
     static constexpr int kMinWavesPerSimd = 2;
     static_assert(S::bytes == 2 && G_ <= 16, "16-bit K/V, at most 16 query heads");
+    static constexpr bool kMultiQuery = true;   // handles several new tokens per sequence
 
     f32x4 acc[8];       // O^T tiles: acc[c][i] = head n, dim 32q + 8i + c (unnormalised)
     float m, l;         // head n: running max (log2 units), this lane's partial sum
@@ -89,6 +90,10 @@ struct MfmaWalker {
     int log2_bs, bs_mask, nblk_valid, max_phys;
     int lane, n, q;
     int t_end;
+    int ncols;          // real columns: num_queries * G (the rest are zero padding)
+    int lim;            // last token position column n may see (causal rule)
+    int mask_from;      // first position some column may not see
+    size_t orow;        // output row of column n
 
     __device__ __forceinline__ void init(int lane_id) {
         lane = lane_id;
@@ -106,11 +111,17 @@ struct MfmaWalker {
         kvhead_off = (size_t)g * ((size_t)ROW << a.log2_bs);
         kbase = reinterpret_cast<const char*>(a.k_pool);
         vbase = reinterpret_cast<const char*>(a.v_pool);
-        const char* qrow = reinterpret_cast<const char*>(a.q) +
-                           ((size_t)seq * a.num_kv_heads * G + (size_t)g * G + n) * ROW + 16 * q;
+        // column n = (query token n / G, head g*G + n % G); a new token at
+        // position L - nq + j sees positions <= its own
+        const int nq = a.num_queries;
+        ncols = nq * G;
+        lim = n < ncols ? L - nq + n / G : L - 1;
+        mask_from = L - nq + 1;
+        orow = out_row(a, seq, g, n < ncols ? n : 0);
+        const char* qrow = reinterpret_cast<const char*>(a.q) + orow * ROW + 16 * q;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            qb[s] = n < G ? load16(qrow + 64 * s) : u32x4{0u, 0u, 0u, 0u};
+            qb[s] = n < ncols ? load16(qrow + 64 * s) : u32x4{0u, 0u, 0u, 0u};
         m = -__builtin_inff();
         l = 0.f;
 #pragma unroll
@@ -171,26 +182,38 @@ struct MfmaWalker {
 
     template <bool TAIL>
     __device__ __forceinline__ void softmax_pv(int c0, float (&sc)[8], u32x4 (&vt)[8]) {
+        // Scores are masked by the range end and by column n's causal limit;
+        // V pieces only by the range end: lane n's V piece holds dims
+        // 8n .. 8n+7 of a token for every column, and a token past one
+        // column's limit is still real data (its weight there is 0).
+        bool valid[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int tok = c0 + 16 * (j >> 2) + 4 * q + (j & 3);
+            valid[j] = !TAIL || (tok < t_end && tok <= lim);
+            if constexpr (TAIL) {
+                const bool in_range = tok < t_end;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) vt[j][w] = in_range ? vt[j][w] : 0u;
+            }
+        }
         if constexpr (TAIL) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const bool valid = c0 + 16 * (j >> 2) + 4 * q + (j & 3) < t_end;
-                sc[j] = valid ? sc[j] : -__builtin_inff();
-#pragma unroll
-                for (int w = 0; w < 4; ++w) vt[j][w] = valid ? vt[j][w] : 0u;
-            }
+            for (int j = 0; j < 8; ++j) sc[j] = valid[j] ? sc[j] : -__builtin_inff();
         }
         float mx = sc[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mx = __builtin_fmaxf(mx, sc[j]);
         mx = strided_max<16>(mx);
-        // Token c0 is always valid (q = 0, j = 0), so mx is finite.
+        // Outside masked chunks every token is valid and mx is finite. In a
+        // masked chunk a column may have seen no valid token yet: then m_new is
+        // -inf, every p is 0 and alpha (1) only multiplies zeros.
         const float m_new = __builtin_fmaxf(m, mx);
-        const float alpha = fast_exp2(m - m_new);
+        const float alpha = (TAIL && m_new == -__builtin_inff()) ? 1.f : fast_exp2(m - m_new);
         float p[8], ps = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[j] = fast_exp2(sc[j] - m_new);
+            p[j] = (TAIL && !valid[j]) ? 0.f : fast_exp2(sc[j] - m_new);
             ps += p[j];
         }
         l = l * alpha + ps;
@@ -242,7 +265,10 @@ struct MfmaWalker {
                 if (nx >= w_end) { softmax_pv<true>(c, sc, vt); break; }
                 load_k(nx, kt);
                 __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
-                softmax_pv<false>(c, sc, vt);
+                if (nx > mask_from)                  // causal limits of several new tokens
+                    softmax_pv<true>(c, sc, vt);
+                else
+                    softmax_pv<false>(c, sc, vt);
                 load_v(nx, vt);
                 __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
                 c = nx;
@@ -254,9 +280,10 @@ struct MfmaWalker {
     __device__ __forceinline__ float total_sum() { return strided_sum<16>(l); }
 
     __device__ __forceinline__ void write_final(const AttnParams& a, int seq, int g) {
-        const float inv = 1.0f / total_sum();
-        if (n >= G) return;
-        const size_t base = ((size_t)seq * a.num_kv_heads * G + (size_t)g * G + n) * D + 32 * q;
+        const float lsum = total_sum();
+        const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;   // 0: a query before the start
+        if (n >= ncols) return;
+        const size_t base = orow * D + 32 * q;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -266,7 +293,7 @@ struct MfmaWalker {
     __device__ __forceinline__ void write_partial(const AttnParams& a, size_t row0,
                                                   size_t row_stride) {
         const float lsum = total_sum();
-        if (n >= G) return;
+        if (n >= ncols) return;
         const size_t row = row0 + (size_t)n * row_stride;
         float* dst = a.ws_acc + row * D + 32 * q;
 #pragma unroll

@@ -39,6 +39,9 @@ struct AttnParams {
                                    // balanced: the compute-unit count on entry to the
                                    // launcher, the persistent wave count in the kernels
     int balanced;                  // 1: balanced schedule (see attention.hip)
+    int num_queries;               // new tokens per sequence (1: decode); q and out are
+                                   // [B][num_queries][H][D]. A segment (seq, kv head) has
+                                   // num_queries * group columns (query token, head).
     int dtype;                     // q / K / V element type (16/32-bit path)
     // FP8 pools: K/V are E4M3 codes times a per-kv-head scale; q has q_dtype
     const float* k_scales;
@@ -68,6 +71,7 @@ struct AppendParams {
     int row_bytes;                 // head_dim * element bytes
     int log2_bs;
     int num_blocks;
+    int num_queries;               // new tokens per sequence: k_new is [B][nq][Hkv][D]
 };
 
 // Quantising append into FP8 E4M3 pools.
@@ -102,6 +106,7 @@ hipError_t launch_paged_attention(const AttnParams& a, hipStream_t stream);
 hipError_t launch_append(const AppendParams& a, hipStream_t stream);
 hipError_t launch_append_fp8(const AppendFp8Params& a, hipStream_t stream);
 hipError_t launch_paged_attention_fp8(const AttnParams& a, hipStream_t stream);
+hipError_t launch_paged_attention_multi(const AttnParams& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& a, hipStream_t stream);
 
 }  // namespace pkv

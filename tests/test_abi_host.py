@@ -242,3 +242,41 @@ def test_copy_blocks_accepts_fp8_pools(lib):
     # a zero-pair call validates the arguments and enqueues nothing
     assert copy(lib, dtype=3, n=0, mapping=0) == OK
     assert copy(lib, dtype=3, D=32) == UNSUPPORTED
+
+
+def attn_multi(lib, **kw):
+    a = dict(out=FAKE, out_dtype=0, q=FAKE, k=FAKE, v=FAKE, tables=FAKE, max_blocks=8, lens=FAKE,
+             max_seq_len=100, B=2, nq=4, H=4, Hkv=4, D=128, bs=16, nb=32, scale=0.1, part=0,
+             ws=0, ws_bytes=0, dtype=1)
+    a.update(kw)
+    return _lib.library().pkv_paged_attention_multi(
+        a["out"], a["out_dtype"], a["q"], a["k"], a["v"], a["tables"], a["max_blocks"], a["lens"],
+        a["max_seq_len"], a["B"], a["nq"], a["H"], a["Hkv"], a["D"], a["bs"], a["nb"], a["scale"],
+        a["part"], a["ws"], a["ws_bytes"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nq=0), INVALID), (dict(nq=-1), INVALID),
+    (dict(dtype=0), UNSUPPORTED),              # fp32 K/V
+    (dict(dtype=3), UNSUPPORTED),              # FP8 pools
+    (dict(D=64), UNSUPPORTED),
+    (dict(nq=5, H=16, Hkv=4), UNSUPPORTED),    # 5 tokens x 4 heads > 16 columns
+    (dict(part=64, ws=0), WORKSPACE),
+    (dict(B=0), OK),
+])
+def test_attention_multi_validation(lib, kw, status):
+    assert attn_multi(lib, **kw) == status
+
+
+def test_append_multi_validation(lib):
+    f = _lib.library().pkv_kv_cache_append_multi
+    args = lambda **kw: [kw.get(k, v) for k, v in (
+        ("kn", FAKE), ("vn", FAKE), ("kp", FAKE), ("vp", FAKE), ("tables", FAKE),
+        ("max_blocks", 4), ("lens", FAKE), ("B", 3), ("nq", 2), ("Hkv", 2), ("D", 64),
+        ("bs", 16), ("nb", 10), ("dtype", 1), ("stream", None))]
+    assert f(*args(nq=0)) == INVALID
+    assert f(*args(B=-1)) == INVALID
+    assert f(*args(D=80)) == UNSUPPORTED
+    assert f(*args(kn=0)) == INVALID
+    assert f(*args(vp=FAKE + 2)) == INVALID
+    assert f(*args(B=0)) == OK
