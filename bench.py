@@ -72,6 +72,7 @@ DEFAULT_SCHEDULE = {
     "shared_prefix_fp16": 512,
     "shared_prefix_cow_fp16": 512,
     "opt13b_fp8": 512,
+    "opt13b_spec4_fp16": "balanced",
     "tiny_fp32": 512,
 }
 
@@ -86,8 +87,8 @@ def cpu_baseline(w):
     attention) over the whole batch, single-threaded float64 numpy."""
     import torch
     from threadpoolctl import threadpool_limits
-    from oracle import (fp8_dequantize_pool, paged_decode_attention, pool_after_append,
-                        pool_after_append_fp8)
+    from oracle import (fp8_dequantize_pool, paged_decode_attention, paged_multi_query_attention,
+                        pool_after_append, pool_after_append_fp8, pool_after_append_multi)
 
     def bits(t):
         ints = {1: torch.uint8, 2: torch.int16, 4: torch.int32}
@@ -108,12 +109,17 @@ def cpu_baseline(w):
                                            w.seq_lens, w.block_size)
             kf, vf = fp8_dequantize_pool(k2, ks), fp8_dequantize_pool(v2, vs)
         else:
-            k2, v2 = pool_after_append(kb, vb, bits(w.k_new), bits(w.v_new), w.block_tables,
-                                       w.seq_lens, w.block_size)
+            app = pool_after_append_multi if w.num_queries > 1 else pool_after_append
+            k2, v2 = app(kb, vb, bits(w.k_new), bits(w.v_new), w.block_tables, w.seq_lens,
+                         w.block_size)
             kf, vf = widen(k2), widen(v2)
-        paged_decode_attention(q, kf, vf, w.block_tables, w.seq_lens, w.block_size, w.scale)
+        if w.num_queries > 1:
+            paged_multi_query_attention(q, kf, vf, w.block_tables, w.seq_lens, w.block_size,
+                                        w.scale)
+        else:
+            paged_decode_attention(q, kf, vf, w.block_tables, w.seq_lens, w.block_size, w.scale)
         dt = time.perf_counter() - t0
-    return {"value": w.num_seqs / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": w.num_seqs * w.num_queries / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"the whole batch ({w.num_seqs} sequences, all heads): one append + "
                       f"attention step, float64 numpy, one thread, {dt:.1f} s wall"}
 
@@ -269,13 +275,21 @@ def main():
     lens = torch.from_numpy(w.seq_lens).to(dev)
     pairs = torch.from_numpy(np.ascontiguousarray(w.copy_pairs, np.int32)).to(dev)
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    need = pkv.paged_attention_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
-                                              w.max_seq_len, args.partition)
+    need = pkv.paged_attention_workspace_size(w.num_seqs, w.num_heads * w.num_queries,
+                                              w.num_kv_heads, w.head_dim, w.max_seq_len,
+                                              args.partition)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     max_len = w.max_seq_len
     stream = torch.cuda.current_stream()
 
-    if w.fp8:
+    if w.num_queries > 1:
+        def attention():
+            pkv.paged_attention_multi(out, q, kp, vp, tables, lens, max_len, w.scale,
+                                      partition_size=args.partition, workspace=ws, stream=stream)
+
+        def append():
+            pkv.kv_cache_append_multi(k_new, v_new, kp, vp, tables, lens, stream=stream)
+    elif w.fp8:
         ks, vs = w.k_scales.to(dev), w.v_scales.to(dev)
 
         def attention():
@@ -342,7 +356,7 @@ def main():
 
     kv_bytes = w.kv_bytes()
     achieved = kv_bytes / (attn_ms * 1e-3) / 1e9
-    tokens_per_s = w.num_seqs / (ms_per_step * 1e-3)
+    tokens_per_s = w.num_seqs * w.num_queries / (ms_per_step * 1e-3)
     log(f"[bench] step {ms_per_step * 1e3:.1f} us, attention {attn_ms * 1e3:.1f} us, "
         f"{achieved:.0f} GB/s of KV = {100 * achieved / PEAK_HBM_GBPS:.1f}% of 8 TB/s, "
         f"{tokens_per_s:.0f} tokens/s; read probe {read_ceiling:.0f} GB/s "
@@ -371,6 +385,7 @@ def main():
         "config": {
             "workload": w.name,
             "num_seqs": w.num_seqs,
+            "new_tokens_per_seq": w.num_queries,
             "num_heads": w.num_heads,
             "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim,

@@ -67,6 +67,9 @@ class Workload:
     # FP8 pools: uint8 E4M3 codes; a code of kv head g means value * scale[g]
     k_scales: torch.Tensor | None = None
     v_scales: torch.Tensor | None = None
+    # several new tokens per sequence: k_new, v_new [B][nq][Hkv][D] and
+    # q [B][nq][H][D]; seq_lens count them, they sit at L-nq .. L-1
+    num_queries: int = 1
 
     @property
     def fp8(self) -> bool:
@@ -277,6 +280,25 @@ def long_gqa_fp8(seed=SEED_BASE + 7, block_size=16, num_seqs=16,
                              dist="normal", seed=seed + 1000 * block_size, fp8_spread=8.0)
 
 
+def opt13b_spec4_fp16(seed=SEED_BASE + 8, num_seqs=64, len_range=(32, 2048), nq=4,
+                      block_size=16) -> Workload:
+    """Speculative verification on the OPT-13B layer: each sequence checks
+    nq = 4 proposed tokens in one pass (the cached history as in opt13b_fp16,
+    plus the 4 new tokens), causal among the new tokens."""
+    rng = np.random.default_rng(np.random.SeedSequence(SEED_BASE + 2).spawn(1)[0])
+    lens = rng.integers(len_range[0], len_range[1], size=num_seqs, endpoint=True) + nq - 1
+    w = build_independent("opt13b_spec4_fp16", lens, dtype=torch.float16, num_heads=40,
+                          num_kv_heads=40, head_dim=128, block_size=block_size, dist="normal",
+                          seed=seed + 100_000)
+    r = np.random.default_rng(np.random.SeedSequence(seed).spawn(2)[1])
+    b = w.num_seqs
+    w.k_new = _small_draw(r, (b, nq, 40, 128), torch.float16, "normal")
+    w.v_new = _small_draw(r, (b, nq, 40, 128), torch.float16, "normal")
+    w.q = _small_draw(r, (b, nq, 40, 128), torch.float16, "normal")
+    w.num_queries = nq
+    return w
+
+
 def llama13b_bf16(seed=SEED_BASE + 3, num_seqs=256, median=350.0, sigma=0.9,
                   max_len=4096, block_size=16) -> Workload:
     """LLaMA-13B attention layer: 40 heads of 128, bf16, batch 256, chat-like
@@ -400,6 +422,7 @@ WORKLOADS = {
     "shared_prefix_cow_fp16": shared_prefix_cow_fp16,
     "long_gqa_bf16": long_gqa_bf16,
     "opt13b_fp8": opt13b_fp8,
+    "opt13b_spec4_fp16": opt13b_spec4_fp16,
     "long_gqa_fp8": long_gqa_fp8,
 }
 

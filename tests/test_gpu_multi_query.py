@@ -95,3 +95,19 @@ def test_one_query_equals_decode_on_the_matrix_cores():
     pkv.paged_attention_decode(dec, q[:, 0].contiguous().cuda(), kp, vp, tables, lens,
                                w.max_seq_len, w.scale, partition_size=BAL)
     assert torch.equal(out[:, 0].cpu(), dec.cpu())
+
+
+def test_full_size_speculative_verification_matches_oracle():
+    """The OPT-13B layer verifying 4 proposed tokens per sequence, in the timed
+    configuration (balanced): pools bit-exact, every output within 2e-3."""
+    w = wl.opt13b_spec4_fp16()
+    kp, vp, out = run(w, w.k_new, w.v_new, w.q, BAL)
+    kb, vb = pool_after_append_multi(bits(w.k_pool), bits(w.v_pool), bits(w.k_new),
+                                     bits(w.v_new), w.block_tables, w.seq_lens, w.block_size)
+    assert np.array_equal(bits(kp), kb) and np.array_equal(bits(vp), vb)
+    del kp, vp
+    ref = paged_multi_query_attention(widen(w.q), widen(from_bits(kb, torch.float16)),
+                                      widen(from_bits(vb, torch.float16)), w.block_tables,
+                                      w.seq_lens, w.block_size, w.scale)
+    err = float(np.abs(out.cpu().double().numpy() - ref).max())
+    assert err <= 2e-3, f"max abs error {err:.3e}"
