@@ -194,6 +194,99 @@ def block_manager_bench(steps: int, warmup: int) -> None:
     }), flush=True)
 
 
+PEAK_HOST_LINK_GBPS = 64.0      # PCIe 5.0 x16, one direction
+
+
+def swap_bench(steps: int, warmup: int, with_cpu: bool) -> None:
+    """Swap a quarter of the OPT-13B layer's batch (16 of 64 sequences, all
+    their blocks) out to a pinned host pool and back in, with pkv_swap_blocks
+    (one launch per direction). A step is that round trip. Beside it, one
+    contiguous DMA copy (torch copy_) of the same byte count in each
+    direction: the practical ceiling of the host link."""
+    import torch
+    import paged_kv_cache_440_amd as pkv
+    from paged_kv_cache_440_amd import workloads as wl
+
+    w = wl.opt13b_fp16()
+    preempt = 16
+    used = [-(-int(w.seq_lens[i]) // w.block_size) for i in range(preempt)]
+    blocks = np.concatenate([w.block_tables[i, :used[i]] for i in range(preempt)]).astype(np.int32)
+    n = len(blocks)
+    host = np.arange(n, dtype=np.int32)
+    dk, dv = w.k_pool.cuda(), w.v_pool.cuda()
+    hk = torch.empty((n,) + tuple(dk.shape[1:]), dtype=dk.dtype).pin_memory()
+    hv = torch.empty_like(hk).pin_memory()
+    out_map = torch.from_numpy(np.stack([blocks, host], 1)).cuda()
+    in_map = torch.from_numpy(np.stack([host, blocks], 1)).cuda()
+    block_bytes = dk[0].numel() * dk.element_size()
+    moved = 2 * n * block_bytes                       # K and V, one direction
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3   # us
+
+    swap_out = lambda: pkv.swap_blocks(dk, dv, hk, hv, out_map, stream=stream)
+    swap_in = lambda: pkv.swap_blocks(hk, hv, dk, dv, in_map, stream=stream)
+    for _ in range(warmup):
+        swap_out()
+        swap_in()
+    torch.cuda.synchronize()
+    steps = max(1, steps)
+    t0 = time.perf_counter()
+    out_us = timed(swap_out, steps)
+    in_us = timed(swap_in, steps)
+    wall = time.perf_counter() - t0
+    ok = (torch.equal(hk.view(torch.int16).cuda(), dk.view(torch.int16)[blocks.tolist()]) and
+          torch.equal(hv.view(torch.int16).cuda(), dv.view(torch.int16)[blocks.tolist()]))
+    if not ok:
+        raise SystemExit("swap round trip does not reproduce the blocks")
+    flat_d = torch.empty(moved, dtype=torch.uint8, device="cuda")
+    flat_h = torch.empty(moved, dtype=torch.uint8).pin_memory()
+    d2h_us = timed(lambda: flat_h.copy_(flat_d, non_blocking=True), max(3, steps // 4))
+    h2d_us = timed(lambda: flat_d.copy_(flat_h, non_blocking=True), max(3, steps // 4))
+    gbps = lambda us: moved / us / 1e3
+    value = 2 * moved / (out_us + in_us) / 1e3
+    log(f"[swap] {n} blocks of {block_bytes} B (K and V): out {out_us:.0f} us "
+        f"({gbps(out_us):.1f} GB/s), in {in_us:.0f} us ({gbps(in_us):.1f} GB/s); "
+        f"contiguous DMA d2h {gbps(d2h_us):.1f} GB/s, h2d {gbps(h2d_us):.1f} GB/s")
+    rec = {
+        "metric": "KV block swap throughput, device <-> pinned host (GB/s)", "value": value,
+        "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": (out_us + in_us) / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": DTYPE_NAMES[str(dk.dtype)], "data": "synthetic",
+        "config": {"workload": "opt13b_fp16 swap of 16 of 64 sequences", "blocks": n,
+                   "block_bytes_per_pool": block_bytes, "bytes_per_direction": moved},
+        "swap_out_gbps": gbps(out_us), "swap_in_gbps": gbps(in_us),
+        "dma_d2h_gbps": gbps(d2h_us), "dma_h2d_gbps": gbps(h2d_us),
+        "roofline": {"bound": "host_link", "achieved": value, "peak": PEAK_HOST_LINK_GBPS,
+                     "unit": "GB/s", "frac": value / PEAK_HOST_LINK_GBPS, "traffic": None},
+        "timed_wall_s": wall,
+    }
+    if with_cpu:
+        from oracle import pool_after_swap
+        kp, vp = w.k_pool.view(torch.int16).numpy(), w.v_pool.view(torch.int16).numpy()
+        hkn = np.empty((n,) + kp.shape[1:], dtype=np.int16)
+        hvn = np.empty_like(hkn)
+        pairs_out = np.stack([blocks, host], 1)
+        pairs_in = np.stack([host, blocks], 1)
+        t0 = time.perf_counter()
+        hkn, hvn = pool_after_swap(kp, vp, hkn, hvn, pairs_out)
+        pool_after_swap(hkn, hvn, kp, vp, pairs_in)
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": 2 * moved / dt / 1e9, "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"one round trip of the same {n} blocks, numpy block "
+                                         f"copies on the host, {dt:.2f} s wall"}
+    print(json.dumps(rec), flush=True)
+
+
 def copy_probe(mib: int, reps: int) -> None:
     """pkv_probe_copy over `mib` MiB, `reps` times: each dispatch reads and
     writes exactly mib MiB, the reference for scaling FETCH_SIZE/WRITE_SIZE."""
@@ -232,6 +325,9 @@ def main():
                     help="only time the host block manager's decode-step bookkeeping "
                          "(parallel sampling: 32 prompts x 8 samples, 1032-token prefix) "
                          "against the oracle's, and exit (no GPU)")
+    ap.add_argument("--swap", action="store_true",
+                    help="only time swapping 16 of the OPT-13B layer's 64 sequences out to "
+                         "pinned host memory and back in, and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run the plain copy probe over buffers of this many MiB "
                          "(a transfer of known size for scaling traffic counters) and exit")
@@ -251,6 +347,9 @@ def main():
 
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib, args.steps)
+        return
+    if args.swap:
+        swap_bench(min(args.steps, 50), min(args.warmup, 5), not args.no_cpu_baseline)
         return
 
     if args.partition is None:

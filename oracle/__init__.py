@@ -14,6 +14,7 @@ from .paged_attention import (  # noqa: F401
     pool_after_append,
     pool_after_append_multi,
     pool_after_copy,
+    pool_after_swap,
 )
 from .fp8 import (  # noqa: F401
     decode as fp8_decode,

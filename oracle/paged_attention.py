@@ -153,6 +153,24 @@ def pool_after_copy(k_pool, v_pool, pairs):
     return k_out, v_out
 
 
+def pool_after_swap(src_k, src_v, dst_k, dst_v, pairs):
+    """The destination pools after moving blocks between two pools (a device
+    pool and a host pool, in either direction): swapping preempted sequences
+    to CPU memory and back (supersilo.blog vLLM/PagedAttention summary,
+    section "적용 범위와 관련 연구").
+
+    pairs: [P][2] of (source block of src, destination block of dst); each
+    copies the whole block image of K and of V. The sources are not changed.
+    Returns copies of the destination pools.
+    """
+    k_out = dst_k.copy()
+    v_out = dst_v.copy()
+    for src, dst in np.asarray(pairs).reshape(-1, 2):
+        k_out[int(dst)] = src_k[int(src)]
+        v_out[int(dst)] = src_v[int(src)]
+    return k_out, v_out
+
+
 def paged_multi_query_attention(q, k_pool, v_pool, block_tables, seq_lens, block_size, scale):
     """Attention of several new tokens per sequence over a paged pool.
 

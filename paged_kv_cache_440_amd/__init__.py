@@ -14,6 +14,7 @@ _API = (
     "paged_attention_decode_fp8",
     "FP8_E4M3",
     "copy_blocks",
+    "swap_blocks",
     "paged_attention_decode",
     "paged_attention_workspace_size",
     "status_string",

@@ -60,6 +60,8 @@ def library() -> ctypes.CDLL:
     lib.pkv_paged_attention_multi.argtypes = [P, I, P, P, P, P, I, P, I, I, I, I, I, I, I, I, F,
                                               I, P, Z, I, P]
     lib.pkv_paged_attention_multi.restype = I
+    lib.pkv_swap_blocks.argtypes = [P, P, I, P, P, I, P, I, I, I, I, I, P]
+    lib.pkv_swap_blocks.restype = I
     lib.pkv_status_string.argtypes = [I]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_probe_read.argtypes = [P, Z, P, P]
@@ -144,6 +146,42 @@ def copy_blocks(k_pool, v_pool, block_mapping, stream=None) -> None:
     ptr = _dev(block_mapping, "block_mapping", torch.int32) if n else 0
     _check("pkv_copy_blocks", library().pkv_copy_blocks(
         _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), ptr, n, hkv, d, bs, nb, code,
+        _stream(stream)))
+
+
+def _reachable(t: torch.Tensor, name: str, dtype=None) -> int:
+    """Pointer of a contiguous device tensor or pinned host tensor."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type == "cpu" and not t.is_pinned():
+        raise ValueError(f"{name} is in pageable host memory; allocate it pinned "
+                         "(pin_memory=True) so the device can reach it")
+    if t.device.type not in ("cpu", "cuda"):
+        raise ValueError(f"{name} must be a cuda tensor or a pinned host tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, block_mapping, stream=None) -> None:
+    """pkv_swap_blocks: for each (src, dst) row of block_mapping [P][2],
+    block dst of dst_k/dst_v becomes a copy of block src of src_k/src_v. Each
+    pool (and the mapping) is a device tensor or a pinned host tensor: a
+    device -> host call swaps blocks out, host -> device swaps them in."""
+    snb, hkv, bs, d, code = _pool_geometry(src_k, src_v)
+    dnb, dhkv, dbs, dd, dcode = _pool_geometry(dst_k, dst_v)
+    if (hkv, bs, d, code) != (dhkv, dbs, dd, dcode):
+        raise ValueError("source and destination pools must share kv heads, block size, "
+                         "head dim and dtype")
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [num_pairs][2]")
+    n = block_mapping.shape[0]
+    ptr = _reachable(block_mapping, "block_mapping", torch.int32) if n else 0
+    _check("pkv_swap_blocks", library().pkv_swap_blocks(
+        _reachable(src_k, "src_k"), _reachable(src_v, "src_v"), snb,
+        _reachable(dst_k, "dst_k"), _reachable(dst_v, "dst_v"), dnb, ptr, n, hkv, d, bs, code,
         _stream(stream)))
 
 

@@ -22,6 +22,8 @@ def _bind():
     P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.pkv_bm_create.argtypes = [I, I]
     lib.pkv_bm_create.restype = P
+    lib.pkv_bm_create_swappable.argtypes = [I, I, I]
+    lib.pkv_bm_create_swappable.restype = P
     lib.pkv_bm_destroy.argtypes = [P]
     lib.pkv_bm_destroy.restype = None
     lib.pkv_bm_add_sequence.argtypes = [P, L]
@@ -35,10 +37,16 @@ def _bind():
     lib.pkv_bm_block_table.argtypes = [P, L, P, I]
     lib.pkv_bm_take_copies.argtypes = [P, P, I]
     lib.pkv_bm_build_batch.argtypes = [P, P, I, P, I, P]
+    lib.pkv_bm_swap_out.argtypes = [P, P, I, P, I]
+    lib.pkv_bm_swap_in.argtypes = [P, P, I, P, I]
+    lib.pkv_bm_is_swapped.argtypes = [P, L]
+    lib.pkv_bm_num_free_host_blocks.argtypes = [P]
+    lib.pkv_bm_host_refcount.argtypes = [P, ctypes.c_int32]
     for name in ("pkv_bm_add_sequence", "pkv_bm_fork", "pkv_bm_append_token", "pkv_bm_append_batch",
                  "pkv_bm_free_sequence", "pkv_bm_num_free_blocks", "pkv_bm_seq_len",
                  "pkv_bm_refcount", "pkv_bm_block_table", "pkv_bm_take_copies",
-                 "pkv_bm_build_batch"):
+                 "pkv_bm_build_batch", "pkv_bm_swap_out", "pkv_bm_swap_in", "pkv_bm_is_swapped",
+                 "pkv_bm_num_free_host_blocks", "pkv_bm_host_refcount"):
         getattr(lib, name).restype = I
     _BOUND = True
     return lib
@@ -52,14 +60,17 @@ def _check(fn, status):
 
 class BlockManager:
     """Blocks of a pool of num_blocks blocks of block_size tokens: on-demand
-    allocation, shared blocks with reference counts, copy-on-write."""
+    allocation, shared blocks with reference counts, copy-on-write, and
+    swapping of sequences to a pool of num_host_blocks host blocks."""
 
-    def __init__(self, num_blocks: int, block_size: int):
+    def __init__(self, num_blocks: int, block_size: int, num_host_blocks: int = 0):
         self._lib = _bind()
-        self._h = self._lib.pkv_bm_create(int(num_blocks), int(block_size))
+        self._h = self._lib.pkv_bm_create_swappable(int(num_blocks), int(num_host_blocks),
+                                                    int(block_size))
         if not self._h:
             raise ValueError("invalid pool size or block size")
         self.num_blocks = int(num_blocks)
+        self.num_host_blocks = int(num_host_blocks)
         self.block_size = int(block_size)
 
     def __del__(self):
@@ -103,10 +114,39 @@ class BlockManager:
         return _check("pkv_bm_refcount", self._lib.pkv_bm_refcount(self._h, block))
 
     def block_table(self, seq_id: int) -> list[int]:
-        buf = np.empty(self.num_blocks, dtype=np.int32)
+        """Logical -> physical blocks (host blocks if the sequence is swapped out)."""
+        cap = max(self.num_blocks, self.num_host_blocks)
+        buf = np.empty(cap, dtype=np.int32)
         n = _check("pkv_bm_block_table", self._lib.pkv_bm_block_table(
-            self._h, seq_id, buf.ctypes.data, self.num_blocks))
+            self._h, seq_id, buf.ctypes.data, cap))
         return buf[:n].tolist()
+
+    def _move(self, fn: str, seq_ids, capacity: int) -> np.ndarray:
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        pairs = np.empty((max(capacity, 1), 2), dtype=np.int32)
+        n = _check(fn, getattr(self._lib, fn)(self._h, ids.ctypes.data, len(ids),
+                                              pairs.ctypes.data, capacity))
+        return pairs[:n].copy()
+
+    def swap_out(self, seq_ids) -> np.ndarray:
+        """Move the sequences to host blocks, all or nothing; returns the
+        int32 [P][2] (device block, host block) pairs to copy."""
+        return self._move("pkv_bm_swap_out", seq_ids, self.num_blocks)
+
+    def swap_in(self, seq_ids) -> np.ndarray:
+        """Bring swapped-out sequences back, all or nothing; returns the
+        int32 [P][2] (host block, device block) pairs to copy."""
+        return self._move("pkv_bm_swap_in", seq_ids, self.num_host_blocks)
+
+    def is_swapped(self, seq_id: int) -> bool:
+        return bool(_check("pkv_bm_is_swapped", self._lib.pkv_bm_is_swapped(self._h, seq_id)))
+
+    def num_free_host_blocks(self) -> int:
+        return _check("pkv_bm_num_free_host_blocks",
+                      self._lib.pkv_bm_num_free_host_blocks(self._h))
+
+    def host_refcount(self, block: int) -> int:
+        return _check("pkv_bm_host_refcount", self._lib.pkv_bm_host_refcount(self._h, block))
 
     def take_copies(self) -> np.ndarray:
         """Queued copy-on-write pairs, int32 [P][2] (src, dst), in order."""

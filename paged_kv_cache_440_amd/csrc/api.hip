@@ -1,11 +1,13 @@
 // C-ABI entry points: argument validation, then one launch (or two) on the
-// caller's stream. Declarations and contracts are in include/pkv.h.
+// caller's stream. Declarations and contracts are in include/pkv.h and
+// include/pkv_swap.h.
 
 #include <math.h>
 
 #include <atomic>
 
 #include "pkv_internal.hpp"
+#include "pkv_swap.h"
 
 namespace {
 
@@ -56,6 +58,38 @@ int compute_units() {
         return -1;
     if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
     return n;
+}
+
+// The address a kernel on `device` uses for `bytes` bytes at p: p itself for
+// memory of that device, the mapped address for pinned host memory. Pageable
+// host memory, other devices' memory and ranges that run past the end of
+// their allocation are refused (the kernel would fault on them).
+int device_view(const void* p, size_t bytes, int device, const void** out) {
+    hipPointerAttribute_t attr{};
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();          // an unknown pointer is the caller's error
+        return PKV_ERR_INVALID;
+    }
+    const void* dp;
+    if (attr.type == hipMemoryTypeDevice) {
+        if (attr.device != device) return PKV_ERR_INVALID;
+        dp = p;
+    } else if (attr.type == hipMemoryTypeHost) {
+        if (!attr.devicePointer) return PKV_ERR_INVALID;
+        dp = attr.devicePointer;
+    } else {
+        return PKV_ERR_INVALID;
+    }
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void*>(dp)) != hipSuccess) {
+        (void)hipGetLastError();
+        return PKV_ERR_INVALID;
+    }
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(base), at = reinterpret_cast<uintptr_t>(dp);
+    if (at < lo || at - lo > size || bytes > size - (at - lo)) return PKV_ERR_INVALID;
+    *out = dp;
+    return PKV_OK;
 }
 
 // Validation and parameter setup shared by the attention entry points
@@ -263,12 +297,53 @@ int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapping, in
     const long long chunks = (block_bytes / 16 + 1023) / 1024;
     if (chunks * num_pairs * 2 > INT32_MAX) return PKV_ERR_INVALID;
     pkv::CopyParams a{};
-    a.k_pool = k_pool;
-    a.v_pool = v_pool;
+    a.src_k = a.dst_k = k_pool;
+    a.src_v = a.dst_v = v_pool;
     a.mapping = block_mapping;
     a.num_pairs = num_pairs;
     a.block_bytes = block_bytes;
-    a.num_blocks = num_blocks;
+    a.src_num_blocks = a.dst_num_blocks = num_blocks;
+    return pkv::launch_copy_blocks(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_swap_blocks(const void* src_k, const void* src_v, int src_num_blocks, void* dst_k,
+                    void* dst_v, int dst_num_blocks, const int32_t* block_mapping, int num_pairs,
+                    int num_kv_heads, int head_dim, int block_size, pkv_dtype dtype,
+                    void* stream) {
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        src_num_blocks <= 0 || dst_num_blocks <= 0 || !valid_pool_dtype(dtype))
+        return PKV_ERR_INVALID;
+    if (!supported_head_dim(head_dim) || block_log2(block_size) < 0) return PKV_ERR_UNSUPPORTED;
+    if (num_pairs == 0) return PKV_OK;
+    if (!src_k || !src_v || !dst_k || !dst_v || !block_mapping) return PKV_ERR_INVALID;
+    if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(dst_k) || !aligned16(dst_v))
+        return PKV_ERR_INVALID;
+    const long long block_bytes = (long long)num_kv_heads * block_size * head_dim * dtype_bytes(dtype);
+    const long long chunks = (block_bytes / 16 + 1023) / 1024;
+    if (chunks * num_pairs * 2 > INT32_MAX) return PKV_ERR_INVALID;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return PKV_ERR_HIP;
+    pkv::CopyParams a{};
+    const void* p[5];
+    const void* want[5] = {src_k, src_v, dst_k, dst_v, block_mapping};
+    const size_t bytes[5] = {(size_t)(src_num_blocks * block_bytes),
+                             (size_t)(src_num_blocks * block_bytes),
+                             (size_t)(dst_num_blocks * block_bytes),
+                             (size_t)(dst_num_blocks * block_bytes),
+                             (size_t)num_pairs * 2 * sizeof(int32_t)};
+    for (int i = 0; i < 5; ++i) {
+        const int st = device_view(want[i], bytes[i], device, &p[i]);
+        if (st != PKV_OK) return st;
+    }
+    a.src_k = p[0];
+    a.src_v = p[1];
+    a.dst_k = const_cast<void*>(p[2]);
+    a.dst_v = const_cast<void*>(p[3]);
+    a.mapping = static_cast<const int32_t*>(p[4]);
+    a.num_pairs = num_pairs;
+    a.block_bytes = block_bytes;
+    a.src_num_blocks = src_num_blocks;
+    a.dst_num_blocks = dst_num_blocks;
     return pkv::launch_copy_blocks(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

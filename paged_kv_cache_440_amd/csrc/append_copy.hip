@@ -8,6 +8,9 @@
 //
 // Copy (same page, section "블록 공유"; blog.aqudi.me section 3): a block
 // shared by several sequences is copied before one of them writes to it.
+// Swap (same page, section "적용 범위와 관련 연구"): blocks of preempted
+// sequences move to a pool in pinned host memory and back; the same kernel
+// does it, reading or writing host memory over the host link.
 // A block image is contiguous in the [num_blocks][kv heads][block_size][D]
 // pool, so the copy is one flat run of 16-byte pieces per pair.
 
@@ -141,7 +144,8 @@ void append_fp8_kernel(const AppendFp8Params a, long long total) {
 }
 
 // Grid: chunks_per_block * num_pairs * 2 workgroups; each moves
-// kThreads * kCopyUnroll pieces of one block image of K or of V.
+// kThreads * kCopyUnroll pieces of one block image of K or of V from the
+// source pool to the destination pool (the same pool for copy-on-write).
 __global__ __launch_bounds__(kThreads)
 void copy_blocks_kernel(const CopyParams a, int chunks_per_block) {
     const int chunk = blockIdx.x % chunks_per_block;
@@ -150,10 +154,10 @@ void copy_blocks_kernel(const CopyParams a, int chunks_per_block) {
     const int which = r & 1;
     const int src = a.mapping[2 * pair];
     const int dst = a.mapping[2 * pair + 1];
-    if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
-    char* pool = reinterpret_cast<char*>(which ? a.v_pool : a.k_pool);
-    const char* s = pool + (size_t)src * a.block_bytes;
-    char* d = pool + (size_t)dst * a.block_bytes;
+    if (src < 0 || src >= a.src_num_blocks || dst < 0 || dst >= a.dst_num_blocks) return;
+    const char* s = reinterpret_cast<const char*>(which ? a.src_v : a.src_k) +
+                    (size_t)src * a.block_bytes;
+    char* d = reinterpret_cast<char*>(which ? a.dst_v : a.dst_k) + (size_t)dst * a.block_bytes;
     const long long pieces = a.block_bytes / 16;
     const long long base = (long long)chunk * kThreads * kCopyUnroll + threadIdx.x;
     u32x4 v[kCopyUnroll];

@@ -1,7 +1,8 @@
 // Host-side block manager for the paged KV cache (declared in
 // include/pkv_block_manager.h): on-demand block allocation from a free
-// stack, per-block reference counts for shared blocks, and copy-on-write of
-// a shared, partly filled last block when a sequence appends to it.
+// stack, per-block reference counts for shared blocks, copy-on-write of a
+// shared, partly filled last block when a sequence appends to it, and
+// swapping of whole sequences to a pool of host blocks and back.
 
 #include "pkv_block_manager.h"
 
@@ -12,12 +13,16 @@
 
 struct pkv_block_manager {
     int num_blocks;
+    int num_host_blocks;
     int block_size;
     std::vector<int32_t> free_stack;          // top = back()
     std::vector<int32_t> refcount;            // per physical block
+    std::vector<int32_t> host_free;           // the same for the host pool
+    std::vector<int32_t> host_refcount;
     struct Seq {
-        std::vector<int32_t> table;           // logical -> physical
+        std::vector<int32_t> table;           // logical -> physical (host blocks if swapped)
         int len = 0;
+        bool swapped = false;
     };
     std::unordered_map<int64_t, Seq> seqs;
     std::vector<std::pair<int32_t, int32_t>> copies;   // queued (src, dst)
@@ -36,25 +41,89 @@ void release(pkv_block_manager* bm, int32_t b) {
     if (--bm->refcount[b] == 0) bm->free_stack.push_back(b);
 }
 
+// Give every distinct block held by the sequences ids[0..n) a block of the
+// other pool (device -> host if to_host, else host -> device), in order of
+// first use, and move the sequences' references there; the blocks of the
+// pool they leave are released as by pkv_bm_free_sequence. Writes the
+// (old, new) pairs and returns their number; all or nothing.
+int move_sequences(pkv_block_manager* bm, const int64_t* ids, int n, int32_t* pairs,
+                   int max_pairs, bool to_host) {
+    if (!bm || n < 0 || max_pairs < 0) return PKV_ERR_INVALID;
+    if (n == 0) return 0;
+    if (!ids || !bm->copies.empty()) return PKV_ERR_INVALID;
+    std::vector<pkv_block_manager::Seq*> seqs;
+    std::unordered_map<int32_t, int32_t> where;
+    std::vector<int32_t> order;
+    try {
+        std::unordered_map<int64_t, int> seen;
+        for (int i = 0; i < n; ++i) {
+            auto it = bm->seqs.find(ids[i]);
+            if (it == bm->seqs.end() || seen[ids[i]]++ || it->second.swapped == to_host)
+                return PKV_ERR_INVALID;
+            seqs.push_back(&it->second);
+        }
+        for (auto* s : seqs)
+            for (int32_t b : s->table)
+                if (where.emplace(b, -1).second) order.push_back(b);
+    } catch (...) {
+        return PKV_ERR_INVALID;
+    }
+    std::vector<int32_t>& src_ref = to_host ? bm->refcount : bm->host_refcount;
+    std::vector<int32_t>& src_free = to_host ? bm->free_stack : bm->host_free;
+    std::vector<int32_t>& dst_ref = to_host ? bm->host_refcount : bm->refcount;
+    std::vector<int32_t>& dst_free = to_host ? bm->host_free : bm->free_stack;
+    if (order.size() > dst_free.size()) return PKV_ERR_NO_BLOCKS;
+    if ((int)order.size() > max_pairs) return PKV_ERR_WORKSPACE;
+    if (!order.empty() && !pairs) return PKV_ERR_INVALID;
+    // From here on nothing allocates: the free stacks have their full
+    // capacity reserved.
+    for (size_t k = 0; k < order.size(); ++k) {
+        const int32_t fresh = dst_free.back();
+        dst_free.pop_back();
+        dst_ref[fresh] = 0;
+        where[order[k]] = fresh;
+        pairs[2 * k] = order[k];
+        pairs[2 * k + 1] = fresh;
+    }
+    for (auto* s : seqs) {
+        for (int32_t& b : s->table) {
+            const int32_t fresh = where[b];
+            ++dst_ref[fresh];
+            if (--src_ref[b] == 0) src_free.push_back(b);
+            b = fresh;
+        }
+        s->swapped = to_host;
+    }
+    return (int)order.size();
+}
+
 }  // namespace
 
 extern "C" {
 
-pkv_block_manager* pkv_bm_create(int num_blocks, int block_size) {
-    if (num_blocks <= 0 || block_size <= 0) return nullptr;
+pkv_block_manager* pkv_bm_create_swappable(int num_blocks, int num_host_blocks, int block_size) {
+    if (num_blocks <= 0 || num_host_blocks < 0 || block_size <= 0) return nullptr;
     pkv_block_manager* bm = new (std::nothrow) pkv_block_manager;
     if (!bm) return nullptr;
     try {
         bm->num_blocks = num_blocks;
+        bm->num_host_blocks = num_host_blocks;
         bm->block_size = block_size;
         bm->free_stack.reserve(num_blocks);
         for (int b = num_blocks - 1; b >= 0; --b) bm->free_stack.push_back(b);
         bm->refcount.assign(num_blocks, 0);
+        bm->host_free.reserve(num_host_blocks);
+        for (int b = num_host_blocks - 1; b >= 0; --b) bm->host_free.push_back(b);
+        bm->host_refcount.assign(num_host_blocks, 0);
     } catch (...) {
         delete bm;
         return nullptr;
     }
     return bm;
+}
+
+pkv_block_manager* pkv_bm_create(int num_blocks, int block_size) {
+    return pkv_bm_create_swappable(num_blocks, 0, block_size);
 }
 
 void pkv_bm_destroy(pkv_block_manager* bm) { delete bm; }
@@ -72,7 +141,7 @@ int pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id) {
 int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child) {
     if (!bm || parent == child || bm->seqs.count(child)) return PKV_ERR_INVALID;
     auto it = bm->seqs.find(parent);
-    if (it == bm->seqs.end()) return PKV_ERR_INVALID;
+    if (it == bm->seqs.end() || it->second.swapped) return PKV_ERR_INVALID;
     try {
         pkv_block_manager::Seq s = it->second;
         bm->seqs.emplace(child, std::move(s));
@@ -86,7 +155,7 @@ int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child) {
 int pkv_bm_append_token(pkv_block_manager* bm, int64_t seq_id, int32_t* block, int32_t* offset) {
     if (!bm) return PKV_ERR_INVALID;
     auto it = bm->seqs.find(seq_id);
-    if (it == bm->seqs.end()) return PKV_ERR_INVALID;
+    if (it == bm->seqs.end() || it->second.swapped) return PKV_ERR_INVALID;
     pkv_block_manager::Seq& s = it->second;
     const int slot = s.len % bm->block_size;
     if (slot == 0) {
@@ -123,7 +192,8 @@ int pkv_bm_append_batch(pkv_block_manager* bm, const int64_t* seq_ids, int n, in
     size_t need = 0;
     for (int i = 0; i < n; ++i) {
         auto it = bm->seqs.find(seq_ids[i]);
-        if (it == bm->seqs.end() || seen[seq_ids[i]]++) return PKV_ERR_INVALID;
+        if (it == bm->seqs.end() || it->second.swapped || seen[seq_ids[i]]++)
+            return PKV_ERR_INVALID;
         const pkv_block_manager::Seq& s = it->second;
         if (s.len % bm->block_size == 0) {
             ++need;
@@ -151,9 +221,39 @@ int pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id) {
     if (!bm) return PKV_ERR_INVALID;
     auto it = bm->seqs.find(seq_id);
     if (it == bm->seqs.end()) return PKV_ERR_INVALID;
-    for (int32_t b : it->second.table) release(bm, b);
+    if (it->second.swapped) {
+        for (int32_t b : it->second.table)
+            if (--bm->host_refcount[b] == 0) bm->host_free.push_back(b);
+    } else {
+        for (int32_t b : it->second.table) release(bm, b);
+    }
     bm->seqs.erase(it);
     return PKV_OK;
+}
+
+int pkv_bm_swap_out(pkv_block_manager* bm, const int64_t* seq_ids, int n, int32_t* pairs,
+                    int max_pairs) {
+    return move_sequences(bm, seq_ids, n, pairs, max_pairs, true);
+}
+
+int pkv_bm_swap_in(pkv_block_manager* bm, const int64_t* seq_ids, int n, int32_t* pairs,
+                   int max_pairs) {
+    return move_sequences(bm, seq_ids, n, pairs, max_pairs, false);
+}
+
+int pkv_bm_is_swapped(const pkv_block_manager* bm, int64_t seq_id) {
+    if (!bm) return PKV_ERR_INVALID;
+    auto it = bm->seqs.find(seq_id);
+    return it == bm->seqs.end() ? PKV_ERR_INVALID : (it->second.swapped ? 1 : 0);
+}
+
+int pkv_bm_num_free_host_blocks(const pkv_block_manager* bm) {
+    return bm ? (int)bm->host_free.size() : PKV_ERR_INVALID;
+}
+
+int pkv_bm_host_refcount(const pkv_block_manager* bm, int32_t block) {
+    if (!bm || block < 0 || block >= bm->num_host_blocks) return PKV_ERR_INVALID;
+    return bm->host_refcount[block];
 }
 
 int pkv_bm_num_free_blocks(const pkv_block_manager* bm) {
@@ -201,7 +301,7 @@ int pkv_bm_build_batch(const pkv_block_manager* bm, const int64_t* seq_ids, int 
     if (!seq_ids || !tables || !seq_lens) return PKV_ERR_INVALID;
     for (int i = 0; i < n; ++i) {            // validate everything before writing
         auto it = bm->seqs.find(seq_ids[i]);
-        if (it == bm->seqs.end()) return PKV_ERR_INVALID;
+        if (it == bm->seqs.end() || it->second.swapped) return PKV_ERR_INVALID;
         if ((int)it->second.table.size() > max_blocks) return PKV_ERR_WORKSPACE;
     }
     for (int i = 0; i < n; ++i) {

@@ -93,13 +93,18 @@ struct AppendFp8Params {
     int num_blocks;
 };
 
+// Block copies from one pool pair into another (the same pair for
+// copy-on-write, a device and a host pool for swapping).
 struct CopyParams {
-    void* k_pool;
-    void* v_pool;
+    const void* src_k;
+    const void* src_v;
+    void* dst_k;
+    void* dst_v;
     const int32_t* mapping;
     int num_pairs;
     long long block_bytes;         // num_kv_heads * block_size * row bytes
-    int num_blocks;
+    int src_num_blocks;
+    int dst_num_blocks;
 };
 
 hipError_t launch_paged_attention(const AttnParams& a, hipStream_t stream);

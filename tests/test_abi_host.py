@@ -280,3 +280,33 @@ def test_append_multi_validation(lib):
     assert f(*args(kn=0)) == INVALID
     assert f(*args(vp=FAKE + 2)) == INVALID
     assert f(*args(B=0)) == OK
+
+
+def swap(lib, **kw):
+    a = dict(sk=FAKE, sv=FAKE, snb=10, dk=FAKE, dv=FAKE, dnb=20, mapping=FAKE, n=3, Hkv=2, D=64,
+             bs=16, dtype=1)
+    a.update(kw)
+    return lib.pkv_swap_blocks(a["sk"], a["sv"], a["snb"], a["dk"], a["dv"], a["dnb"],
+                               a["mapping"], a["n"], a["Hkv"], a["D"], a["bs"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), INVALID), (dict(Hkv=0), INVALID), (dict(snb=0), INVALID), (dict(dnb=-2), INVALID),
+    (dict(dtype=9), INVALID), (dict(D=96), UNSUPPORTED), (dict(bs=12), UNSUPPORTED),
+    (dict(sk=0), INVALID), (dict(dv=0), INVALID), (dict(mapping=0), INVALID),
+    (dict(dk=FAKE + 8), INVALID), (dict(n=0, mapping=0), OK), (dict(n=0, dtype=3), OK),
+])
+def test_swap_validation(lib, kw, status):
+    assert swap(lib, **kw) == status
+
+
+def test_swap_refuses_memory_the_device_cannot_reach(lib):
+    """Pageable host memory (a numpy array) and unknown addresses never reach
+    a launch: PKV_ERR_INVALID where a GPU is present, PKV_ERR_HIP where the
+    runtime has no device to ask."""
+    import numpy as np
+    pageable = np.zeros(20 * 2 * 16 * 64, dtype=np.float16)
+    mapping = np.zeros((3, 2), dtype=np.int32)
+    p = pageable.ctypes.data
+    for kw in (dict(), dict(sk=p, sv=p, dk=p, dv=p, mapping=mapping.ctypes.data)):
+        assert swap(lib, **kw) in (INVALID, -4)

@@ -11,6 +11,7 @@ PINS = [name for name in dir(pins) if name.startswith("test_")]
 
 class CopyEvenWhenFull(obm.BlockManagerOracle):
     def append_token(self, seq):
+        assert seq not in self.swapped
         table = self.tables[seq]
         offset = self.lens[seq] % self.block_size
         if table and self.ref[table[-1]] > 1:
@@ -27,6 +28,7 @@ class CopyEvenWhenFull(obm.BlockManagerOracle):
 
 class NoDecrementOnCopy(obm.BlockManagerOracle):
     def append_token(self, seq):
+        assert seq not in self.swapped
         table = self.tables[seq]
         offset = self.lens[seq] % self.block_size
         if offset == 0:
@@ -43,6 +45,7 @@ class NoDecrementOnCopy(obm.BlockManagerOracle):
 class CopyOnEveryPartialWrite(obm.BlockManagerOracle):
     """Copies a partly filled last block on every write, shared or not."""
     def append_token(self, seq):
+        assert seq not in self.swapped
         table = self.tables[seq]
         offset = self.lens[seq] % self.block_size
         if offset == 0:
@@ -61,6 +64,7 @@ class CopyOnEveryPartialWrite(obm.BlockManagerOracle):
 
 class BlockPerToken(obm.BlockManagerOracle):
     def append_token(self, seq):
+        assert seq not in self.swapped
         self.tables[seq].append(self._take())
         self.lens[seq] += 1
         return self.tables[seq][-1], 0
@@ -75,9 +79,55 @@ class FreeInReverse(obm.BlockManagerOracle):
         del self.lens[seq]
 
 
+class SwapKeepsDeviceBlocks(obm.BlockManagerOracle):
+    """Swapping out does not give the device blocks back."""
+    def swap_out(self, seqs):
+        ref, free = list(self.ref), list(self.free)
+        pairs = super().swap_out(seqs)
+        self.ref, self.free = ref, free
+        return pairs
+
+
+class SwapEveryReference(obm.BlockManagerOracle):
+    """One host block per table entry: a shared block moves once per holder."""
+    def _move(self, seqs, to_host):
+        pairs = []
+        for s in seqs:
+            pairs += super()._move([s], to_host)
+        return pairs
+
+
+class SwapInPairsBackwards(obm.BlockManagerOracle):
+    """Swap-in pairs name (device, host) instead of (host, device)."""
+    def swap_in(self, seqs):
+        return [(d, h) for h, d in super().swap_in(seqs)]
+
+
+class SwapPartly(obm.BlockManagerOracle):
+    """Moves the leading sequences that fit instead of refusing the set."""
+    def _move(self, seqs, to_host):
+        seqs = list(seqs)
+        while seqs:
+            try:
+                return super()._move(seqs, to_host)
+            except obm.NoFreeBlock:
+                seqs.pop()
+        return []
+
+
+class SwapForgetsTheHostSide(obm.BlockManagerOracle):
+    """Swapping in never gives the host blocks back."""
+    def swap_in(self, seqs):
+        host_ref, host_free = list(self.host_ref), list(self.host_free)
+        pairs = super().swap_in(seqs)
+        self.host_ref, self.host_free = host_ref, host_free
+        return pairs
+
+
 MUTANTS = {c.__name__: c for c in
            (CopyEvenWhenFull, NoDecrementOnCopy, CopyOnEveryPartialWrite, BlockPerToken,
-            FreeInReverse)}
+            FreeInReverse, SwapKeepsDeviceBlocks, SwapEveryReference, SwapInPairsBackwards,
+            SwapPartly, SwapForgetsTheHostSide)}
 
 
 def _failing():
@@ -91,7 +141,7 @@ def _failing():
         for a in args:
             try:
                 fn(*a)
-            except Exception:
+            except (Exception, pytest.fail.Exception):
                 failed.append(name)
                 break
     return failed
