@@ -46,10 +46,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, partition: int, achieved_bytes: float):
+def measured_traffic(workload: str, partition: int, policy: str):
     """HBM bytes per attention launch from the committed rocprofv3 --pmc
     summary, if it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_p{partition}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_p{partition}_{policy}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -63,7 +63,8 @@ def measured_traffic(workload: str, partition: int, achieved_bytes: float):
 # sequences are long and their lengths spread (few segments per persistent
 # wave); fixed partitions win for many short sequences, for sequences that
 # share prefix blocks (neighbours run side by side and hit the cache) and for
-# the FP8 vector walker.
+# the FP8 vector walker. The K/V load policy follows the workload: cached
+# loads (kv_reuse) where tables share blocks, streaming loads otherwise.
 DEFAULT_SCHEDULE = {
     "opt13b_fp16": "balanced",
     "long_gqa_bf16": "balanced",
@@ -320,6 +321,9 @@ def main():
     ap.add_argument("--partition", type=int, default=None,
                     help="0: one pass per sequence; a multiple of 64: fixed partitions; "
                          "-1: balanced (default: the workload's entry in DEFAULT_SCHEDULE)")
+    ap.add_argument("--kv-policy", choices=("auto", "stream", "reuse"), default="auto",
+                    help="K/V load policy: streaming (non-temporal) or cached loads; auto = "
+                         "cached exactly when the workload's tables share blocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-manager", action="store_true",
                     help="only time the host block manager's decode-step bookkeeping "
@@ -380,11 +384,13 @@ def main():
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     max_len = w.max_seq_len
     stream = torch.cuda.current_stream()
+    reuse = w.shared_blocks if args.kv_policy == "auto" else args.kv_policy == "reuse"
 
     if w.num_queries > 1:
         def attention():
             pkv.paged_attention_multi(out, q, kp, vp, tables, lens, max_len, w.scale,
-                                      partition_size=args.partition, workspace=ws, stream=stream)
+                                      partition_size=args.partition, workspace=ws, stream=stream,
+                                      kv_reuse=reuse)
 
         def append():
             pkv.kv_cache_append_multi(k_new, v_new, kp, vp, tables, lens, stream=stream)
@@ -394,14 +400,15 @@ def main():
         def attention():
             pkv.paged_attention_decode_fp8(out, q, kp, vp, ks, vs, tables, lens, max_len, w.scale,
                                            partition_size=args.partition, workspace=ws,
-                                           stream=stream)
+                                           stream=stream, kv_reuse=reuse)
 
         def append():
             pkv.kv_cache_append_fp8(k_new, v_new, kp, vp, ks, vs, tables, lens, stream=stream)
     else:
         def attention():
             pkv.paged_attention_decode(out, q, kp, vp, tables, lens, max_len, w.scale,
-                                       partition_size=args.partition, workspace=ws, stream=stream)
+                                       partition_size=args.partition, workspace=ws, stream=stream,
+                                       kv_reuse=reuse)
 
         def append():
             pkv.kv_cache_append(k_new, v_new, kp, vp, tables, lens, stream=stream)
@@ -461,7 +468,7 @@ def main():
         f"{tokens_per_s:.0f} tokens/s; read probe {read_ceiling:.0f} GB/s "
         f"({100 * achieved / read_ceiling:.1f}% of it)")
 
-    traffic = measured_traffic(w.name, args.partition, kv_bytes)
+    traffic = measured_traffic(w.name, args.partition, "reuse" if reuse else "stream")
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on the host")
@@ -492,6 +499,7 @@ def main():
             "seq_len_total": int(w.seq_lens.sum()),
             "max_seq_len": w.max_seq_len,
             "partition_size": args.partition,
+            "kv_policy": "reuse" if reuse else "stream",
             "kv_bytes_per_step": kv_bytes,
         },
         "attention_us": attn_ms * 1e3,

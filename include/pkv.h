@@ -117,6 +117,23 @@ PKV_API int pkv_copy_blocks(void* k_pool, void* v_pool,
 #define PKV_PARTITION_BALANCED (-1)
 
 /*
+ * kv_policy of the attention entry points: how K/V are read. It changes
+ * speed only, never a result bit.
+ *   PKV_KV_STREAM  every block is read by one sequence of the batch: K/V are
+ *                  read with non-temporal loads, which stream through the
+ *                  caches without displacing reused data (the fast choice
+ *                  when no block is shared);
+ *   PKV_KV_REUSE   blocks may be shared by several sequences of the batch (a
+ *                  common prompt prefix, parallel sampling; [summary] section
+ *                  "블록 공유"): ordinary cached loads, so that a shared
+ *                  block read by one sequence is found in cache by the
+ *                  others (pair it with fixed partitions, which run
+ *                  neighbouring sequences side by side).
+ */
+#define PKV_KV_STREAM 0
+#define PKV_KV_REUSE 1
+
+/*
  * Bytes of workspace pkv_paged_attention_decode needs for the given sizes and
  * partition_size (0 when it needs none: partition_size == 0, or every
  * sequence fits one partition). Returns 0 for invalid sizes as well. For
@@ -167,6 +184,9 @@ PKV_API size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, i
  * pkv_paged_attention_workspace_size(...) bytes, contents ignored and
  * overwritten) holds the partial results. Work enqueued on `stream` by
  * different calls must not share a workspace unless ordered by the stream.
+ *
+ * kv_policy is PKV_KV_STREAM or PKV_KV_REUSE (see above; PKV_ERR_INVALID
+ * otherwise).
  */
 PKV_API int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype,
                                const void* q,
@@ -177,7 +197,7 @@ PKV_API int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype,
                                int head_dim, int block_size, int num_blocks,
                                float scale, int partition_size,
                                void* workspace, size_t workspace_bytes,
-                               pkv_dtype dtype, void* stream);
+                               pkv_dtype dtype, int kv_policy, void* stream);
 
 /*
  * Several new tokens per sequence (blog.aqudi.me "벤치마크가 다가 아니야!
@@ -195,7 +215,7 @@ PKV_API int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype,
  *   out[i][j][h] = sum_{t <= p} softmax_t(scale * q[i][j][h] . K_i[t][g]) V_i[t][g]
  * (a token with p < 0 gets a zero row). F16 / BF16 K/V and q, head_dim 128,
  * nq * (num_heads / num_kv_heads) <= 16 (PKV_ERR_UNSUPPORTED otherwise).
- * partition_size and the workspace work as in pkv_paged_attention_decode;
+ * partition_size, kv_policy and the workspace work as in pkv_paged_attention_decode;
  * size the workspace with pkv_paged_attention_workspace_size(num_seqs,
  * num_heads * nq, num_kv_heads, head_dim, max_seq_len, partition_size).
  */
@@ -214,7 +234,7 @@ PKV_API int pkv_paged_attention_multi(void* out, pkv_dtype out_dtype, const void
                               int head_dim, int block_size, int num_blocks,
                               float scale, int partition_size,
                               void* workspace, size_t workspace_bytes,
-                              pkv_dtype dtype, void* stream);
+                              pkv_dtype dtype, int kv_policy, void* stream);
 
 /*
  * FP8 KV cache (blog.aqudi.me "벤치마크가 다가 아니야! vLLM으로 보는 LLM 추론
@@ -246,7 +266,8 @@ PKV_API int pkv_kv_cache_append_fp8(const void* k_new, const void* v_new, pkv_dt
  * V_i[t][g] = value(code) * v_scales[g]. q has q_dtype (F32, F16 or BF16);
  * arithmetic is fp32 as in the 16-bit path. head_dim must be 128; with more
  * than one query head per kv head q must be F16 or BF16. The workspace is sized by
- * pkv_paged_attention_workspace_size exactly as for the 16-bit path.
+ * pkv_paged_attention_workspace_size exactly as for the 16-bit path; kv_policy
+ * is as there.
  */
 PKV_API int pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype,
                                const void* q, pkv_dtype q_dtype,
@@ -257,7 +278,8 @@ PKV_API int pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype,
                                int num_seqs, int num_heads, int num_kv_heads,
                                int head_dim, int block_size, int num_blocks,
                                float scale, int partition_size,
-                               void* workspace, size_t workspace_bytes, void* stream);
+                               void* workspace, size_t workspace_bytes, int kv_policy,
+                               void* stream);
 
 /* Static, NUL-terminated description of a pkv_status value. */
 PKV_API const char* pkv_status_string(int status);

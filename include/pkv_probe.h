@@ -3,9 +3,11 @@
  * library (libpkv.so). They compute nothing of attention: they give the
  * memory-system reference points the attention kernel is judged against.
  *
- *   pkv_probe_read   streams a buffer once with 16-byte loads: the practical
+ *   pkv_probe_read   streams a buffer once with 16-byte non-temporal loads
+ *                    (the flavour the attention kernels use for K/V): the practical
  *                    HBM read ceiling for a kernel that only reads.
- *   pkv_probe_copy   copies a buffer with 16-byte loads and stores: a
+ *   pkv_probe_copy   copies a buffer with 16-byte loads (non-temporal, as
+ *                    above) and plain stores: a
  *                    transfer of known size, used to scale hardware traffic
  *                    counters (bytes fetched / written per dispatch) into
  *                    bytes.

@@ -23,6 +23,8 @@ _API = (
     "library",
     "DTYPE_CODES",
     "PARTITION_BALANCED",
+    "KV_STREAM",
+    "KV_REUSE",
     "PkvError",
 )
 

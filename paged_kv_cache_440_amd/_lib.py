@@ -48,17 +48,17 @@ def library() -> ctypes.CDLL:
     lib.pkv_paged_attention_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.pkv_paged_attention_workspace_size.restype = Z
     lib.pkv_paged_attention_decode.argtypes = [P, I, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I,
-                                               P, Z, I, P]
+                                               P, Z, I, I, P]
     lib.pkv_paged_attention_decode.restype = I
     lib.pkv_kv_cache_append_fp8.argtypes = [P, P, I, P, P, P, P, P, I, P, I, I, I, I, I, P]
     lib.pkv_kv_cache_append_fp8.restype = I
     lib.pkv_paged_attention_decode_fp8.argtypes = [P, I, P, I, P, P, P, P, P, I, P, I, I, I, I, I,
-                                                   I, I, F, I, P, Z, P]
+                                                   I, I, F, I, P, Z, I, P]
     lib.pkv_paged_attention_decode_fp8.restype = I
     lib.pkv_kv_cache_append_multi.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, I, P]
     lib.pkv_kv_cache_append_multi.restype = I
     lib.pkv_paged_attention_multi.argtypes = [P, I, P, P, P, P, I, P, I, I, I, I, I, I, I, I, F,
-                                              I, P, Z, I, P]
+                                              I, P, Z, I, I, P]
     lib.pkv_paged_attention_multi.restype = I
     lib.pkv_swap_blocks.argtypes = [P, P, I, P, P, I, P, I, I, I, I, I, P]
     lib.pkv_swap_blocks.restype = I
@@ -186,6 +186,11 @@ def swap_blocks(src_k, src_v, dst_k, dst_v, block_mapping, stream=None) -> None:
 
 
 PARTITION_BALANCED = -1     # PKV_PARTITION_BALANCED
+KV_STREAM, KV_REUSE = 0, 1  # PKV_KV_STREAM, PKV_KV_REUSE
+
+
+def _policy(kv_reuse: bool) -> int:
+    return KV_REUSE if kv_reuse else KV_STREAM
 
 
 def kv_cache_append_fp8(k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens,
@@ -221,12 +226,13 @@ def paged_attention_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, 
 
 def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len, scale,
                            partition_size=PARTITION_BALANCED, workspace=None,
-                           stream=None) -> torch.Tensor:
+                           stream=None, kv_reuse: bool = False) -> torch.Tensor:
     """pkv_paged_attention_decode into `out` [B][H][D] (float32, float16 or
     bfloat16). partition_size: 0 (one pass per sequence), a multiple of 64
     (fixed partitions) or PARTITION_BALANCED (the default). `workspace` (a
     uint8 device tensor) is allocated here when the call needs one and none
-    is given."""
+    is given. kv_reuse: the batch's sequences share blocks (PKV_KV_REUSE:
+    cached K/V loads); by default K/V stream through (PKV_KV_STREAM)."""
     nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
     if code == FP8_E4M3:
         raise TypeError("uint8 (FP8) pools are read by paged_attention_decode_fp8")
@@ -247,7 +253,7 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, max_s
         _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32),
         block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len),
         b, h, hkv, d, bs, nb, float(scale), int(partition_size), ws_ptr, ws_bytes, code,
-        _stream(stream)))
+        _policy(kv_reuse), _stream(stream)))
     return out
 
 
@@ -281,9 +287,10 @@ def probe_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
 
 def paged_attention_decode_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens,
                                max_seq_len, scale, partition_size=PARTITION_BALANCED,
-                               workspace=None, stream=None) -> torch.Tensor:
+                               workspace=None, stream=None, kv_reuse: bool = False) -> torch.Tensor:
     """pkv_paged_attention_decode_fp8 into `out` [B][H][D] over uint8 E4M3
-    pools with per-head float32 scales; q is float32, float16 or bfloat16."""
+    pools with per-head float32 scales; q is float32, float16 or bfloat16.
+    kv_reuse as for paged_attention_decode."""
     nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
     if code != FP8_E4M3:
         raise TypeError("paged_attention_decode_fp8 needs uint8 (FP8) pools")
@@ -305,7 +312,7 @@ def paged_attention_decode_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block
         _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), ks, vs,
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), b, h, hkv, d, bs, nb,
-        float(scale), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+        float(scale), int(partition_size), ws_ptr, ws_bytes, _policy(kv_reuse), _stream(stream)))
     return out
 
 
@@ -333,9 +340,10 @@ def kv_cache_append_multi(k_new, v_new, k_pool, v_pool, block_tables, seq_lens,
 
 def paged_attention_multi(out, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len, scale,
                           partition_size=PARTITION_BALANCED, workspace=None,
-                          stream=None) -> torch.Tensor:
+                          stream=None, kv_reuse: bool = False) -> torch.Tensor:
     """pkv_paged_attention_multi into `out` [B][nq][H][D]: new token j of
-    sequence i (position seq_lens[i] - nq + j) attends causally to the cache."""
+    sequence i (position seq_lens[i] - nq + j) attends causally to the cache.
+    kv_reuse as for paged_attention_decode."""
     nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
     if code == FP8_E4M3:
         raise TypeError("FP8 pools are not supported by paged_attention_multi")
@@ -356,5 +364,5 @@ def paged_attention_multi(out, q, k_pool, v_pool, block_tables, seq_lens, max_se
         _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32),
         block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len),
         b, nq, h, hkv, d, bs, nb, float(scale), int(partition_size), ws_ptr, ws_bytes, code,
-        _stream(stream)))
+        _policy(kv_reuse), _stream(stream)))
     return out

@@ -100,7 +100,9 @@ int prepare_attention(pkv::AttnParams& a, void* out, int out_dtype, const void* 
                       int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
                       int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                       int block_size, int num_blocks, float scale, int partition_size,
-                      void* workspace, size_t workspace_bytes, int num_queries = 1) {
+                      void* workspace, size_t workspace_bytes, int kv_policy,
+                      int num_queries = 1) {
+    if (kv_policy != PKV_KV_STREAM && kv_policy != PKV_KV_REUSE) return PKV_ERR_INVALID;
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
         partition_size < PKV_PARTITION_BALANCED || !valid_dtype(out_dtype) || !isfinite(scale))
@@ -162,6 +164,7 @@ int prepare_attention(pkv::AttnParams& a, void* out, int out_dtype, const void* 
     a.max_tokens = max_seq_len;
     a.num_items = (int)items;
     a.balanced = balanced ? 1 : 0;
+    a.kv_stream = kv_policy == PKV_KV_STREAM ? 1 : 0;
     return PKV_OK;
 }
 
@@ -364,14 +367,15 @@ int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
                                const int32_t* seq_lens, int max_seq_len, int num_seqs,
                                int num_heads, int num_kv_heads, int head_dim, int block_size,
                                int num_blocks, float scale, int partition_size, void* workspace,
-                               size_t workspace_bytes, pkv_dtype dtype, void* stream) {
+                               size_t workspace_bytes, pkv_dtype dtype, int kv_policy,
+                               void* stream) {
     if (!valid_pool_dtype(dtype)) return PKV_ERR_INVALID;
     if (dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;   // see pkv_paged_attention_decode_fp8
     pkv::AttnParams a{};
     const int st = prepare_attention(a, out, out_dtype, q, k_pool, v_pool, block_tables,
                                      max_blocks_per_seq, seq_lens, max_seq_len, num_seqs, num_heads,
                                      num_kv_heads, head_dim, block_size, num_blocks, scale,
-                                     partition_size, workspace, workspace_bytes);
+                                     partition_size, workspace, workspace_bytes, kv_policy);
     if (st != PKV_OK || num_seqs == 0) return st;
     a.dtype = dtype;
     a.q_dtype = dtype;
@@ -385,13 +389,14 @@ int pkv_paged_attention_multi(void* out, pkv_dtype out_dtype, const void* q,
                               int num_queries, int num_heads, int num_kv_heads, int head_dim,
                               int block_size, int num_blocks, float scale, int partition_size,
                               void* workspace, size_t workspace_bytes, pkv_dtype dtype,
-                              void* stream) {
+                              int kv_policy, void* stream) {
     if (!valid_pool_dtype(dtype) || num_queries <= 0) return PKV_ERR_INVALID;
     pkv::AttnParams a{};
     const int st = prepare_attention(a, out, out_dtype, q, k_pool, v_pool, block_tables,
                                      max_blocks_per_seq, seq_lens, max_seq_len, num_seqs, num_heads,
                                      num_kv_heads, head_dim, block_size, num_blocks, scale,
-                                     partition_size, workspace, workspace_bytes, num_queries);
+                                     partition_size, workspace, workspace_bytes, kv_policy,
+                                     num_queries);
     if (st != PKV_OK) return st;
     if ((dtype != PKV_F16 && dtype != PKV_BF16) || head_dim != 128 || num_queries * a.group > 16)
         return PKV_ERR_UNSUPPORTED;
@@ -409,13 +414,14 @@ int pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype, const void* q
                                    const int32_t* seq_lens, int max_seq_len, int num_seqs,
                                    int num_heads, int num_kv_heads, int head_dim, int block_size,
                                    int num_blocks, float scale, int partition_size,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+                                   void* workspace, size_t workspace_bytes, int kv_policy,
+                                   void* stream) {
     if (!valid_dtype(q_dtype)) return PKV_ERR_INVALID;
     pkv::AttnParams a{};
     const int st = prepare_attention(a, out, out_dtype, q, k_pool, v_pool, block_tables,
                                      max_blocks_per_seq, seq_lens, max_seq_len, num_seqs, num_heads,
                                      num_kv_heads, head_dim, block_size, num_blocks, scale,
-                                     partition_size, workspace, workspace_bytes);
+                                     partition_size, workspace, workspace_bytes, kv_policy);
     if (st != PKV_OK) return st;
     if (head_dim != 128) return PKV_ERR_UNSUPPORTED;
     if (q_dtype == PKV_F32 && a.group > 1) return PKV_ERR_UNSUPPORTED;

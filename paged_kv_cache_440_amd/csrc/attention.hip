@@ -340,68 +340,84 @@ hipError_t launch_walker(const AttnParams& a_in, hipStream_t stream) {
 }
 
 // Matrix cores for 16-bit K/V with head_dim 128 and 4 or 8 query heads per
-// kv head; the vector walker otherwise.
-template <typename S, int D, int G>
+// kv head; the vector walker otherwise. STREAM selects the K/V load policy.
+template <typename S, int D, int G, bool STREAM>
 hipError_t launch_typed(const AttnParams& a, hipStream_t stream) {
     if constexpr (S::bytes == 2 && D == 128 && (G == 4 || G == 8))
-        return launch_walker<MfmaWalker<S, G>>(a, stream);
+        return launch_walker<MfmaWalker<S, G, STREAM>>(a, stream);
     else
-        return launch_walker<VecWalker<S, D, G>>(a, stream);
+        return launch_walker<VecWalker<S, D, G, STREAM>>(a, stream);
 }
 
-template <typename S, int D>
+template <typename S, int D, bool STREAM>
 hipError_t launch_group(const AttnParams& a, hipStream_t stream) {
     switch (a.group) {
-        case 1: return launch_typed<S, D, 1>(a, stream);
-        case 2: return launch_typed<S, D, 2>(a, stream);
-        case 4: return launch_typed<S, D, 4>(a, stream);
-        case 8: return launch_typed<S, D, 8>(a, stream);
+        case 1: return launch_typed<S, D, 1, STREAM>(a, stream);
+        case 2: return launch_typed<S, D, 2, STREAM>(a, stream);
+        case 4: return launch_typed<S, D, 4, STREAM>(a, stream);
+        case 8: return launch_typed<S, D, 8, STREAM>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename S, bool STREAM>
+hipError_t launch_dim(const AttnParams& a, hipStream_t stream) {
+    switch (a.head_dim) {
+        case 64: return launch_group<S, 64, STREAM>(a, stream);
+        case 128: return launch_group<S, 128, STREAM>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename S>
-hipError_t launch_dim(const AttnParams& a, hipStream_t stream) {
-    switch (a.head_dim) {
-        case 64: return launch_group<S, 64>(a, stream);
-        case 128: return launch_group<S, 128>(a, stream);
-        default: return hipErrorInvalidValue;
-    }
+hipError_t launch_policy(const AttnParams& a, hipStream_t stream) {
+    return a.kv_stream ? launch_dim<S, true>(a, stream) : launch_dim<S, false>(a, stream);
 }
 
 // FP8 pools: the vector walker for one query head per kv head, the matrix
 // cores for 2, 4 or 8 (q in fp16 / bf16; the entry point rejects fp32 q
 // there). head_dim is 128.
-template <typename Q, int G>
+template <typename Q, int G, bool STREAM>
 hipError_t launch_fp8_typed(const AttnParams& a, hipStream_t stream) {
     if constexpr (G == 1)
-        return launch_walker<Fp8VecWalker<Q, G>>(a, stream);
+        return launch_walker<Fp8VecWalker<Q, G, STREAM>>(a, stream);
     else if constexpr (Q::bytes == 2)
-        return launch_walker<Fp8MfmaWalker<Q, G>>(a, stream);
+        return launch_walker<Fp8MfmaWalker<Q, G, STREAM>>(a, stream);
     else
         return hipErrorInvalidValue;
 }
 
-template <typename Q>
+template <typename Q, bool STREAM>
 hipError_t launch_fp8_group(const AttnParams& a, hipStream_t stream) {
     switch (a.group) {
-        case 1: return launch_fp8_typed<Q, 1>(a, stream);
-        case 2: return launch_fp8_typed<Q, 2>(a, stream);
-        case 4: return launch_fp8_typed<Q, 4>(a, stream);
-        case 8: return launch_fp8_typed<Q, 8>(a, stream);
+        case 1: return launch_fp8_typed<Q, 1, STREAM>(a, stream);
+        case 2: return launch_fp8_typed<Q, 2, STREAM>(a, stream);
+        case 4: return launch_fp8_typed<Q, 4, STREAM>(a, stream);
+        case 8: return launch_fp8_typed<Q, 8, STREAM>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename Q>
+hipError_t launch_fp8_policy(const AttnParams& a, hipStream_t stream) {
+    return a.kv_stream ? launch_fp8_group<Q, true>(a, stream) : launch_fp8_group<Q, false>(a, stream);
+}
+
+template <typename S, bool STREAM>
+hipError_t launch_multi_group(const AttnParams& a, hipStream_t stream) {
+    switch (a.group) {
+        case 1: return launch_walker<MfmaWalker<S, 1, STREAM>>(a, stream);
+        case 2: return launch_walker<MfmaWalker<S, 2, STREAM>>(a, stream);
+        case 4: return launch_walker<MfmaWalker<S, 4, STREAM>>(a, stream);
+        case 8: return launch_walker<MfmaWalker<S, 8, STREAM>>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename S>
-hipError_t launch_multi_group(const AttnParams& a, hipStream_t stream) {
-    switch (a.group) {
-        case 1: return launch_walker<MfmaWalker<S, 1>>(a, stream);
-        case 2: return launch_walker<MfmaWalker<S, 2>>(a, stream);
-        case 4: return launch_walker<MfmaWalker<S, 4>>(a, stream);
-        case 8: return launch_walker<MfmaWalker<S, 8>>(a, stream);
-        default: return hipErrorInvalidValue;
-    }
+hipError_t launch_multi_policy(const AttnParams& a, hipStream_t stream) {
+    return a.kv_stream ? launch_multi_group<S, true>(a, stream)
+                       : launch_multi_group<S, false>(a, stream);
 }
 
 }  // namespace
@@ -411,8 +427,8 @@ hipError_t launch_multi_group(const AttnParams& a, hipStream_t stream) {
 hipError_t launch_paged_attention_multi(const AttnParams& a, hipStream_t stream) {
     if (a.head_dim != 128 || a.num_queries * a.group > 16) return hipErrorInvalidValue;
     switch (a.dtype) {
-        case PKV_F16: return launch_multi_group<F16>(a, stream);
-        case PKV_BF16: return launch_multi_group<BF16>(a, stream);
+        case PKV_F16: return launch_multi_policy<F16>(a, stream);
+        case PKV_BF16: return launch_multi_policy<BF16>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -420,18 +436,18 @@ hipError_t launch_paged_attention_multi(const AttnParams& a, hipStream_t stream)
 hipError_t launch_paged_attention_fp8(const AttnParams& a, hipStream_t stream) {
     if (a.head_dim != 128) return hipErrorInvalidValue;
     switch (a.q_dtype) {
-        case PKV_F32: return launch_fp8_group<F32>(a, stream);
-        case PKV_F16: return launch_fp8_group<F16>(a, stream);
-        case PKV_BF16: return launch_fp8_group<BF16>(a, stream);
+        case PKV_F32: return launch_fp8_policy<F32>(a, stream);
+        case PKV_F16: return launch_fp8_policy<F16>(a, stream);
+        case PKV_BF16: return launch_fp8_policy<BF16>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_paged_attention(const AttnParams& a, hipStream_t stream) {
     switch (a.dtype) {
-        case PKV_F32: return launch_dim<F32>(a, stream);
-        case PKV_F16: return launch_dim<F16>(a, stream);
-        case PKV_BF16: return launch_dim<BF16>(a, stream);
+        case PKV_F32: return launch_policy<F32>(a, stream);
+        case PKV_F16: return launch_policy<F16>(a, stream);
+        case PKV_BF16: return launch_policy<BF16>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

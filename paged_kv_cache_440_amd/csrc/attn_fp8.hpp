@@ -14,7 +14,6 @@ namespace pkv {
 namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // the four E4M3 codes of a dword as float32, in byte order
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
@@ -46,7 +45,7 @@ template <> __device__ __forceinline__ float q_elem<BF16>(const char* row, int i
 // to float32 and pre-multiplied by scale * log2(e) * k_scale, so a score is
 // one 16-term FMA chain plus a 3-step DPP row sum. Softmax bookkeeping is
 // that of the 16-bit vector walker (token classes merged at the end).
-template <typename Q, int G_>
+template <typename Q, int G_, bool STREAM>
 struct Fp8VecWalker {
     static constexpr int D = 128, G = G_;
     static constexpr int ROW = 128, LPT = 8, TPL = 8, NLOAD = 4, CHUNK = TPL * NLOAD, EPL = 16;
@@ -115,8 +114,8 @@ struct Fp8VecWalker {
             const uint32_t p = phys(tg >> log2_bs);
             const size_t blk_off = (size_t)p * head_stride_bytes + kvhead_off;
             const uint32_t off = (uint32_t)(((tg & bs_mask) + tok) * ROW + piece * 16);
-            kr[j] = load16(kbase + blk_off + off);
-            vr[j] = load16(vbase + blk_off + off);
+            kr[j] = load16_kv<STREAM>(kbase + blk_off + off);
+            vr[j] = load16_kv<STREAM>(vbase + blk_off + off);
         }
     }
 
@@ -255,7 +254,7 @@ struct Fp8VecWalker {
 //     bytes 16q or 64 + 16q of the row): one 16-byte load gives two steps.
 //   V: lane (n, q) loads the 8 codes of dims 8n .. 8n+7 of each of its
 //     tokens (an 8-byte load); tile c takes code c of the eight tokens.
-template <typename Q, int G_>
+template <typename Q, int G_, bool STREAM>
 struct Fp8MfmaWalker {
     static constexpr int D = 128, G = G_;
     static constexpr int ROW = 128;
@@ -333,8 +332,8 @@ struct Fp8MfmaWalker {
             const int tok = c0 + 16 * t + n;
             const char* p = kbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes +
                             kvhead_off + (uint32_t)((tok & bs_mask) * ROW + 16 * q);
-            kt[t][0] = load16(p);
-            kt[t][1] = load16(p + 64);
+            kt[t][0] = load16_kv<STREAM>(p);
+            kt[t][1] = load16_kv<STREAM>(p + 64);
         }
     }
 
@@ -346,7 +345,7 @@ struct Fp8MfmaWalker {
             const char* p = vbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes +
                             kvhead_off + (uint32_t)((tok & bs_mask) * ROW + 8 * n);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vt[4 * h + j] = *reinterpret_cast<const u32x2*>(p + ROW * j);
+            for (int j = 0; j < 4; ++j) vt[4 * h + j] = load8_kv<STREAM>(p + ROW * j);
         }
     }
 

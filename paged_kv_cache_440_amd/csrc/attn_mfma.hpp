@@ -68,7 +68,7 @@ __device__ __forceinline__ float from16(F16, uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-template <typename S, int G_>
+template <typename S, int G_, bool STREAM>
 struct MfmaWalker {
     static constexpr int D = 128, G = G_;
     static constexpr int ROW = 256;             // bytes of one token row of one kv head
@@ -147,7 +147,7 @@ struct MfmaWalker {
             const char* p = kbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes +
                             kvhead_off + (uint32_t)((tok & bs_mask) * ROW + 16 * q);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) kt[t][s] = load16(p + 64 * s);
+            for (int s = 0; s < 4; ++s) kt[t][s] = load16_kv<STREAM>(p + 64 * s);
         }
     }
 
@@ -160,7 +160,7 @@ struct MfmaWalker {
             const char* p = vbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes +
                             kvhead_off + (uint32_t)((tok & bs_mask) * ROW + 16 * n);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vt[4 * h + j] = load16(p + ROW * j);
+            for (int j = 0; j < 4; ++j) vt[4 * h + j] = load16_kv<STREAM>(p + ROW * j);
         }
     }
 

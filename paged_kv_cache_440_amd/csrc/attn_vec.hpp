@@ -45,7 +45,7 @@ struct Geo {
     static_assert(LPT >= 8 && LPT <= 32, "row must span 8..32 lanes");
 };
 
-template <typename S, int D_, int G_>
+template <typename S, int D_, int G_, bool STREAM>
 struct VecWalker {
     static constexpr int D = D_, G = G_;
     using Gm = Geo<S, D_>;
@@ -97,8 +97,8 @@ struct VecWalker {
             const uint32_t p = phys(tg >> log2_bs);
             const size_t blk_off = (size_t)p * head_stride_bytes + kvhead_off;
             const uint32_t off = (uint32_t)(((tg & bs_mask) + tok) * Gm::ROW + piece * 16);
-            kr[j] = load16(kbase + blk_off + off);
-            vr[j] = load16(vbase + blk_off + off);
+            kr[j] = load16_kv<STREAM>(kbase + blk_off + off);
+            vr[j] = load16_kv<STREAM>(vbase + blk_off + off);
         }
     }
 

@@ -8,6 +8,7 @@
 namespace pkv {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -86,6 +87,25 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 }
 __device__ __forceinline__ void store16(void* p, const u32x4& v) {
     *reinterpret_cast<u32x4*>(p) = v;
+}
+// Loads of K/V data. STREAM: non-temporal loads, for calls that read each
+// K/V byte once (the lines take the streaming replacement policy instead of
+// displacing data that is reused); otherwise ordinary cached loads, for
+// batches whose sequences share blocks (a shared prompt prefix), which then
+// come from cache after the first reader.
+template <bool STREAM>
+__device__ __forceinline__ u32x4 load16_kv(const void* p) {
+    if constexpr (STREAM)
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else
+        return *reinterpret_cast<const u32x4*>(p);
+}
+template <bool STREAM>
+__device__ __forceinline__ u32x2 load8_kv(const void* p) {
+    if constexpr (STREAM)
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    else
+        return *reinterpret_cast<const u32x2*>(p);
 }
 
 // -- cross-lane reductions inside a wave64 ---------------------------------

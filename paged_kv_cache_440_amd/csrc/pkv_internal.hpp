@@ -39,6 +39,7 @@ struct AttnParams {
                                    // balanced: the compute-unit count on entry to the
                                    // launcher, the persistent wave count in the kernels
     int balanced;                  // 1: balanced schedule (see attention.hip)
+    int kv_stream;                 // 1: non-temporal K/V loads (PKV_KV_STREAM), 0: cached
     int num_queries;               // new tokens per sequence (1: decode); q and out are
                                    // [B][num_queries][H][D]. A segment (seq, kv head) has
                                    // num_queries * group columns (query token, head).

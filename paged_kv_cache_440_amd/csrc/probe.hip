@@ -1,6 +1,7 @@
 // Memory-system reference kernels (declared in include/pkv_probe.h): a
 // read-only stream that gives the practical HBM read ceiling, and a plain
-// copy of known size for scaling traffic counters.
+// copy of known size for scaling traffic counters. Both read with the
+// non-temporal 16-byte loads the attention kernels use for K/V.
 
 #include "pkv_probe.h"
 #include "pkv_device.hpp"
@@ -31,7 +32,7 @@ void probe_read_kernel(const u32x4* __restrict__ src, long long pieces, uint32_t
 #pragma unroll
         for (int u = 0; u < kProbeUnroll; ++u) {
             const long long p = base + (long long)u * kProbeThreads + threadIdx.x;
-            v[u] = p < pieces ? src[p] : u32x4{0u, 0u, 0u, 0u};
+            v[u] = p < pieces ? __builtin_nontemporal_load(src + p) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < kProbeUnroll; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
@@ -56,7 +57,7 @@ void probe_copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src, l
 #pragma unroll
         for (int u = 0; u < kProbeUnroll; ++u) {
             const long long p = base + (long long)u * kProbeThreads + threadIdx.x;
-            if (p < pieces) v[u] = src[p];
+            if (p < pieces) v[u] = __builtin_nontemporal_load(src + p);
         }
 #pragma unroll
         for (int u = 0; u < kProbeUnroll; ++u) {

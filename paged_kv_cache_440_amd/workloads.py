@@ -70,6 +70,8 @@ class Workload:
     # several new tokens per sequence: k_new, v_new [B][nq][Hkv][D] and
     # q [B][nq][H][D]; seq_lens count them, they sit at L-nq .. L-1
     num_queries: int = 1
+    # several tables name the same physical blocks (a shared prompt prefix)
+    shared_blocks: bool = False
 
     @property
     def fp8(self) -> bool:
@@ -404,7 +406,8 @@ def shared_prefix_fp16(seed=SEED_BASE + 4, prefix_len=1024, num_prompts=32,
                     copy_pairs=np.asarray(pairs, dtype=np.int32).reshape(-1, 2),
                     pending_k=pending_k, pending_v=pending_v, pending_lens=pending_lens,
                     info={"prefix_len": prefix_len, "num_prompts": num_prompts,
-                          "samples": samples, "unique_blocks": needed})
+                          "samples": samples, "unique_blocks": needed},
+                    shared_blocks=True)
 
 
 def shared_prefix_cow_fp16(seed=SEED_BASE + 4, **kw) -> Workload:

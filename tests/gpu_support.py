@@ -99,18 +99,23 @@ class Device:
         self.append(self.k_new, self.v_new, self.lens)
         return w
 
-    def attention(self, partition_size=-1, out_dtype=torch.float32, workspace=None):
+    def attention(self, partition_size=-1, out_dtype=torch.float32, workspace=None,
+                  kv_reuse=None):
+        """Decode attention; kv_reuse defaults to whether the workload's
+        tables share blocks."""
         w = self.w
+        reuse = w.shared_blocks if kv_reuse is None else kv_reuse
         out = torch.empty(self.q.shape, dtype=out_dtype, device=self.q.device)
         if w.fp8:
             pkv.paged_attention_decode_fp8(out, self.q, self.k_pool, self.v_pool, self.k_scales,
                                            self.v_scales, self.tables, self.lens, w.max_seq_len,
                                            w.scale, partition_size=partition_size,
-                                           workspace=workspace)
+                                           workspace=workspace, kv_reuse=reuse)
         else:
             pkv.paged_attention_decode(out, self.q, self.k_pool, self.v_pool, self.tables,
                                        self.lens, w.max_seq_len, w.scale,
-                                       partition_size=partition_size, workspace=workspace)
+                                       partition_size=partition_size, workspace=workspace,
+                                       kv_reuse=reuse)
         return out
 
 

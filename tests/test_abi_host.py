@@ -3,7 +3,6 @@ header declares, and rejects bad arguments before enqueuing anything. None
 of these calls reaches the GPU (every call here fails validation or is a
 no-op), so they run without one."""
 
-import ctypes
 import os
 import re
 import subprocess
@@ -60,14 +59,14 @@ def test_status_strings(lib):
 def attn(lib, **kw):
     args = dict(out=FAKE, out_dtype=0, q=FAKE, k=FAKE, v=FAKE, tables=FAKE, max_blocks=8,
                 lens=FAKE, max_seq_len=100, B=2, H=4, Hkv=4, D=128, bs=16, nb=32,
-                scale=0.1, part=0, ws=0, ws_bytes=0, dtype=1)
+                scale=0.1, part=0, ws=0, ws_bytes=0, dtype=1, policy=0)
     args.update(kw)
     a = args
     return lib.pkv_paged_attention_decode(a["out"], a["out_dtype"], a["q"], a["k"], a["v"],
                                           a["tables"], a["max_blocks"], a["lens"],
                                           a["max_seq_len"], a["B"], a["H"], a["Hkv"], a["D"],
                                           a["bs"], a["nb"], a["scale"], a["part"], a["ws"],
-                                          a["ws_bytes"], a["dtype"], None)
+                                          a["ws_bytes"], a["dtype"], a["policy"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -98,7 +97,10 @@ def attn(lib, **kw):
     (dict(part=64, ws=0), WORKSPACE),       # 100 tokens in 64-token partitions need a workspace
     (dict(part=64, ws=FAKE, ws_bytes=16), WORKSPACE),
     (dict(part=64, ws=FAKE + 8, ws_bytes=1 << 20), WORKSPACE),
+    (dict(policy=2), INVALID),              # neither PKV_KV_STREAM nor PKV_KV_REUSE
+    (dict(policy=-1), INVALID),
     (dict(B=0), OK),                        # nothing to do, nothing enqueued
+    (dict(B=0, policy=1), OK),
 ])
 def test_attention_validation(lib, kw, status):
     assert attn(lib, **kw) == status
@@ -169,10 +171,6 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
 
 
 def test_probe_validation(lib):
-    lib.pkv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                   ctypes.c_void_p]
-    lib.pkv_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                   ctypes.c_void_p]
     assert lib.pkv_probe_read(0, 1 << 20, FAKE, None) == INVALID
     assert lib.pkv_probe_read(FAKE, 0, FAKE, None) == INVALID
     assert lib.pkv_probe_read(FAKE, 24, FAKE, None) == INVALID        # not a multiple of 16
@@ -193,13 +191,11 @@ def attn_fp8(lib, **kw):
              tables=FAKE, max_blocks=8, lens=FAKE, max_seq_len=100, B=2, H=4, Hkv=4, D=128,
              bs=16, nb=32, scale=0.1, part=0, ws=0, ws_bytes=0)
     a.update(kw)
-    f = lib.pkv_paged_attention_decode_fp8
-    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int] + \
-        [ctypes.c_void_p] * 5 + [ctypes.c_int, ctypes.c_void_p] + [ctypes.c_int] * 7 + \
-        [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    f = lib.pkv_paged_attention_decode_fp8           # argument types set by the binding
     return f(a["out"], a["out_dtype"], a["q"], a["q_dtype"], a["k"], a["v"], a["ks"], a["vs"],
              a["tables"], a["max_blocks"], a["lens"], a["max_seq_len"], a["B"], a["H"], a["Hkv"],
-             a["D"], a["bs"], a["nb"], a["scale"], a["part"], a["ws"], a["ws_bytes"], None)
+             a["D"], a["bs"], a["nb"], a["scale"], a["part"], a["ws"], a["ws_bytes"],
+             a.get("policy", 0), None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -212,6 +208,7 @@ def attn_fp8(lib, **kw):
     (dict(k=FAKE + 8), INVALID),
     (dict(part=64, ws=0), WORKSPACE),
     (dict(B=-1), INVALID),
+    (dict(policy=5), INVALID),
     (dict(B=0), OK),
 ])
 def test_attention_fp8_validation(lib, kw, status):
@@ -222,9 +219,7 @@ def append_fp8(lib, **kw):
     a = dict(kn=FAKE, vn=FAKE, new_dtype=1, kp=FAKE, vp=FAKE, ks=FAKE, vs=FAKE, tables=FAKE,
              max_blocks=4, lens=FAKE, B=3, Hkv=2, D=128, bs=16, nb=10)
     a.update(kw)
-    f = lib.pkv_kv_cache_append_fp8
-    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int] + [ctypes.c_void_p] * 5 + \
-        [ctypes.c_int, ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p]
+    f = lib.pkv_kv_cache_append_fp8                  # argument types set by the binding
     return f(a["kn"], a["vn"], a["new_dtype"], a["kp"], a["vp"], a["ks"], a["vs"], a["tables"],
              a["max_blocks"], a["lens"], a["B"], a["Hkv"], a["D"], a["bs"], a["nb"], None)
 
@@ -247,12 +242,12 @@ def test_copy_blocks_accepts_fp8_pools(lib):
 def attn_multi(lib, **kw):
     a = dict(out=FAKE, out_dtype=0, q=FAKE, k=FAKE, v=FAKE, tables=FAKE, max_blocks=8, lens=FAKE,
              max_seq_len=100, B=2, nq=4, H=4, Hkv=4, D=128, bs=16, nb=32, scale=0.1, part=0,
-             ws=0, ws_bytes=0, dtype=1)
+             ws=0, ws_bytes=0, dtype=1, policy=0)
     a.update(kw)
     return _lib.library().pkv_paged_attention_multi(
         a["out"], a["out_dtype"], a["q"], a["k"], a["v"], a["tables"], a["max_blocks"], a["lens"],
         a["max_seq_len"], a["B"], a["nq"], a["H"], a["Hkv"], a["D"], a["bs"], a["nb"], a["scale"],
-        a["part"], a["ws"], a["ws_bytes"], a["dtype"], None)
+        a["part"], a["ws"], a["ws_bytes"], a["dtype"], a["policy"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -262,6 +257,7 @@ def attn_multi(lib, **kw):
     (dict(D=64), UNSUPPORTED),
     (dict(nq=5, H=16, Hkv=4), UNSUPPORTED),    # 5 tokens x 4 heads > 16 columns
     (dict(part=64, ws=0), WORKSPACE),
+    (dict(policy=3), INVALID),
     (dict(B=0), OK),
 ])
 def test_attention_multi_validation(lib, kw, status):

@@ -72,7 +72,8 @@ def test_parallel_sampling_through_the_block_manager(prompt_len, samples, steps)
         q = torch.from_numpy(rng.standard_normal((samples, h, d), dtype=np.float32)).half()
         out = torch.empty((samples, h, d), dtype=torch.float32, device=dev)
         pkv.paged_attention_decode(out, q.to(dev), k_pool, v_pool, tables_d, lens_d,
-                                   int(lens.max()), 1.0 / np.sqrt(d), partition_size=64)
+                                   int(lens.max()), 1.0 / np.sqrt(d), partition_size=64,
+                                   kv_reuse=True)
         out = out.cpu().double().numpy()
         kp, vp = k_pool.cpu(), v_pool.cpu()
         for i, s in enumerate(sample_ids):

@@ -150,3 +150,14 @@ def test_full_size_matches_oracle(name):
     del d
     err = max_err(out, expected_attention(w, kb, vb))
     assert err <= tol(w), f"max abs error {err:.3e}"
+
+
+@pytest.mark.parametrize("group", [1, 8])
+def test_kv_policies_give_identical_bits(group):
+    w = fp8_workload(RAGGED, torch.bfloat16, group)
+    d = Device(w)
+    d.copy_and_append()
+    for partition in (512, BAL):
+        a = d.attention(partition_size=partition, kv_reuse=False).cpu()
+        b = d.attention(partition_size=partition, kv_reuse=True).cpu()
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))

@@ -47,7 +47,7 @@ def setup(nq, group, dtype, block_size=16, hkv=2, seed=41):
     return w, k_new, v_new, q
 
 
-def run(w, k_new, v_new, q, partition):
+def run(w, k_new, v_new, q, partition, kv_reuse=False):
     dev = "cuda"
     kp, vp = w.k_pool.to(dev), w.v_pool.to(dev)
     tables = torch.from_numpy(w.block_tables).to(dev)
@@ -55,7 +55,7 @@ def run(w, k_new, v_new, q, partition):
     pkv.kv_cache_append_multi(k_new.to(dev), v_new.to(dev), kp, vp, tables, lens)
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     pkv.paged_attention_multi(out, q.to(dev), kp, vp, tables, lens, w.max_seq_len, w.scale,
-                              partition_size=partition)
+                              partition_size=partition, kv_reuse=kv_reuse)
     return kp, vp, out
 
 
@@ -111,3 +111,11 @@ def test_full_size_speculative_verification_matches_oracle():
                                       w.seq_lens, w.block_size, w.scale)
     err = float(np.abs(out.cpu().double().numpy() - ref).max())
     assert err <= 2e-3, f"max abs error {err:.3e}"
+
+
+@pytest.mark.parametrize("partition", [64, BAL])
+def test_kv_policies_give_identical_bits(partition):
+    w, k_new, v_new, q = setup(4, 2, torch.float16)
+    _, _, a = run(w, k_new, v_new, q, partition, kv_reuse=False)
+    _, _, b = run(w, k_new, v_new, q, partition, kv_reuse=True)
+    assert torch.equal(a.cpu().view(torch.int32), b.cpu().view(torch.int32))

@@ -341,3 +341,25 @@ def test_grouped_query_walkers(dtype, head_dim, group, block_size, partition):
     assert torch.isfinite(out).all()
     ref = expected_attention(w, *expected_pools(w))
     assert max_err(out, ref) <= TOL[w.dtype], f"max abs error {max_err(out, ref):.3e}"
+
+
+@pytest.mark.parametrize("partition", [0, 512, BAL])
+@pytest.mark.parametrize("dtype,head_dim,group", [
+    (torch.float32, 64, 1),            # vector walker
+    (torch.float16, 128, 1),           # vector walker, the OPT-13B shape
+    (torch.bfloat16, 128, 8),          # matrix-core walker
+])
+def test_kv_policies_give_identical_bits(dtype, head_dim, group, partition):
+    """Streaming and cached K/V loads differ in cache behaviour only: the
+    outputs are the same bits, and match the oracle."""
+    lens = [1, 17, 64, 100, 129, 700, 1000]
+    w = wl.build_independent("policy", lens, dtype=dtype, num_heads=2 * group, num_kv_heads=2,
+                             head_dim=head_dim, block_size=16, dist="normal", seed=77)
+    poison_unwritten_slots(w)
+    d = Device(w)
+    d.copy_and_append()
+    streamed = d.attention(partition_size=partition, kv_reuse=False).cpu()
+    cached = d.attention(partition_size=partition, kv_reuse=True).cpu()
+    assert torch.equal(bits_t(streamed), bits_t(cached))
+    ref = expected_attention(w, *expected_pools(w))
+    assert max_err(streamed, ref) <= TOL[w.dtype]

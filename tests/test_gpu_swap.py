@@ -7,7 +7,6 @@ in, and attention over the restored blocks matches the oracle's dense
 attention over each sequence's logical history.
 """
 
-import ctypes
 import sys
 
 import numpy as np
@@ -166,7 +165,7 @@ def test_preempted_sequences_return_intact(dtype):
         out = torch.empty((len(seqs), h, d), dtype=torch.float32, device=dev)
         pkv.paged_attention_decode(out, q.to(dev), k_pool, v_pool, torch.from_numpy(tables).to(dev),
                                    torch.from_numpy(lens).to(dev), int(lens.max()),
-                                   1.0 / np.sqrt(d), partition_size=64)
+                                   1.0 / np.sqrt(d), partition_size=64, kv_reuse=True)
         out = out.cpu().double().numpy()
         kp, vp = k_pool.cpu(), v_pool.cpu()
         for i, s in enumerate(seqs):
