@@ -169,10 +169,11 @@ PKV_API size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, i
  *   a positive multiple of 64
  *                           each sequence is cut into partitions of that many
  *                           tokens, handled independently and merged by a
- *                           log-sum-exp reduce. Sequences next to each other
- *                           in the batch are processed side by side, so
- *                           blocks they share (parallel sampling) are read
- *                           once from HBM and then from cache;
+ *                           log-sum-exp reduce. Under PKV_KV_REUSE, the
+ *                           sequences next to each other in the batch are
+ *                           processed side by side, so blocks they share
+ *                           (parallel sampling) are read once from HBM and
+ *                           then from cache;
  *   PKV_PARTITION_BALANCED  a fixed set of persistent waves (8 per compute
  *                           unit, at most 4096) each takes an equal share of
  *                           all tokens of the batch, whatever the lengths;

@@ -15,10 +15,11 @@
 // schedules decide the ranges:
 //   single pass      one wave per segment (partition_size 0);
 //   fixed partitions one wave per (segment, partition of part_len tokens),
-//                    numbered g fastest, then i, then the partition; the
-//                    hardware dispatcher hands them out, and waves of
-//                    neighbouring sequences run side by side (blocks those
-//                    sequences share are read from cache);
+//                    handed out by the hardware dispatcher; numbered g
+//                    fastest, then i, then the partition for streamed K/V,
+//                    and i fastest, then g, then the partition for the
+//                    cached-load policy, so that neighbouring sequences run
+//                    side by side and blocks they share come from cache;
 //   balanced         a fixed number W of persistent waves; the segments, cut
 //                    into 32-token units and laid end to end in (i, g) order,
 //                    are split into W equal runs, one per wave, so every wave
@@ -51,10 +52,21 @@ void paged_decode_kernel(const AttnParams a) {
     // the wave index is uniform; say so, so that item-derived values live in SGPRs
     const int item = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (item >= a.num_items) return;
-    const int g = item % a.num_kv_heads;
-    const int rest = item / a.num_kv_heads;
-    const int seq = rest % a.num_seqs;
-    const int part = rest / a.num_seqs;
+    int g, seq, part;
+    if constexpr (Walker::kStream) {
+        // the kv heads of one sequence side by side: their tiles are neighbours
+        g = item % a.num_kv_heads;
+        const int rest = item / a.num_kv_heads;
+        seq = rest % a.num_seqs;
+        part = rest / a.num_seqs;
+    } else {
+        // neighbouring sequences side by side, in the same workgroup: blocks
+        // they share are read from HBM once and then found in cache
+        seq = item % a.num_seqs;
+        const int rest = item / a.num_seqs;
+        g = rest % a.num_kv_heads;
+        part = rest / a.num_kv_heads;
+    }
 
     const int L = clamp_len(a, a.seq_lens[seq]);
     if (L == 0) {                                   // padding row: zero output

@@ -47,6 +47,7 @@ template <> __device__ __forceinline__ float q_elem<BF16>(const char* row, int i
 // that of the 16-bit vector walker (token classes merged at the end).
 template <typename Q, int G_, bool STREAM>
 struct Fp8VecWalker {
+    static constexpr bool kStream = STREAM;     // K/V load policy
     static constexpr int D = 128, G = G_;
     static constexpr int ROW = 128, LPT = 8, TPL = 8, NLOAD = 4, CHUNK = TPL * NLOAD, EPL = 16;
     static constexpr int kMinWavesPerSimd = 2;
@@ -256,6 +257,7 @@ struct Fp8VecWalker {
 //     tokens (an 8-byte load); tile c takes code c of the eight tokens.
 template <typename Q, int G_, bool STREAM>
 struct Fp8MfmaWalker {
+    static constexpr bool kStream = STREAM;     // K/V load policy
     static constexpr int D = 128, G = G_;
     static constexpr int ROW = 128;
     static constexpr int CHUNK = 32;

@@ -70,6 +70,7 @@ __device__ __forceinline__ float from16(F16, uint32_t h) {
 
 template <typename S, int G_, bool STREAM>
 struct MfmaWalker {
+    static constexpr bool kStream = STREAM;     // K/V load policy
     static constexpr int D = 128, G = G_;
     static constexpr int ROW = 256;             // bytes of one token row of one kv head
     static constexpr int CHUNK = 32;            // tokens per chunk

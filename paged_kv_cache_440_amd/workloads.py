@@ -99,6 +99,24 @@ class Workload:
         per_token = 2 * self.num_kv_heads * self.head_dim * self.elem_bytes
         return int(self.seq_lens.astype(np.int64).sum()) * per_token
 
+    def unique_kv_bytes(self) -> int:
+        """The same over distinct (physical block, slot) pairs: what HBM must
+        deliver at least once when tables share blocks (equal to kv_bytes
+        when they do not)."""
+        if not self.shared_blocks:
+            return self.kv_bytes()
+        bs = self.block_size
+        slots = set()
+        for i, n in enumerate(self.seq_lens):
+            n = int(n)
+            nb = -(-n // bs)
+            for b in range(nb):
+                phys = int(self.block_tables[i, b])
+                used = min(bs, n - b * bs)
+                slots.update((phys, s) for s in range(used))
+        per_token = 2 * self.num_kv_heads * self.head_dim * self.elem_bytes
+        return len(slots) * per_token
+
 
 # ----------------------------------------------------------------------------
 # value draws
