@@ -90,3 +90,14 @@ def test_bf16_rounding_is_nearest_even_from_float32():
     assert w.dtype == torch.bfloat16 and w.num_heads == 64 and w.num_kv_heads == 8
     x = w.q.float()
     assert torch.equal(x.to(torch.bfloat16).float(), x)
+
+
+def test_unique_bytes_count_shared_prefix_rows_once():
+    w = wl.shared_prefix_fp16(num_prompts=3, samples=4, max_divergent=40, num_heads=4)
+    per_token = 2 * w.num_kv_heads * w.head_dim * 2
+    prefix = w.info["prefix_len"]
+    own = int((w.seq_lens.astype(np.int64) - prefix).sum())
+    assert w.unique_kv_bytes() == (3 * prefix + own) * per_token
+    assert w.kv_bytes() == int(w.seq_lens.sum()) * per_token
+    plain = wl.opt13b_fp16(num_seqs=4, len_range=(32, 200))
+    assert plain.unique_kv_bytes() == plain.kv_bytes()
