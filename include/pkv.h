@@ -174,8 +174,9 @@ PKV_API size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, i
  *                           processed side by side, so blocks they share
  *                           (parallel sampling) are read once from HBM and
  *                           then from cache;
- *   PKV_PARTITION_BALANCED  a fixed set of persistent waves (8 per compute
- *                           unit, at most 4096) each takes an equal share of
+ *   PKV_PARTITION_BALANCED  a fixed set of persistent waves (4 or 8 per
+ *                           compute unit, depending on the kernel; at most
+ *                           4096) each takes an equal share of
  *                           all tokens of the batch, whatever the lengths;
  *                           pieces of a sequence split between waves are
  *                           merged by a log-sum-exp reduce. The split points

@@ -327,7 +327,8 @@ hipError_t launch_walker(const AttnParams& a_in, hipStream_t stream) {
         // start at once and finish together
         const int resident = balanced_resident_waves_per_cu<Walker>();
         if (resident <= 0) return hipErrorInvalidValue;
-        const int per_cu = resident < kBalancedWavesPerCU ? resident : kBalancedWavesPerCU;
+        const int want = Walker::kBalancedWavesPerCU;
+        const int per_cu = resident < want ? resident : want;
         const long long w = (long long)a.num_items * per_cu;
         a.num_items = (int)(w < kMaxBalancedWaves ? w : kMaxBalancedWaves);
     }

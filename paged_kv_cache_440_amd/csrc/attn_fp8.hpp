@@ -48,6 +48,7 @@ template <> __device__ __forceinline__ float q_elem<BF16>(const char* row, int i
 template <typename Q, int G_, bool STREAM>
 struct Fp8VecWalker {
     static constexpr bool kStream = STREAM;     // K/V load policy
+    static constexpr int kBalancedWavesPerCU = 8;
     static constexpr int D = 128, G = G_;
     static constexpr int ROW = 128, LPT = 8, TPL = 8, NLOAD = 4, CHUNK = TPL * NLOAD, EPL = 16;
     static constexpr int kMinWavesPerSimd = 2;
@@ -258,6 +259,7 @@ struct Fp8VecWalker {
 template <typename Q, int G_, bool STREAM>
 struct Fp8MfmaWalker {
     static constexpr bool kStream = STREAM;     // K/V load policy
+    static constexpr int kBalancedWavesPerCU = 8;
     static constexpr int D = 128, G = G_;
     static constexpr int ROW = 128;
     static constexpr int CHUNK = 32;

@@ -71,6 +71,11 @@ __device__ __forceinline__ float from16(F16, uint32_t h) {
 template <typename S, int G_, bool STREAM>
 struct MfmaWalker {
     static constexpr bool kStream = STREAM;     // K/V load policy
+    // persistent waves per compute unit in the balanced schedule: one per
+    // SIMD for grouped heads (measured on MI355X: 4 waves beat 8 by 3-5% at 4
+    // and 8 query heads per kv head), two per SIMD for multi-query columns of
+    // one head (8 beat 4 by 9%)
+    static constexpr int kBalancedWavesPerCU = G_ >= 4 ? 4 : 8;
     static constexpr int D = 128, G = G_;
     static constexpr int ROW = 256;             // bytes of one token row of one kv head
     static constexpr int CHUNK = 32;            // tokens per chunk

@@ -48,6 +48,7 @@ struct Geo {
 template <typename S, int D_, int G_, bool STREAM>
 struct VecWalker {
     static constexpr bool kStream = STREAM;     // K/V load policy
+    static constexpr int kBalancedWavesPerCU = 8;
     static constexpr int D = D_, G = G_;
     using Gm = Geo<S, D_>;
     static constexpr int LPT = Gm::LPT, TPL = Gm::TPL, NLOAD = Gm::NLOAD;

@@ -50,13 +50,9 @@ struct AttnParams {
     int q_dtype;
 };
 
-// Persistent waves of the balanced schedule: kBalancedWavesPerCU per compute
-// unit (fewer if fewer fit), at most kMaxBalancedWaves (which sizes the
-// workspace).
-#ifndef PKV_BAL_WAVES_PER_CU
-#define PKV_BAL_WAVES_PER_CU 8
-#endif
-constexpr int kBalancedWavesPerCU = PKV_BAL_WAVES_PER_CU;
+// Persistent waves of the balanced schedule: each walker's
+// kBalancedWavesPerCU per compute unit (fewer if fewer fit), at most
+// kMaxBalancedWaves (which sizes the workspace).
 constexpr int kMaxBalancedWaves = 4096;
 
 struct AppendParams {
