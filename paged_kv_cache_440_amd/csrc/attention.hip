@@ -317,39 +317,48 @@ int balanced_resident_waves_per_cu() {
     return v;
 }
 
+// The balanced schedule: persistent waves, then the merge of split segments.
 template <class Walker>
-hipError_t launch_walker(const AttnParams& a_in, hipStream_t stream) {
+hipError_t launch_balanced(const AttnParams& a_in, hipStream_t stream) {
     constexpr int D = Walker::D, G = Walker::G;
     AttnParams a = a_in;
-    if (a.balanced) {
-        // a.num_items holds the compute-unit count; launch at most as many
-        // persistent waves as are resident together, so that all of them
-        // start at once and finish together
-        const int resident = balanced_resident_waves_per_cu<Walker>();
-        if (resident <= 0) return hipErrorInvalidValue;
-        const int want = Walker::kBalancedWavesPerCU;
-        const int per_cu = resident < want ? resident : want;
-        const long long w = (long long)a.num_items * per_cu;
-        a.num_items = (int)(w < kMaxBalancedWaves ? w : kMaxBalancedWaves);
-    }
+    // a.num_items holds the compute-unit count; launch at most as many
+    // persistent waves as are resident together, so that all of them start
+    // at once and finish together
+    const int resident = balanced_resident_waves_per_cu<Walker>();
+    if (resident <= 0) return hipErrorInvalidValue;
+    const int want = Walker::kBalancedWavesPerCU;
+    const int per_cu = resident < want ? resident : want;
+    const long long w = (long long)a.num_items * per_cu;
+    a.num_items = (int)(w < kMaxBalancedWaves ? w : kMaxBalancedWaves);
     const int cols = a.num_queries * G;
-    const int blocks = (a.num_items + kWaves - 1) / kWaves;
-    const int rblocks = (a.num_seqs * a.num_kv_heads * cols + kWaves - 1) / kWaves;
-    if (a.balanced) {
-        hipLaunchKernelGGL((paged_decode_balanced_kernel<Walker>), dim3(blocks), dim3(64 * kWaves),
-                           0, stream, a);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-        hipLaunchKernelGGL((balanced_reduce_kernel<D>),
-                           dim3((a.num_items * cols + kWaves - 1) / kWaves), dim3(64 * kWaves), 0,
-                           stream, a);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((paged_decode_kernel<Walker>), dim3(blocks), dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((paged_decode_balanced_kernel<Walker>),
+                       dim3((a.num_items + kWaves - 1) / kWaves), dim3(64 * kWaves), 0, stream, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((balanced_reduce_kernel<D>), dim3((a.num_items * cols + kWaves - 1) / kWaves),
+                       dim3(64 * kWaves), 0, stream, a);
+    return hipGetLastError();
+}
+
+// Single pass or fixed partitions, then the reduce of split sequences.
+template <class Walker>
+hipError_t launch_partitioned(const AttnParams& a, hipStream_t stream) {
+    constexpr int D = Walker::D, G = Walker::G;
+    const int cols = a.num_queries * G;
+    hipLaunchKernelGGL((paged_decode_kernel<Walker>), dim3((a.num_items + kWaves - 1) / kWaves),
+                       dim3(64 * kWaves), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.max_parts <= 1) return err;
-    hipLaunchKernelGGL((lse_reduce_kernel<D>), dim3(rblocks), dim3(64 * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((lse_reduce_kernel<D>),
+                       dim3((a.num_seqs * a.num_kv_heads * cols + kWaves - 1) / kWaves),
+                       dim3(64 * kWaves), 0, stream, a);
     return hipGetLastError();
+}
+
+template <class Walker>
+hipError_t launch_walker(const AttnParams& a, hipStream_t stream) {
+    return a.balanced ? launch_balanced<Walker>(a, stream) : launch_partitioned<Walker>(a, stream);
 }
 
 // Matrix cores for 16-bit K/V with head_dim 128 and 4 or 8 query heads per
@@ -392,8 +401,12 @@ hipError_t launch_policy(const AttnParams& a, hipStream_t stream) {
 // there). head_dim is 128.
 template <typename Q, int G, bool STREAM>
 hipError_t launch_fp8_typed(const AttnParams& a, hipStream_t stream) {
+    // the vector walker keeps two loads of K and V per chunk in flight under
+    // the balanced schedule (four spill registers next to its bookkeeping),
+    // four under fixed partitions
     if constexpr (G == 1)
-        return launch_walker<Fp8VecWalker<Q, G, STREAM>>(a, stream);
+        return a.balanced ? launch_balanced<Fp8VecWalker<Q, G, STREAM, 2>>(a, stream)
+                          : launch_partitioned<Fp8VecWalker<Q, G, STREAM, 4>>(a, stream);
     else if constexpr (Q::bytes == 2)
         return launch_walker<Fp8MfmaWalker<Q, G, STREAM>>(a, stream);
     else

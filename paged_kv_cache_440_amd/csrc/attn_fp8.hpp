@@ -45,12 +45,13 @@ template <> __device__ __forceinline__ float q_elem<BF16>(const char* row, int i
 // to float32 and pre-multiplied by scale * log2(e) * k_scale, so a score is
 // one 16-term FMA chain plus a 3-step DPP row sum. Softmax bookkeeping is
 // that of the 16-bit vector walker (token classes merged at the end).
-template <typename Q, int G_, bool STREAM>
+template <typename Q, int G_, bool STREAM, int NLOAD_>
 struct Fp8VecWalker {
     static constexpr bool kStream = STREAM;     // K/V load policy
     static constexpr int kBalancedWavesPerCU = 8;
     static constexpr int D = 128, G = G_;
-    static constexpr int ROW = 128, LPT = 8, TPL = 8, NLOAD = 4, CHUNK = TPL * NLOAD, EPL = 16;
+    // NLOAD_ wave loads of K (and of V) per chunk
+    static constexpr int ROW = 128, LPT = 8, TPL = 8, NLOAD = NLOAD_, CHUNK = TPL * NLOAD, EPL = 16;
     static constexpr int kMinWavesPerSimd = 2;
 
     float qf[G][EPL];
