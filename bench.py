@@ -324,6 +324,9 @@ def main():
     ap.add_argument("--kv-policy", choices=("auto", "stream", "reuse"), default="auto",
                     help="K/V load policy: streaming (non-temporal) or cached loads; auto = "
                          "cached exactly when the workload's tables share blocks")
+    ap.add_argument("--no-grouped", action="store_true",
+                    help="time parallel-sampling workloads with the plain decode call instead "
+                         "of the grouped one (shared prompt blocks read once per group)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-manager", action="store_true",
                     help="only time the host block manager's decode-step bookkeeping "
@@ -404,6 +407,17 @@ def main():
 
         def append():
             pkv.kv_cache_append_fp8(k_new, v_new, kp, vp, ks, vs, tables, lens, stream=stream)
+    elif "samples" in w.info and not args.no_grouped and args.partition > 0:
+        samples = w.info["samples"]
+        shared = torch.from_numpy(wl.shared_tokens(w, samples)).to(dev)
+
+        def attention():
+            pkv.paged_attention_decode_grouped(out, q, kp, vp, tables, lens, max_len, w.scale,
+                                               samples, shared, partition_size=args.partition,
+                                               workspace=ws, stream=stream, kv_reuse=reuse)
+
+        def append():
+            pkv.kv_cache_append(k_new, v_new, kp, vp, tables, lens, stream=stream)
     else:
         def attention():
             pkv.paged_attention_decode(out, q, kp, vp, tables, lens, max_len, w.scale,
@@ -412,6 +426,12 @@ def main():
 
         def append():
             pkv.kv_cache_append(k_new, v_new, kp, vp, tables, lens, stream=stream)
+
+    entry = ("paged_attention_multi" if w.num_queries > 1 else
+             "paged_attention_decode_fp8" if w.fp8 else
+             "paged_attention_decode_grouped" if ("samples" in w.info and not args.no_grouped
+                                                  and args.partition > 0) else
+             "paged_attention_decode")
 
     def step(ev=None):
         pkv.copy_blocks(kp, vp, pairs, stream=stream)
@@ -504,6 +524,7 @@ def main():
             "max_seq_len": w.max_seq_len,
             "partition_size": args.partition,
             "kv_policy": "reuse" if reuse else "stream",
+            "entry": entry,
             "kv_bytes_per_step": kv_bytes,
             "unique_kv_bytes_per_step": unique_bytes,
         },

@@ -202,6 +202,39 @@ PKV_API int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype,
                                pkv_dtype dtype, int kv_policy, void* stream);
 
 /*
+ * Decode attention for parallel sampling ([summary] section "블록 공유": the
+ * samples of one prompt share the prompt's blocks, by reference). The batch
+ * is cut into groups of group_size consecutive sequences (num_seqs must be a
+ * multiple of group_size); shared_tokens (device int32 [num_seqs /
+ * group_size]) gives, per group, how many leading tokens every sequence of
+ * the group reads from the same physical blocks (the caller's contract: a
+ * block manager knows it; pkv_bm_shared_prefix computes it). The result is
+ * that of pkv_paged_attention_decode with the same arguments, up to
+ * floating-point summation order.
+ *
+ * partition_size must be a positive multiple of 64 (fixed partitions). A
+ * partition lying inside the tokens its group shares (for a sequence of
+ * length L: ending at or before min(shared_tokens, L - 1)) is computed once
+ * for the whole group on the matrix cores, the group's queries forming the
+ * columns, so its blocks are read from HBM once instead of once per sample;
+ * every other partition is computed per sequence. F16 / BF16 K/V and q,
+ * head_dim 128, group_size * (num_heads / num_kv_heads) <= 16
+ * (PKV_ERR_UNSUPPORTED otherwise). The workspace is sized as for
+ * pkv_paged_attention_decode with the same partition_size. shared_tokens = 0
+ * everywhere gives exactly the bits of pkv_paged_attention_decode.
+ */
+PKV_API int pkv_paged_attention_decode_grouped(void* out, pkv_dtype out_dtype, const void* q,
+                               const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* seq_lens, int max_seq_len,
+                               int num_seqs, int num_heads, int num_kv_heads,
+                               int head_dim, int block_size, int num_blocks,
+                               float scale, int partition_size,
+                               int group_size, const int32_t* shared_tokens,
+                               void* workspace, size_t workspace_bytes,
+                               pkv_dtype dtype, int kv_policy, void* stream);
+
+/*
  * Several new tokens per sequence (blog.aqudi.me "벤치마크가 다가 아니야!
  * vLLM으로 보는 LLM 추론 최적화", section 4: chunked prefill feeds a long
  * prompt in pieces between decode steps; speculative decoding checks several

@@ -144,6 +144,16 @@ PKV_API int pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq_id, int3
  * and removes them from the queue; returns how many were written. */
 PKV_API int pkv_bm_take_copies(pkv_block_manager* bm, int32_t* pairs, int max_pairs);
 
+/* For pkv_paged_attention_decode_grouped: seq_ids[0..n) form groups of
+ * group_size consecutive ids (n a multiple of group_size); shared_tokens[k]
+ * receives block_size times the number of leading logical blocks that every
+ * sequence of group k maps to the same physical block. Such a block has not
+ * been written since it became shared (a write into a shared block copies
+ * it first), so every sequence reads the same tokens from it.
+ * PKV_ERR_INVALID for an unknown or swapped-out id. */
+PKV_API int pkv_bm_shared_prefix(const pkv_block_manager* bm, const int64_t* seq_ids, int n,
+                                 int group_size, int32_t* shared_tokens);
+
 /* The launch inputs for a batch: row i of tables ([n][max_blocks], padded
  * with -1) and seq_lens[i] for seq_ids[i]. PKV_ERR_WORKSPACE if a sequence
  * has more than max_blocks blocks, PKV_ERR_INVALID if one is swapped out. */

@@ -134,6 +134,22 @@ class BlockManagerOracle:
                 self.swapped.discard(s)
         return [(b, where[b]) for b in order]
 
+    def shared_prefix(self, seqs, group_size):
+        """Per group of group_size consecutive ids: block_size times the number
+        of leading logical blocks every sequence of the group maps to the same
+        physical block."""
+        seqs = list(seqs)
+        assert len(seqs) % group_size == 0
+        assert all(s in self.tables and s not in self.swapped for s in seqs)
+        out = []
+        for k in range(0, len(seqs), group_size):
+            tables = [self.tables[s] for s in seqs[k:k + group_size]]
+            b = 0
+            while all(b < len(t) for t in tables) and len({t[b] for t in tables}) == 1:
+                b += 1
+            out.append(b * self.block_size)
+        return out
+
     def swap_out(self, seqs):
         """Move resident sequences to host blocks; returns the (device block,
         host block) pairs whose contents must be copied device -> host."""

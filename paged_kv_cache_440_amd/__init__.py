@@ -12,6 +12,7 @@ _API = (
     "kv_cache_append_multi",
     "paged_attention_multi",
     "paged_attention_decode_fp8",
+    "paged_attention_decode_grouped",
     "FP8_E4M3",
     "copy_blocks",
     "swap_blocks",

@@ -60,6 +60,9 @@ def library() -> ctypes.CDLL:
     lib.pkv_paged_attention_multi.argtypes = [P, I, P, P, P, P, I, P, I, I, I, I, I, I, I, I, F,
                                               I, P, Z, I, I, P]
     lib.pkv_paged_attention_multi.restype = I
+    lib.pkv_paged_attention_decode_grouped.argtypes = [P, I, P, P, P, P, I, P, I, I, I, I, I,
+                                                       I, I, F, I, I, P, P, Z, I, I, P]
+    lib.pkv_paged_attention_decode_grouped.restype = I
     lib.pkv_swap_blocks.argtypes = [P, P, I, P, P, I, P, I, I, I, I, I, P]
     lib.pkv_swap_blocks.restype = I
     lib.pkv_status_string.argtypes = [I]
@@ -283,6 +286,43 @@ def probe_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
         raise ValueError("dst and src must have the same byte size")
     _check("pkv_probe_copy", library().pkv_probe_copy(
         _dev(dst, "dst"), _dev(src, "src"), nbytes, _stream(stream)))
+
+
+def paged_attention_decode_grouped(out, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len,
+                                   scale, group_size, shared_tokens, partition_size=512,
+                                   workspace=None, stream=None,
+                                   kv_reuse: bool = False) -> torch.Tensor:
+    """pkv_paged_attention_decode_grouped into `out` [B][H][D]: sequences
+    k*group_size .. (k+1)*group_size - 1 share the blocks of their first
+    shared_tokens[k] tokens (int32 device tensor [B / group_size]); shared
+    partitions are read once per group."""
+    nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
+    if code == FP8_E4M3:
+        raise TypeError("FP8 pools are not supported by paged_attention_decode_grouped")
+    if q.dim() != 3 or q.shape[2] != d or q.dtype != k_pool.dtype:
+        raise ValueError("q must be [num_seqs][num_heads][head_dim] in the pool's dtype")
+    b, h = q.shape[0], q.shape[1]
+    if out.shape != q.shape or out.dtype not in DTYPE_CODES:
+        raise ValueError("out must be [num_seqs][num_heads][head_dim], float32/16 or bfloat16")
+    if group_size <= 0 or b % group_size != 0:
+        raise ValueError("num_seqs must be a multiple of group_size")
+    if shared_tokens.shape != (b // group_size,):
+        raise ValueError("shared_tokens must be [num_seqs // group_size]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or seq_lens.shape != (b,):
+        raise ValueError("block_tables must be [num_seqs][max_blocks], seq_lens [num_seqs]")
+    need = paged_attention_workspace_size(b, h, hkv, d, max_seq_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("pkv_paged_attention_decode_grouped", library().pkv_paged_attention_decode_grouped(
+        _dev(out, "out"), DTYPE_CODES[out.dtype], _dev(q, "q"), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len),
+        b, h, hkv, d, bs, nb, float(scale), int(partition_size), int(group_size),
+        _dev(shared_tokens, "shared_tokens", torch.int32), ws_ptr, ws_bytes, code,
+        _policy(kv_reuse), _stream(stream)))
+    return out
 
 
 def paged_attention_decode_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens,

@@ -37,6 +37,7 @@ def _bind():
     lib.pkv_bm_block_table.argtypes = [P, L, P, I]
     lib.pkv_bm_take_copies.argtypes = [P, P, I]
     lib.pkv_bm_build_batch.argtypes = [P, P, I, P, I, P]
+    lib.pkv_bm_shared_prefix.argtypes = [P, P, I, I, P]
     lib.pkv_bm_swap_out.argtypes = [P, P, I, P, I]
     lib.pkv_bm_swap_in.argtypes = [P, P, I, P, I]
     lib.pkv_bm_is_swapped.argtypes = [P, L]
@@ -46,7 +47,7 @@ def _bind():
                  "pkv_bm_free_sequence", "pkv_bm_num_free_blocks", "pkv_bm_seq_len",
                  "pkv_bm_refcount", "pkv_bm_block_table", "pkv_bm_take_copies",
                  "pkv_bm_build_batch", "pkv_bm_swap_out", "pkv_bm_swap_in", "pkv_bm_is_swapped",
-                 "pkv_bm_num_free_host_blocks", "pkv_bm_host_refcount"):
+                 "pkv_bm_num_free_host_blocks", "pkv_bm_host_refcount", "pkv_bm_shared_prefix"):
         getattr(lib, name).restype = I
     _BOUND = True
     return lib
@@ -159,6 +160,15 @@ class BlockManager:
             if n < buf.shape[0]:
                 break
         return np.concatenate(out).reshape(-1, 2)
+
+    def shared_prefix(self, seq_ids, group_size: int) -> np.ndarray:
+        """int32 [n // group_size]: per group of group_size consecutive ids, the
+        tokens of the leading blocks all its sequences share."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        out = np.empty(max(len(ids) // max(group_size, 1), 1), dtype=np.int32)
+        _check("pkv_bm_shared_prefix", self._lib.pkv_bm_shared_prefix(
+            self._h, ids.ctypes.data, len(ids), int(group_size), out.ctypes.data))
+        return out[:len(ids) // group_size]
 
     def build_batch(self, seq_ids, max_blocks: int) -> tuple[np.ndarray, np.ndarray]:
         """int32 block tables [n][max_blocks] (padded with -1) and seq_lens [n]."""

@@ -407,6 +407,37 @@ int pkv_paged_attention_multi(void* out, pkv_dtype out_dtype, const void* q,
                                                                                    : PKV_ERR_HIP;
 }
 
+int pkv_paged_attention_decode_grouped(void* out, pkv_dtype out_dtype, const void* q,
+                                       const void* k_pool, const void* v_pool,
+                                       const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* seq_lens, int max_seq_len, int num_seqs,
+                                       int num_heads, int num_kv_heads, int head_dim,
+                                       int block_size, int num_blocks, float scale,
+                                       int partition_size, int group_size,
+                                       const int32_t* shared_tokens, void* workspace,
+                                       size_t workspace_bytes, pkv_dtype dtype, int kv_policy,
+                                       void* stream) {
+    if (!valid_pool_dtype(dtype) || group_size <= 0 || partition_size <= 0) return PKV_ERR_INVALID;
+    pkv::AttnParams a{};
+    const int st = prepare_attention(a, out, out_dtype, q, k_pool, v_pool, block_tables,
+                                     max_blocks_per_seq, seq_lens, max_seq_len, num_seqs, num_heads,
+                                     num_kv_heads, head_dim, block_size, num_blocks, scale,
+                                     partition_size, workspace, workspace_bytes, kv_policy);
+    if (st != PKV_OK) return st;
+    if ((dtype != PKV_F16 && dtype != PKV_BF16) || head_dim != 128 ||
+        (long long)group_size * a.group > 16)
+        return PKV_ERR_UNSUPPORTED;
+    if (num_seqs % group_size != 0) return PKV_ERR_INVALID;
+    if (num_seqs == 0) return PKV_OK;
+    if (!shared_tokens) return PKV_ERR_INVALID;
+    a.dtype = dtype;
+    a.q_dtype = dtype;
+    a.group_size = group_size;
+    a.shared_tokens = shared_tokens;
+    return pkv::launch_paged_attention_grouped(a, (hipStream_t)stream) == hipSuccess ? PKV_OK
+                                                                                     : PKV_ERR_HIP;
+}
+
 int pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype, const void* q,
                                    pkv_dtype q_dtype, const void* k_pool, const void* v_pool,
                                    const float* k_scales, const float* v_scales,

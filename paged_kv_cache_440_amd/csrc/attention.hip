@@ -30,6 +30,7 @@
 // changes no output bit.
 
 #include <atomic>
+#include <type_traits>
 
 #include "attn_common.hpp"
 #include "attn_fp8.hpp"
@@ -39,6 +40,17 @@
 namespace pkv {
 
 namespace {
+
+// Sampling groups: partition `part` of sequence seq (length L) lies inside
+// the tokens its group shares, so the group kernel computes it for all the
+// group's sequences at once. The same predicate decides on both sides, so
+// every (sequence, partition) is computed exactly once. The last token of a
+// sequence is never in a shared partition.
+__device__ __forceinline__ bool in_shared_part(const AttnParams& a, int seq, int part, int L) {
+    const int P = a.shared_tokens[seq / a.group_size];
+    const int lim = P < L - 1 ? P : L - 1;
+    return (part + 1) * a.part_tokens <= lim;
+}
 
 // ---------------------------------------------------------------------------
 // Single pass and fixed partitions: one wave per (segment, partition).
@@ -76,6 +88,7 @@ void paged_decode_kernel(const AttnParams a) {
     const int part_len = a.part_tokens > 0 ? a.part_tokens : L;
     const int nparts = (L + part_len - 1) / part_len;
     if (part >= nparts) return;
+    if (a.shared_tokens != nullptr && a.part_tokens > 0 && in_shared_part(a, seq, part, L)) return;
     const int t_begin = part * part_len;
     const int t_stop = (t_begin + part_len < L) ? t_begin + part_len : L;
 
@@ -90,6 +103,46 @@ void paged_decode_kernel(const AttnParams a) {
         const size_t row0 = ((size_t)seq * a.num_kv_heads * cols + (size_t)g * cols) * a.max_parts + part;
         st.write_partial(a, row0, (size_t)a.max_parts);
     }
+}
+
+// Sampling groups: one wave per (group k, kv head g, partition). Column n of
+// the matrix-core walker is sample n / G of the group with query head
+// g*G + n % G; the partition's K/V are read once for all of them. A column
+// whose sequence does not share the partition is left to the sequence
+// kernel. Partial rows as in paged_decode_kernel.
+template <class Walker>
+__global__ __launch_bounds__(64 * kWaves)
+__attribute__((amdgpu_waves_per_eu(Walker::kMinWavesPerSimd)))
+void paged_decode_group_kernel(const AttnParams a) {
+    const int lane = threadIdx.x & 63;
+    const int item = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int num_groups = a.num_seqs / a.group_size;
+    if (item >= num_groups * a.num_kv_heads * a.max_parts) return;
+    const int g = item % a.num_kv_heads;
+    const int rest = item / a.num_kv_heads;
+    const int k = rest % num_groups;
+    const int part = rest / num_groups;
+    const int G = a.group;
+    const int n = lane & 15;
+    const int sample = n / G < a.group_size ? n / G : a.group_size - 1;
+    const int seq = k * a.group_size + sample;
+    bool active = false;
+    if (n < a.group_size * G) {
+        const int L = clamp_len(a, a.seq_lens[seq]);
+        active = L > 0 && in_shared_part(a, seq, part, L);
+    }
+    const unsigned long long act = __ballot(active);
+    if (act == 0) return;
+    // the blocks of the partition, through the table of a sequence that shares it
+    const int table_seq = __shfl(seq, __builtin_ctzll(act), 64);
+    const int t_begin = part * a.part_tokens;
+    const int t_stop = t_begin + a.part_tokens;
+    const size_t head_row = (size_t)seq * a.num_kv_heads * G + (size_t)g * G + n % G;
+    Walker st;
+    st.init(lane);
+    st.begin_columns(a, table_seq, g, t_stop, head_row, active);
+    st.walk(t_begin, t_stop, a.scale * kLog2e);
+    st.write_partial_at(a, head_row * a.max_parts + part, active);
 }
 
 // Merge the partitions of every (segment, column) that has more than one:
@@ -364,11 +417,45 @@ hipError_t launch_walker(const AttnParams& a, hipStream_t stream) {
 // Matrix cores for 16-bit K/V with head_dim 128 and 4 or 8 query heads per
 // kv head; the vector walker otherwise. STREAM selects the K/V load policy.
 template <typename S, int D, int G, bool STREAM>
+using DecodeWalker = std::conditional_t<S::bytes == 2 && D == 128 && (G == 4 || G == 8),
+                                        MfmaWalker<S, G, STREAM>, VecWalker<S, D, G, STREAM>>;
+
+template <typename S, int D, int G, bool STREAM>
 hipError_t launch_typed(const AttnParams& a, hipStream_t stream) {
-    if constexpr (S::bytes == 2 && D == 128 && (G == 4 || G == 8))
-        return launch_walker<MfmaWalker<S, G, STREAM>>(a, stream);
-    else
-        return launch_walker<VecWalker<S, D, G, STREAM>>(a, stream);
+    return launch_walker<DecodeWalker<S, D, G, STREAM>>(a, stream);
+}
+
+// Sampling groups: the shared partitions on the matrix cores, one wave per
+// (group, kv head, partition), then every sequence's own partitions and the
+// reduce over both.
+template <typename S, int G, bool STREAM>
+hipError_t launch_grouped_typed(const AttnParams& a, hipStream_t stream) {
+    const long long items = (long long)(a.num_seqs / a.group_size) * a.num_kv_heads * a.max_parts;
+    if (a.max_parts > 1 && items > 0) {
+        hipLaunchKernelGGL((paged_decode_group_kernel<MfmaWalker<S, G, STREAM>>),
+                           dim3((unsigned)((items + kWaves - 1) / kWaves)), dim3(64 * kWaves), 0,
+                           stream, a);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return launch_partitioned<DecodeWalker<S, 128, G, STREAM>>(a, stream);
+}
+
+template <typename S, bool STREAM>
+hipError_t launch_grouped_group(const AttnParams& a, hipStream_t stream) {
+    switch (a.group) {
+        case 1: return launch_grouped_typed<S, 1, STREAM>(a, stream);
+        case 2: return launch_grouped_typed<S, 2, STREAM>(a, stream);
+        case 4: return launch_grouped_typed<S, 4, STREAM>(a, stream);
+        case 8: return launch_grouped_typed<S, 8, STREAM>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename S>
+hipError_t launch_grouped_policy(const AttnParams& a, hipStream_t stream) {
+    return a.kv_stream ? launch_grouped_group<S, true>(a, stream)
+                       : launch_grouped_group<S, false>(a, stream);
 }
 
 template <typename S, int D, bool STREAM>
@@ -455,6 +542,16 @@ hipError_t launch_paged_attention_multi(const AttnParams& a, hipStream_t stream)
     switch (a.dtype) {
         case PKV_F16: return launch_multi_policy<F16>(a, stream);
         case PKV_BF16: return launch_multi_policy<BF16>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// Parallel-sampling groups: 16-bit K/V, head_dim 128, fixed partitions.
+hipError_t launch_paged_attention_grouped(const AttnParams& a, hipStream_t stream) {
+    if (a.head_dim != 128 || a.balanced || a.group_size * a.group > 16) return hipErrorInvalidValue;
+    switch (a.dtype) {
+        case PKV_F16: return launch_grouped_policy<F16>(a, stream);
+        case PKV_BF16: return launch_grouped_policy<BF16>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -134,6 +134,35 @@ struct MfmaWalker {
         for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    // Columns taken from several sequences that share the blocks of tokens
+    // [0, L) (the samples of one prompt): the tables of table_seq are walked,
+    // this lane's column n reads q row qrow_idx if active and a zero row
+    // otherwise, and every token of the walked range is visible to every
+    // column.
+    __device__ __forceinline__ void begin_columns(const AttnParams& a, int table_seq, int g, int L,
+                                                  size_t qrow_idx, bool active) {
+        log2_bs = a.log2_bs;
+        bs_mask = (1 << a.log2_bs) - 1;
+        nblk_valid = (L + bs_mask) >> a.log2_bs;
+        max_phys = a.num_blocks;
+        trow = a.block_tables + (size_t)table_seq * a.max_blocks;
+        head_stride_bytes = (size_t)a.num_kv_heads * ((size_t)ROW << a.log2_bs);
+        kvhead_off = (size_t)g * ((size_t)ROW << a.log2_bs);
+        kbase = reinterpret_cast<const char*>(a.k_pool);
+        vbase = reinterpret_cast<const char*>(a.v_pool);
+        ncols = 16;
+        lim = L - 1;
+        mask_from = L;
+        orow = qrow_idx;
+        const char* qrow = reinterpret_cast<const char*>(a.q) + qrow_idx * ROW + 16 * q;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qb[s] = active ? load16(qrow + 64 * s) : u32x4{0u, 0u, 0u, 0u};
+        m = -__builtin_inff();
+        l = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
     __device__ __forceinline__ void load_window(int first_block) {
         wb = first_block;
         tv = (wb + lane < nblk_valid) ? trow[wb + lane] : 0;
@@ -298,9 +327,13 @@ struct MfmaWalker {
 
     __device__ __forceinline__ void write_partial(const AttnParams& a, size_t row0,
                                                   size_t row_stride) {
+        write_partial_at(a, row0 + (size_t)n * row_stride, n < ncols);
+    }
+
+    // Column n's partial result into workspace row `row` (this lane's), if active.
+    __device__ __forceinline__ void write_partial_at(const AttnParams& a, size_t row, bool active) {
         const float lsum = total_sum();
-        if (n >= ncols) return;
-        const size_t row = row0 + (size_t)n * row_stride;
+        if (!active) return;
         float* dst = a.ws_acc + row * D + 32 * q;
 #pragma unroll
         for (int i = 0; i < 4; ++i)

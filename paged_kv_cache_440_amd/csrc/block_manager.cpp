@@ -294,6 +294,36 @@ int pkv_bm_take_copies(pkv_block_manager* bm, int32_t* pairs, int max_pairs) {
     return n;
 }
 
+int pkv_bm_shared_prefix(const pkv_block_manager* bm, const int64_t* seq_ids, int n,
+                         int group_size, int32_t* shared_tokens) {
+    if (!bm || n < 0 || group_size <= 0 || n % group_size != 0) return PKV_ERR_INVALID;
+    if (n == 0) return PKV_OK;
+    if (!seq_ids || !shared_tokens) return PKV_ERR_INVALID;
+    std::vector<const pkv_block_manager::Seq*> seqs;
+    try {
+        seqs.reserve(n);
+    } catch (...) {
+        return PKV_ERR_INVALID;
+    }
+    for (int i = 0; i < n; ++i) {             // validate everything before writing
+        auto it = bm->seqs.find(seq_ids[i]);
+        if (it == bm->seqs.end() || it->second.swapped) return PKV_ERR_INVALID;
+        seqs.push_back(&it->second);
+    }
+    for (int k = 0; k < n / group_size; ++k) {
+        const pkv_block_manager::Seq* first = seqs[(size_t)k * group_size];
+        size_t blocks = first->table.size();
+        for (int j = 1; j < group_size; ++j) {
+            const std::vector<int32_t>& t = seqs[(size_t)k * group_size + j]->table;
+            size_t b = 0;
+            while (b < blocks && b < t.size() && t[b] == first->table[b]) ++b;
+            blocks = b;
+        }
+        shared_tokens[k] = (int32_t)(blocks * (size_t)bm->block_size);
+    }
+    return PKV_OK;
+}
+
 int pkv_bm_build_batch(const pkv_block_manager* bm, const int64_t* seq_ids, int n,
                        int32_t* tables, int max_blocks, int32_t* seq_lens) {
     if (!bm || n < 0 || max_blocks <= 0) return PKV_ERR_INVALID;

@@ -40,6 +40,11 @@ struct AttnParams {
                                    // launcher, the persistent wave count in the kernels
     int balanced;                  // 1: balanced schedule (see attention.hip)
     int kv_stream;                 // 1: non-temporal K/V loads (PKV_KV_STREAM), 0: cached
+    // sampling groups (pkv_paged_attention_decode_grouped): sequences
+    // k*group_size .. (k+1)*group_size - 1 share their first shared_tokens[k]
+    // tokens' blocks; shared_tokens is null for every other call
+    int group_size;
+    const int32_t* shared_tokens;
     int num_queries;               // new tokens per sequence (1: decode); q and out are
                                    // [B][num_queries][H][D]. A segment (seq, kv head) has
                                    // num_queries * group columns (query token, head).
@@ -109,6 +114,7 @@ hipError_t launch_append(const AppendParams& a, hipStream_t stream);
 hipError_t launch_append_fp8(const AppendFp8Params& a, hipStream_t stream);
 hipError_t launch_paged_attention_fp8(const AttnParams& a, hipStream_t stream);
 hipError_t launch_paged_attention_multi(const AttnParams& a, hipStream_t stream);
+hipError_t launch_paged_attention_grouped(const AttnParams& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyParams& a, hipStream_t stream);
 
 }  // namespace pkv

@@ -201,6 +201,22 @@ def _pool(num_blocks, num_kv_heads, block_size, head_dim, dtype, seed_seq, dist,
     return pool
 
 
+def shared_tokens(w: Workload, group_size: int) -> np.ndarray:
+    """int32 [B // group_size]: per group of group_size consecutive
+    sequences, block_size times the number of leading logical blocks all of
+    them map to the same physical block (read off the tables)."""
+    out = np.zeros(w.num_seqs // group_size, dtype=np.int32)
+    bs = w.block_size
+    for k in range(len(out)):
+        rows = range(k * group_size, (k + 1) * group_size)
+        blocks = min(-(-int(w.seq_lens[i]) // bs) for i in rows)
+        b = 0
+        while b < blocks and len({int(w.block_tables[i, b]) for i in rows}) == 1:
+            b += 1
+        out[k] = b * bs
+    return out
+
+
 def fp8_head_scales(num_kv_heads: int, spread: float) -> np.ndarray:
     """Per-head scales for FP8 pools: head g gets (1 + g / Hkv) * spread / 448,
     so N(0, 1) values of magnitude up to `spread` stay within the format."""

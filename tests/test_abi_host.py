@@ -306,3 +306,32 @@ def test_swap_refuses_memory_the_device_cannot_reach(lib):
     p = pageable.ctypes.data
     for kw in (dict(), dict(sk=p, sv=p, dk=p, dv=p, mapping=mapping.ctypes.data)):
         assert swap(lib, **kw) in (INVALID, -4)
+
+
+def attn_grouped(lib, **kw):
+    a = dict(out=FAKE, out_dtype=0, q=FAKE, k=FAKE, v=FAKE, tables=FAKE, max_blocks=8, lens=FAKE,
+             max_seq_len=100, B=8, H=4, Hkv=4, D=128, bs=16, nb=32, scale=0.1, part=64,
+             gs=4, shared=FAKE, ws=FAKE, ws_bytes=1 << 20, dtype=1, policy=1)
+    a.update(kw)
+    return lib.pkv_paged_attention_decode_grouped(
+        a["out"], a["out_dtype"], a["q"], a["k"], a["v"], a["tables"], a["max_blocks"], a["lens"],
+        a["max_seq_len"], a["B"], a["H"], a["Hkv"], a["D"], a["bs"], a["nb"], a["scale"],
+        a["part"], a["gs"], a["shared"], a["ws"], a["ws_bytes"], a["dtype"], a["policy"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(part=0), INVALID),                  # fixed partitions only
+    (dict(part=-1), INVALID),
+    (dict(gs=0), INVALID),
+    (dict(B=6), INVALID),                     # not a multiple of the group size
+    (dict(shared=0), INVALID),
+    (dict(dtype=0), UNSUPPORTED),             # fp32 K/V
+    (dict(dtype=3), UNSUPPORTED),             # FP8 pools
+    (dict(D=64), UNSUPPORTED),
+    (dict(gs=8, H=16, Hkv=4), UNSUPPORTED),   # 8 samples x 4 heads > 16 columns
+    (dict(ws=0), WORKSPACE),
+    (dict(policy=7), INVALID),
+    (dict(B=0), OK),
+])
+def test_attention_grouped_validation(lib, kw, status):
+    assert attn_grouped(lib, **kw) == status

@@ -297,3 +297,69 @@ def test_random_steps_keep_every_history(seed):
             assert c.history(bm, s) == hist[s]
         assert len(bm.free) + sum(1 for r in bm.ref if r) == nb
         assert len(bm.host_free) + sum(1 for r in bm.host_ref if r) == nh
+
+
+# --------------------------------------------------------- shared prefixes
+# Samples forked from one prompt read the prompt's blocks by reference
+# ([summary] "블록 공유"); the grouped decode reads such blocks once per group.
+# What must hold: inside the reported shared tokens, every sequence of the
+# group holds the same token in the same place.
+
+def test_shared_prefix_of_forked_samples():
+    bm = BlockManagerOracle(num_blocks=200, block_size=16)
+    c, hist = Contents(200, 0, 16), {0: []}
+    bm.add_sequence(0)
+    _grow(bm, c, 0, hist, 1032, 0)                            # 64 full blocks + 8 tokens
+    for s in range(1, 8):
+        bm.fork(0, s)
+        hist[s] = list(hist[0])
+    assert bm.shared_prefix(list(range(8)), 8) == [65 * 16]   # the partial block too, for now
+    tok = 5000
+    for s in range(8):
+        tok = _grow(bm, c, s, hist, 1, tok)                   # copy-on-write of the partial block
+    assert bm.shared_prefix(list(range(8)), 8) == [64 * 16]
+    assert bm.shared_prefix(list(range(8)), 4) == [64 * 16, 64 * 16]
+    assert bm.shared_prefix(list(range(8)), 1) == [len(bm.tables[s]) * 16 for s in range(8)]
+    bm.add_sequence(99)
+    for _ in range(40):
+        bm.append_token(99)
+    assert bm.shared_prefix([0, 99], 2) == [0]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_shared_tokens_hold_the_same_history(seed):
+    """Random forks, growth and frees: inside every group's reported shared
+    tokens (and each sequence's length) the group's histories agree."""
+    rng = random.Random(100 + seed)
+    bm, c = BlockManagerOracle(64, 4), Contents(64, 0, 4)
+    hist, tok, next_id = {}, 0, 0
+    for _ in range(120):
+        live = sorted(bm.tables)
+        op = rng.random()
+        if op < 0.15 or not live:
+            bm.add_sequence(next_id)
+            hist[next_id] = []
+            next_id += 1
+        elif op < 0.35:
+            parent = rng.choice(live)
+            bm.fork(parent, next_id)
+            hist[next_id] = list(hist[parent])
+            next_id += 1
+        elif op < 0.42 and len(live) > 1:
+            s = rng.choice(live)
+            bm.free_sequence(s)
+            del hist[s]
+        else:
+            s = rng.choice(live)
+            try:
+                tok = _grow(bm, c, s, hist, 1, tok)
+            except NoFreeBlock:
+                pass
+        live = sorted(bm.tables)
+        for size in (1, 2, 3):
+            ids = live[:len(live) // size * size]
+            for k, shared in enumerate(bm.shared_prefix(ids, size) if ids else []):
+                group = ids[k * size:(k + 1) * size]
+                upto = min([shared] + [len(hist[s]) for s in group])
+                assert len({tuple(hist[s][:upto]) for s in group}) == 1
+                assert shared % 4 == 0

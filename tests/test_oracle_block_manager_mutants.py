@@ -124,10 +124,34 @@ class SwapForgetsTheHostSide(obm.BlockManagerOracle):
         return pairs
 
 
+class SharedByTheFirstTwo(obm.BlockManagerOracle):
+    """Compares only the first two sequences of a group."""
+    def shared_prefix(self, seqs, group_size):
+        seqs = list(seqs)
+        out = []
+        for k in range(0, len(seqs), group_size):
+            pair = seqs[k:k + min(2, group_size)]
+            out += super().shared_prefix(pair, len(pair))
+        return out
+
+
+class SharedCountsAllBlocks(obm.BlockManagerOracle):
+    """Counts every block any sequence of the group shares with the first."""
+    def shared_prefix(self, seqs, group_size):
+        seqs = list(seqs)
+        out = []
+        for k in range(0, len(seqs), group_size):
+            first = self.tables[seqs[k]]
+            n = max(sum(1 for b in range(min(len(first), len(self.tables[s])))
+                        if self.tables[s][b] == first[b]) for s in seqs[k:k + group_size])
+            out.append(n * self.block_size)
+        return out
+
+
 MUTANTS = {c.__name__: c for c in
            (CopyEvenWhenFull, NoDecrementOnCopy, CopyOnEveryPartialWrite, BlockPerToken,
             FreeInReverse, SwapKeepsDeviceBlocks, SwapEveryReference, SwapInPairsBackwards,
-            SwapPartly, SwapForgetsTheHostSide)}
+            SwapPartly, SwapForgetsTheHostSide, SharedByTheFirstTwo, SharedCountsAllBlocks)}
 
 
 def _failing():
