@@ -64,14 +64,16 @@ def measured_traffic(workload: str, partition: int, policy: str):
 # wave); fixed partitions win for many short sequences, for sequences that
 # share prefix blocks (neighbours run side by side and hit the cache) and for
 # the FP8 vector walker. The K/V load policy follows the workload: cached
-# loads (kv_reuse) where tables share blocks, streaming loads otherwise.
+# loads (kv_reuse) where tables share blocks and the plain decode call reads
+# them once per sequence, streaming loads otherwise (the grouped call reads
+# shared blocks once per group).
 DEFAULT_SCHEDULE = {
     "opt13b_fp16": "balanced",
     "long_gqa_bf16": "balanced",
     "long_gqa_fp8": "balanced",
     "llama13b_bf16": 512,
-    "shared_prefix_fp16": 512,
-    "shared_prefix_cow_fp16": 512,
+    "shared_prefix_fp16": 1024,          # grouped call (512 for --no-grouped)
+    "shared_prefix_cow_fp16": 1024,
     "opt13b_fp8": 512,
     "opt13b_spec4_fp16": "balanced",
     "tiny_fp32": 512,
@@ -387,7 +389,11 @@ def main():
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     max_len = w.max_seq_len
     stream = torch.cuda.current_stream()
-    reuse = w.shared_blocks if args.kv_policy == "auto" else args.kv_policy == "reuse"
+    grouped = "samples" in w.info and not args.no_grouped and args.partition > 0
+    # cached loads where tables share blocks that several waves read; the
+    # grouped entry reads shared blocks once, so it streams
+    auto_reuse = w.shared_blocks and not grouped
+    reuse = auto_reuse if args.kv_policy == "auto" else args.kv_policy == "reuse"
 
     if w.num_queries > 1:
         def attention():
@@ -407,7 +413,7 @@ def main():
 
         def append():
             pkv.kv_cache_append_fp8(k_new, v_new, kp, vp, ks, vs, tables, lens, stream=stream)
-    elif "samples" in w.info and not args.no_grouped and args.partition > 0:
+    elif grouped:
         samples = w.info["samples"]
         shared = torch.from_numpy(wl.shared_tokens(w, samples)).to(dev)
 
@@ -429,8 +435,7 @@ def main():
 
     entry = ("paged_attention_multi" if w.num_queries > 1 else
              "paged_attention_decode_fp8" if w.fp8 else
-             "paged_attention_decode_grouped" if ("samples" in w.info and not args.no_grouped
-                                                  and args.partition > 0) else
+             "paged_attention_decode_grouped" if grouped else
              "paged_attention_decode")
 
     def step(ev=None):
