@@ -90,3 +90,56 @@ def test_parallel_sampling_through_the_block_manager(prompt_len, samples, steps)
     # a partly filled shared last block is copied by all but one sample
     want = samples - 1 if prompt_len % bs else 0
     assert copies_seen == want
+
+
+@pytest.mark.parametrize("prompt_len,samples", [(200, 4), (130, 8)])
+def test_grouped_decode_with_shared_prefix_from_the_manager(prompt_len, samples):
+    """The block manager's shared-prefix report drives the grouped decode:
+    after forking and a few decode steps, the grouped call equals the oracle's
+    dense attention over each sample's own history."""
+    nb, hkv, bs, d, h = 64, 2, 16, 128, 2
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(prompt_len + samples)
+    k_pool = torch.full((nb, hkv, bs, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.full_like(k_pool, float("nan"))
+    bm = BlockManager(nb, bs)
+    hist = {0: []}
+
+    def step(seqs):
+        for s in seqs:
+            bm.append_token(s)
+        pkv.copy_blocks(k_pool, v_pool, torch.from_numpy(bm.take_copies()).to(dev))
+        tables, lens = bm.build_batch(seqs, nb)
+        k = torch.from_numpy(rng.standard_normal((len(seqs), hkv, d), dtype=np.float32)).bfloat16()
+        v = torch.from_numpy(rng.standard_normal((len(seqs), hkv, d), dtype=np.float32)).bfloat16()
+        pkv.kv_cache_append(k.to(dev), v.to(dev), k_pool, v_pool, torch.from_numpy(tables).to(dev),
+                            torch.from_numpy(lens).to(dev))
+        for i, s in enumerate(seqs):
+            hist[s].append((k[i], v[i]))
+
+    bm.add_sequence(0)
+    for _ in range(prompt_len):
+        step([0])
+    ids = list(range(1, samples + 1))
+    for s in ids:
+        bm.fork(0, s)
+        hist[s] = list(hist[0])
+    bm.free_sequence(0)
+    for _ in range(5):
+        step(ids)
+    shared = bm.shared_prefix(ids, samples)
+    assert shared[0] == (prompt_len // bs) * bs
+    tables, lens = bm.build_batch(ids, nb)
+    q = torch.from_numpy(rng.standard_normal((samples, h, d), dtype=np.float32)).bfloat16()
+    out = torch.empty((samples, h, d), dtype=torch.float32, device=dev)
+    pkv.paged_attention_decode_grouped(out, q.to(dev), k_pool, v_pool,
+                                       torch.from_numpy(tables).to(dev),
+                                       torch.from_numpy(lens).to(dev), int(lens.max()),
+                                       1.0 / np.sqrt(d), samples,
+                                       torch.from_numpy(shared).to(dev), partition_size=64)
+    out = out.cpu().double().numpy()
+    for i, s in enumerate(ids):
+        K = torch.stack([r[0] for r in hist[s]]).float().numpy()
+        V = torch.stack([r[1] for r in hist[s]]).float().numpy()
+        ref = dense_decode_attention(q[i].float().numpy(), K, V, 1.0 / np.sqrt(d))
+        assert np.abs(out[i] - ref).max() <= 2e-3
