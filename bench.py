@@ -85,9 +85,10 @@ def pkv_balanced() -> int:
     return PARTITION_BALANCED
 
 
-def cpu_baseline(w):
-    """The oracle, as it stands, on the host: one decode step (append, then
-    attention) over the whole batch, single-threaded float64 numpy."""
+def cpu_baseline(w, min_seconds: float = 10.0):
+    """The oracle, as it stands, on the host: decode steps (append, then
+    attention) over the whole batch, single-threaded float64 numpy, repeated
+    for about min_seconds."""
     import torch
     from threadpoolctl import threadpool_limits
     from oracle import (fp8_dequantize_pool, paged_decode_attention, paged_multi_query_attention,
@@ -103,8 +104,8 @@ def cpu_baseline(w):
 
     q = widen(bits(w.q))
     kb, vb = bits(w.k_pool), bits(w.v_pool)
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
+
+    def one_step():
         if w.fp8:
             ks, vs = w.k_scales.numpy(), w.v_scales.numpy()
             k2, v2 = pool_after_append_fp8(kb, vb, w.k_new.float().numpy(),
@@ -121,10 +122,21 @@ def cpu_baseline(w):
                                         w.scale)
         else:
             paged_decode_attention(q, kf, vf, w.block_tables, w.seq_lens, w.block_size, w.scale)
-        dt = time.perf_counter() - t0
-    return {"value": w.num_seqs * w.num_queries / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"the whole batch ({w.num_seqs} sequences, all heads): one append + "
-                      f"attention step, float64 numpy, one thread, {dt:.1f} s wall"}
+
+    # whole steps until at least min_seconds of oracle work (one step at least)
+    with threadpool_limits(limits=1):
+        steps = 0
+        t0 = time.perf_counter()
+        while True:
+            one_step()
+            steps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    return {"value": steps * w.num_seqs * w.num_queries / dt, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{steps} whole decode steps of the batch ({w.num_seqs} sequences, all "
+                      f"heads: append + attention), float64 numpy, one thread, {dt:.1f} s wall"}
 
 
 def block_manager_bench(steps: int, warmup: int) -> None:
@@ -279,14 +291,19 @@ def swap_bench(steps: int, warmup: int, with_cpu: bool) -> None:
         hvn = np.empty_like(hkn)
         pairs_out = np.stack([blocks, host], 1)
         pairs_in = np.stack([host, blocks], 1)
+        trips = 0
         t0 = time.perf_counter()
-        hkn, hvn = pool_after_swap(kp, vp, hkn, hvn, pairs_out)
-        pool_after_swap(hkn, hvn, kp, vp, pairs_in)
-        dt = time.perf_counter() - t0
-        rec["cpu_baseline"] = {"value": 2 * moved / dt / 1e9, "unit": "GB/s", "cores": 1,
+        while True:                    # round trips for about 10 s of host work
+            hkn, hvn = pool_after_swap(kp, vp, hkn, hvn, pairs_out)
+            pool_after_swap(hkn, hvn, kp, vp, pairs_in)
+            trips += 1
+            dt = time.perf_counter() - t0
+            if dt >= 10.0:
+                break
+        rec["cpu_baseline"] = {"value": trips * 2 * moved / dt / 1e9, "unit": "GB/s", "cores": 1,
                                "kind": "oracle",
-                               "sample": f"one round trip of the same {n} blocks, numpy block "
-                                         f"copies on the host, {dt:.2f} s wall"}
+                               "sample": f"{trips} round trips of the same {n} blocks, numpy "
+                                         f"block copies on the host, {dt:.1f} s wall"}
     print(json.dumps(rec), flush=True)
 
 
