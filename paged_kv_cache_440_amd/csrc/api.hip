@@ -119,7 +119,8 @@ int prepare_attention(pkv::AttnParams& a, void* out, int out_dtype, const void* 
     a.num_queries = num_queries;
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_pool || !v_pool || !block_tables || !seq_lens) return PKV_ERR_INVALID;
-    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_INVALID;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PKV_ERR_INVALID;
     if ((long long)num_seqs * max_blocks_per_seq > INT32_MAX) return PKV_ERR_INVALID;
     if ((long long)num_seqs * num_queries * num_heads * head_dim > INT32_MAX) return PKV_ERR_INVALID;
     const int cols = group * num_queries;       // output rows per (sequence, kv head)

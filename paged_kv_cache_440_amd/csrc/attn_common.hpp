@@ -23,6 +23,31 @@ __device__ __forceinline__ void store_out(void* out, int out_dtype, size_t idx, 
     }
 }
 
+// Eight consecutive outputs from idx (a multiple of 8; out is 16-byte
+// aligned) with 16-byte stores, rounded as store_out rounds.
+__device__ __forceinline__ void store_out8(void* out, int out_dtype, size_t idx, const float (&v)[8]) {
+    if (out_dtype == PKV_F32) {
+        f32x4* p = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + idx);
+        p[0] = f32x4{v[0], v[1], v[2], v[3]};
+        p[1] = f32x4{v[4], v[5], v[6], v[7]};
+        return;
+    }
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t lo, hi;
+        if (out_dtype == PKV_F16) {
+            lo = __builtin_bit_cast(uint16_t, (_Float16)v[2 * k]);
+            hi = __builtin_bit_cast(uint16_t, (_Float16)v[2 * k + 1]);
+        } else {
+            lo = __builtin_bit_cast(uint16_t, (__bf16)v[2 * k]);
+            hi = __builtin_bit_cast(uint16_t, (__bf16)v[2 * k + 1]);
+        }
+        w[k] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + idx) = w;
+}
+
 __device__ __forceinline__ int clamp_len(const AttnParams& a, int L) {
     L = L < 0 ? 0 : L;
     return L < a.max_tokens ? L : a.max_tokens;

@@ -223,8 +223,12 @@ struct Fp8VecWalker {
             const float inv = 1.0f / lsum;
             if (tok == 0) {
 #pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    store_out(a.out, a.out_dtype, (row0 + h) * D + piece * EPL + e, acc[h][e] * inv);
+                for (int r = 0; r < EPL / 8; ++r) {
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = acc[h][8 * r + e] * inv;
+                    store_out8(a.out, a.out_dtype, (row0 + h) * D + piece * EPL + 8 * r, v);
+                }
             }
         }
     }
@@ -237,8 +241,11 @@ struct Fp8VecWalker {
             merge_classes(h, mall, lsum);
             const size_t row = row0 + (size_t)h * row_stride;
             if (tok == 0) {
+                f32x4* dst = reinterpret_cast<f32x4*>(a.ws_acc + row * D + piece * EPL);
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) a.ws_acc[row * D + piece * EPL + e] = acc[h][e];
+                for (int r = 0; r < EPL / 4; ++r)
+                    dst[r] = f32x4{acc[h][4 * r], acc[h][4 * r + 1], acc[h][4 * r + 2],
+                                   acc[h][4 * r + 3]};
             }
             if (lane == 0) {
                 a.ws_ml[2 * row] = mall;
@@ -468,24 +475,22 @@ struct Fp8MfmaWalker {
 
     __device__ __forceinline__ void write_final(const AttnParams& a, int seq, int g) {
         const float inv = vscale / strided_sum<16>(l);
-        if (n >= G) return;
-        const size_t base = ((size_t)seq * a.num_kv_heads * G + (size_t)g * G + n) * D + 32 * q;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) store_out(a.out, a.out_dtype, base + 8 * i + c, acc[c][i] * inv);
+        const size_t row = (size_t)seq * a.num_kv_heads * G + (size_t)g * G + (n < G ? n : 0);
+        void* out = a.out;
+        const int dt = a.out_dtype;
+        store_column_tile(acc, inv, row, n < G,
+                          [&](size_t r, int piece, f32x4 v) { store_out4(out, dt, r, piece, v); });
     }
 
     __device__ __forceinline__ void write_partial(const AttnParams& a, size_t row0,
                                                   size_t row_stride) {
         const float lsum = strided_sum<16>(l);
+        const size_t row = row0 + (size_t)(n < G ? n : 0) * row_stride;
+        float* ws = a.ws_acc;
+        store_column_tile(acc, vscale, row, n < G, [&](size_t r, int piece, f32x4 v) {
+            *reinterpret_cast<f32x4*>(ws + r * D + 4 * piece) = v;
+        });
         if (n >= G) return;
-        const size_t row = row0 + (size_t)n * row_stride;
-        float* dst = a.ws_acc + row * D + 32 * q;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) dst[8 * i + c] = acc[c][i] * vscale;
         if (q == 0) {
             a.ws_ml[2 * row] = m;
             a.ws_ml[2 * row + 1] = lsum;

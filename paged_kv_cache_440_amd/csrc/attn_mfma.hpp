@@ -45,7 +45,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(BF16, const u32x4& a, const u32x4& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -66,6 +65,64 @@ __device__ __forceinline__ uint32_t to16(F16, float x) {
 __device__ __forceinline__ float from16(BF16, uint32_t h) { return u2f(h << 16); }
 __device__ __forceinline__ float from16(F16, uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// The results of up to 16 columns leave a matrix-core walker as a 16 x 128
+// tile: lane (n, q) holds dims 32q .. 32q+31 of column n (acc[c][i] is dim
+// 32q + 8i + c). Stored straight from registers, every store instruction
+// would touch 16 rows at once; the tile is transposed through the wave's own
+// LDS slice instead, so that each instruction writes two whole rows (lanes
+// 0-31 one row, 32-63 the next). `row` is this lane's column's destination
+// row, `active` whether the column is written; store(row, piece, v) writes
+// dims 4 piece .. 4 piece + 3 of a row.
+// The calling wave's 8 KB slice of LDS (one allocation per kernel, however
+// many call sites).
+__device__ __forceinline__ f32x4 (*wave_tile())[32] {
+    __shared__ f32x4 tile[kWaves][16][32];
+    return tile[threadIdx.x >> 6];
+}
+
+template <class Store>
+__device__ __forceinline__ void store_column_tile(const f32x4 (&acc)[8], float scale, size_t row,
+                                                  bool active, Store store) {
+    const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+    f32x4 (*t)[32] = wave_tile();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        t[n][8 * q + 2 * i] = f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]} * scale;
+        t[n][8 * q + 2 * i + 1] = f32x4{acc[4][i], acc[5][i], acc[6][i], acc[7][i]} * scale;
+    }
+    // the wave's own LDS operations complete in order; only keep the compiler
+    // from moving the reads above the writes
+    __builtin_amdgcn_wave_barrier();
+    const unsigned long long act = __ballot(active);
+    const uint32_t row_lo = (uint32_t)row, row_hi = (uint32_t)(row >> 32);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int r = 2 * k + (lane >> 5);           // lane r holds column r (q = 0)
+        const size_t rr = ((size_t)(uint32_t)__shfl((int)row_hi, r, 64) << 32) |
+                          (uint32_t)__shfl((int)row_lo, r, 64);
+        const f32x4 v = t[r][lane & 31];
+        if ((act >> r) & 1) store(rr, lane & 31, v);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// dims 4 piece .. 4 piece + 3 of output row `row` (16-byte or 8-byte store)
+__device__ __forceinline__ void store_out4(void* out, int out_dtype, size_t row, int piece,
+                                           f32x4 v) {
+    const size_t idx = row * 128 + 4 * (size_t)piece;
+    if (out_dtype == PKV_F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + idx) = v;
+        return;
+    }
+    uint32_t h[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        h[k] = out_dtype == PKV_F16 ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[k])
+                                    : (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[k]);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + idx) =
+        u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
 }
 
 template <typename S, int G_, bool STREAM>
@@ -317,12 +374,10 @@ struct MfmaWalker {
     __device__ __forceinline__ void write_final(const AttnParams& a, int seq, int g) {
         const float lsum = total_sum();
         const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;   // 0: a query before the start
-        if (n >= ncols) return;
-        const size_t base = orow * D + 32 * q;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) store_out(a.out, a.out_dtype, base + 8 * i + c, acc[c][i] * inv);
+        void* out = a.out;
+        const int dt = a.out_dtype;
+        store_column_tile(acc, inv, orow, n < ncols,
+                          [&](size_t r, int piece, f32x4 v) { store_out4(out, dt, r, piece, v); });
     }
 
     __device__ __forceinline__ void write_partial(const AttnParams& a, size_t row0,
@@ -333,12 +388,11 @@ struct MfmaWalker {
     // Column n's partial result into workspace row `row` (this lane's), if active.
     __device__ __forceinline__ void write_partial_at(const AttnParams& a, size_t row, bool active) {
         const float lsum = total_sum();
+        float* ws = a.ws_acc;
+        store_column_tile(acc, 1.f, row, active, [&](size_t r, int piece, f32x4 v) {
+            *reinterpret_cast<f32x4*>(ws + r * D + 4 * piece) = v;
+        });
         if (!active) return;
-        float* dst = a.ws_acc + row * D + 32 * q;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) dst[8 * i + c] = acc[c][i];
         if (q == 0) {
             a.ws_ml[2 * row] = m;
             a.ws_ml[2 * row + 1] = lsum;

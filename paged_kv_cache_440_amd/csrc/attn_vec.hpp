@@ -230,9 +230,17 @@ struct VecWalker {
             merge_classes(h, mall, lsum);
             const float inv = 1.0f / lsum;
             if (tok == 0) {
+                if constexpr (EPL == 8) {
+                    float v[8];
 #pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    store_out(a.out, a.out_dtype, (row0 + h) * D + piece * EPL + e, acc[h][e] * inv);
+                    for (int e = 0; e < 8; ++e) v[e] = acc[h][e] * inv;
+                    store_out8(a.out, a.out_dtype, (row0 + h) * D + piece * EPL, v);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e)
+                        store_out(a.out, a.out_dtype, (row0 + h) * D + piece * EPL + e,
+                                  acc[h][e] * inv);
+                }
             }
         }
     }
@@ -247,8 +255,11 @@ struct VecWalker {
             merge_classes(h, mall, lsum);
             const size_t row = row0 + (size_t)h * row_stride;
             if (tok == 0) {
+                f32x4* dst = reinterpret_cast<f32x4*>(a.ws_acc + row * D + piece * EPL);
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) a.ws_acc[row * D + piece * EPL + e] = acc[h][e];
+                for (int r = 0; r < EPL / 4; ++r)
+                    dst[r] = f32x4{acc[h][4 * r], acc[h][4 * r + 1], acc[h][4 * r + 2],
+                                   acc[h][4 * r + 3]};
             }
             if (lane == 0) {
                 a.ws_ml[2 * row] = mall;

@@ -94,6 +94,7 @@ def attn(lib, **kw):
     (dict(lens=0), INVALID),
     (dict(out=0), INVALID),
     (dict(q=FAKE + 4), INVALID),            # misaligned
+    (dict(out=FAKE + 8), INVALID),          # output rows are written 16 bytes at a time
     (dict(part=64, ws=0), WORKSPACE),       # 100 tokens in 64-token partitions need a workspace
     (dict(part=64, ws=FAKE, ws_bytes=16), WORKSPACE),
     (dict(part=64, ws=FAKE + 8, ws_bytes=1 << 20), WORKSPACE),
