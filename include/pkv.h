@@ -28,6 +28,9 @@
  *   q, out           [num_seqs][num_heads][head_dim]
  *   k_new, v_new     [num_seqs][num_kv_heads][head_dim]
  *   block_mapping    int32 [num_pairs][2] = (source block, destination block)
+ * Alignment.  q, out, k_pool, v_pool, k_new and v_new must be 16-byte
+ *   aligned (the kernels move them 16 bytes at a time); PKV_ERR_INVALID
+ *   otherwise.
  * Element types.  pkv_dtype. In pkv_kv_cache_append and
  *   pkv_paged_attention_decode all of q, k_new, v_new, k_pool, v_pool share
  *   one of F32, F16, BF16. PKV_FP8_E4M3 is a pool storage type: pools of
