@@ -258,8 +258,8 @@ struct Fp8VecWalker {
 // ---------------------------------------------------------------------------
 // Matrix-core walker (2, 4 or 8 query heads per kv head, q in fp16 or bf16).
 // Same contractions and layouts as MfmaWalker<F16> (attn_mfma.hpp); the
-// codes are widened to fp16 (exact) on the way into the operands, and q is
-// converted to fp16 once per segment.
+// codes are widened to fp16 (exact) on the way into the operands, two per
+// v_cvt_scalef32_pk_f16_fp8, and q is converted to fp16 once per segment.
 //   K, step s of group q: dims 16q + 8s' .. (s = 2h + s', h = 0, 1 picks
 //     bytes 16q or 64 + 16q of the row): one 16-byte load gives two steps.
 //   V: lane (n, q) loads the 8 codes of dims 8n .. 8n+7 of each of its
@@ -361,15 +361,18 @@ struct Fp8MfmaWalker {
         }
     }
 
+    // two codes (bytes 2h, 2h + 1 of w) -> two fp16 values, packed, in one
+    // gfx950 conversion (scale 1: every E4M3 value is an fp16 value, exact)
+    template <bool H>
+    __device__ __forceinline__ static uint32_t pair_to_f16(uint32_t w) {
+        return __builtin_bit_cast(uint32_t,
+                                  __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, H));
+    }
+
     // 8 codes (two dwords) -> the fp16 A operand of one k-step
     __device__ __forceinline__ u32x4 codes_to_f16(uint32_t w0, uint32_t w1) {
-        float f[8];
-        fp8x4_to_f32(w0, f);
-        fp8x4_to_f32(w1, f + 4);
-        u32x4 r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = to16(F16{}, f[2 * i]) | (to16(F16{}, f[2 * i + 1]) << 16);
-        return r;
+        return u32x4{pair_to_f16<false>(w0), pair_to_f16<true>(w0), pair_to_f16<false>(w1),
+                     pair_to_f16<true>(w1)};
     }
 
     __device__ __forceinline__ void scores(const u32x4 (&kt)[2][2], float scale_log2,
@@ -428,19 +431,24 @@ struct Fp8MfmaWalker {
             bhi[w] = h0 | (h1 << 16);
             blo[w] = r0 | (r1 << 16);
         }
-        // widen the eight V pieces: vf[j][c] = code c of token j
-        float vf[8][8];
+        // widen the eight V pieces: hv[j][k] = codes 2k, 2k+1 of token j as fp16
+        uint32_t hv[8][4];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            fp8x4_to_f32(vt[j][0], vf[j]);
-            fp8x4_to_f32(vt[j][1], vf[j] + 4);
+            hv[j][0] = pair_to_f16<false>(vt[j][0]);
+            hv[j][1] = pair_to_f16<true>(vt[j][0]);
+            hv[j][2] = pair_to_f16<false>(vt[j][1]);
+            hv[j][3] = pair_to_f16<true>(vt[j][1]);
         }
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
+            // V^T tile c: value c of the eight tokens, token order as k-slots
             u32x4 av;
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-                av[w] = to16(F16{}, vf[2 * w][c]) | (to16(F16{}, vf[2 * w + 1][c]) << 16);
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t x = hv[2 * w][c >> 1], y = hv[2 * w + 1][c >> 1];
+                av[w] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+            }
             f32x4 o = acc[c] * alpha;
             o = mfma_16x16x32(F16{}, av, bhi, o);
             acc[c] = mfma_16x16x32(F16{}, av, blo, o);
