@@ -25,6 +25,23 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
     f[3] = hi[1];
 }
 
+// Codes H*2, H*2 + 1 (bytes) of w as two packed 16-bit values of type S, in
+// one gfx950 conversion (scale 1; every E4M3 value is exact in fp16 and bf16).
+template <typename S, bool H>
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t w);
+template <> __device__ __forceinline__ uint32_t fp8_pair<F16, false>(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, false));
+}
+template <> __device__ __forceinline__ uint32_t fp8_pair<F16, true>(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, true));
+}
+template <> __device__ __forceinline__ uint32_t fp8_pair<BF16, false>(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false));
+}
+template <> __device__ __forceinline__ uint32_t fp8_pair<BF16, true>(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true));
+}
+
 // q elements [first, first + n) of one row as float32
 template <typename Q>
 __device__ __forceinline__ float q_elem(const char* row, int i);
@@ -41,9 +58,11 @@ template <> __device__ __forceinline__ float q_elem<BF16>(const char* row, int i
 // ---------------------------------------------------------------------------
 // Vector walker (one query head per kv head). Lane l holds 16-byte piece
 // l % 8 (16 codes, dims 16 (l % 8) ..) of token l / 8 of an 8-token group;
-// one wave load covers 8 whole rows (1 KB). q is widened once per segment
-// to float32 and pre-multiplied by scale * log2(e) * k_scale, so a score is
-// one 16-term FMA chain plus a 3-step DPP row sum. Softmax bookkeeping is
+// one wave load covers 8 whole rows (1 KB). With fp16 / bf16 q, K codes are
+// widened to pairs of q's type and a score is 8 packed dot products plus a
+// 3-step DPP row sum, scaled by scale * log2(e) * k_scale; with fp32 q, q is
+// widened once per segment, pre-multiplied by that factor, and a score is a
+// 16-term FMA chain. Softmax bookkeeping is
 // that of the 16-bit vector walker (token classes merged at the end).
 template <typename Q, int G_, bool STREAM, int NLOAD_>
 struct Fp8VecWalker {
@@ -54,7 +73,9 @@ struct Fp8VecWalker {
     static constexpr int ROW = 128, LPT = 8, TPL = 8, NLOAD = NLOAD_, CHUNK = TPL * NLOAD, EPL = 16;
     static constexpr int kMinWavesPerSimd = 2;
 
-    float qf[G][EPL];
+    float qf[G][EPL];   // fp32 q: pre-multiplied by scale * log2(e) * k_scale
+    u32x4 qh[G][2];     // 16-bit q: the lane's 16 values as 8 pairs, unscaled
+    float qmul;         // scale * log2(e) * k_scale
     float m[G], l[G], acc[G][EPL];
     float vscale;
 
@@ -84,14 +105,20 @@ struct Fp8VecWalker {
         kbase = reinterpret_cast<const char*>(a.k_pool);
         vbase = reinterpret_cast<const char*>(a.v_pool);
         vscale = a.v_scales[g];
-        const float qmul = a.scale * kLog2e * a.k_scales[g];
+        qmul = a.scale * kLog2e * a.k_scales[g];
         const char* q0 = reinterpret_cast<const char*>(a.q) +
                          ((size_t)seq * a.num_kv_heads * G + (size_t)g * G) * D * Q::bytes;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
+            if constexpr (Q::bytes == 2) {
+                const char* qrow = q0 + (size_t)h * D * 2 + piece * EPL * 2;
+                qh[h][0] = load16(qrow);
+                qh[h][1] = load16(qrow + 16);
+            } else {
 #pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                qf[h][e] = q_elem<Q>(q0 + (size_t)h * D * Q::bytes, piece * EPL + e) * qmul;
+                for (int e = 0; e < EPL; ++e)
+                    qf[h][e] = q_elem<Q>(q0 + (size_t)h * D * Q::bytes, piece * EPL + e) * qmul;
+            }
             m[h] = -__builtin_inff();
             l[h] = 0.f;
 #pragma unroll
@@ -128,20 +155,35 @@ struct Fp8VecWalker {
         bool valid[NLOAD];
 #pragma unroll
         for (int j = 0; j < NLOAD; ++j) valid[j] = !TAIL || (c0 + j * TPL + tok < t_end);
-        // scores, one K piece widened at a time
+        // scores, one K piece widened at a time: for 16-bit q, to pairs of q's
+        // type and packed dot products (exact products, fp32 sums); for fp32
+        // q, to fp32 and FMAs
         float s[G][NLOAD];
 #pragma unroll
         for (int j = 0; j < NLOAD; ++j) {
-            float kf[EPL];
+            if constexpr (Q::bytes == 2) {
+                const u32x4 k0 = {fp8_pair<Q, false>(kr[j][0]), fp8_pair<Q, true>(kr[j][0]),
+                                  fp8_pair<Q, false>(kr[j][1]), fp8_pair<Q, true>(kr[j][1])};
+                const u32x4 k1 = {fp8_pair<Q, false>(kr[j][2]), fp8_pair<Q, true>(kr[j][2]),
+                                  fp8_pair<Q, false>(kr[j][3]), fp8_pair<Q, true>(kr[j][3])};
 #pragma unroll
-            for (int w = 0; w < 4; ++w) fp8x4_to_f32(kr[j][w], kf + 4 * w);
+                for (int h = 0; h < G; ++h) {
+                    float d = dot16(Q{}, qh[h][0], k0) + dot16(Q{}, qh[h][1], k1);
+                    d = group_sum<LPT>(d) * qmul;
+                    s[h][j] = (TAIL && !valid[j]) ? -__builtin_inff() : d;
+                }
+            } else {
+                float kf[EPL];
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float d = qf[h][0] * kf[0];
+                for (int w = 0; w < 4; ++w) fp8x4_to_f32(kr[j][w], kf + 4 * w);
 #pragma unroll
-                for (int e = 1; e < EPL; ++e) d = __builtin_fmaf(qf[h][e], kf[e], d);
-                d = group_sum<LPT>(d);
-                s[h][j] = (TAIL && !valid[j]) ? -__builtin_inff() : d;
+                for (int h = 0; h < G; ++h) {
+                    float d = qf[h][0] * kf[0];
+#pragma unroll
+                    for (int e = 1; e < EPL; ++e) d = __builtin_fmaf(qf[h][e], kf[e], d);
+                    d = group_sum<LPT>(d);
+                    s[h][j] = (TAIL && !valid[j]) ? -__builtin_inff() : d;
+                }
             }
         }
         // online softmax update, then the V pieces one at a time
