@@ -510,11 +510,10 @@ hipError_t launch_policy(const AttnParams& a, hipStream_t stream) {
 // there). head_dim is 128.
 template <typename Q, int G, bool STREAM>
 hipError_t launch_fp8_typed(const AttnParams& a, hipStream_t stream) {
-    // the vector walker keeps two loads of K and V per chunk in flight under
-    // the balanced schedule (four spill registers next to its bookkeeping),
-    // four under fixed partitions
+    // the vector walker keeps four loads of K and V per chunk in flight, two
+    // under the balanced schedule with fp32 q (four spill registers there)
     if constexpr (G == 1)
-        return a.balanced ? launch_balanced<Fp8VecWalker<Q, G, STREAM, 2>>(a, stream)
+        return a.balanced ? launch_balanced<Fp8VecWalker<Q, G, STREAM, Q::bytes == 2 ? 4 : 2>>(a, stream)
                           : launch_partitioned<Fp8VecWalker<Q, G, STREAM, 4>>(a, stream);
     else if constexpr (Q::bytes == 2)
         return launch_walker<Fp8MfmaWalker<Q, G, STREAM>>(a, stream);
