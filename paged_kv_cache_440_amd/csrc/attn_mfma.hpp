@@ -1,12 +1,15 @@
-// Matrix-core walker for paged decode attention (gfx950), for grouped-query
-// attention: 4 or 8 query heads share each kv head, 16-bit K/V, head_dim 128.
-// With G query heads per kv head every K/V byte feeds 2G flops; on the vector
-// units that is ALU-bound for G = 8, so both contractions of a 32-token chunk
-// run as v_mfma_f32_16x16x32_{bf16,f16} (fp32 accumulation):
+// Matrix-core walker for paged attention (gfx950), 16-bit K/V, head_dim 128.
+// It serves every case where several query columns read the same K/V: 4 or
+// 8 query heads per kv head (grouped-query decode), several new tokens per
+// sequence (multi-query attention, each column with its own causal limit)
+// and the samples of a prompt over their shared blocks (grouped decode).
+// With N columns every K/V byte feeds 2N flops; on the vector units that is
+// ALU-bound for N = 8, so both contractions of a 32-token chunk run as
+// v_mfma_f32_16x16x32_{bf16,f16} (fp32 accumulation):
 //
-//   S^T = K . Q^T     M = 16 tokens (two tiles), N = 16 query heads (G real,
-//                     the rest zero), K = 128 dims in four steps of 32.
-//   O^T += V^T . P^T  M = 16 dims (eight tiles), N = 16 query heads,
+//   S^T = K . Q^T     M = 16 tokens (two tiles), N = 16 columns (the unused
+//                     ones zero), K = 128 dims in four steps of 32.
+//   O^T += V^T . P^T  M = 16 dims (eight tiles), N = 16 columns,
 //                     K = the chunk's 32 tokens.
 //
 // Operand layouts (16x16x32): lane l, with n = l % 16 and q = l / 16, holds
@@ -35,7 +38,9 @@
 // weights keep about 16 significant bits.
 //
 // Masking: tokens at or past the range end (tail chunk only) get score -inf
-// and their V pieces are zeroed by select before the products.
+// and their V pieces are zeroed by select before the products; a token past
+// a column's causal limit (multi-query) gets score -inf in that column only,
+// and its V piece stays, since other columns see it.
 #pragma once
 
 #include "attn_common.hpp"
@@ -138,7 +143,6 @@ struct MfmaWalker {
     static constexpr int CHUNK = 32;            // tokens per chunk
     static constexpr int kMinWavesPerSimd = 2;
     static_assert(S::bytes == 2 && G_ <= 16, "16-bit K/V, at most 16 query heads");
-    static constexpr bool kMultiQuery = true;   // handles several new tokens per sequence
 
     f32x4 acc[8];       // O^T tiles: acc[c][i] = head n, dim 32q + 8i + c (unnormalised)
     float m, l;         // head n: running max (log2 units), this lane's partial sum
