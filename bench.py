@@ -37,12 +37,18 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and blank space removed, so
+    that a counter record stays valid across comment-only edits."""
+    import re
     csrc = os.path.join(ROOT, "paged_kv_cache_440_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".hpp")):
+            text = open(os.path.join(csrc, f), encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
             h.update(f.encode())
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
