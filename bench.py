@@ -488,7 +488,8 @@ def main():
     for e in evs:
         step(e)
     torch.cuda.synchronize()
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    attn_all = np.array([a.elapsed_time(b) for a, b in evs])
+    attn_ms = float(np.mean(attn_all))
 
     # practical read ceiling: the probe streams both pools once (contiguous
     # 16-byte loads, no compute), timed the same way on the same stream
@@ -557,6 +558,8 @@ def main():
             "unique_kv_bytes_per_step": unique_bytes,
         },
         "attention_us": attn_ms * 1e3,
+        "attention_us_median": float(np.median(attn_all)) * 1e3,
+        "attention_us_min": float(np.min(attn_all)) * 1e3,
         "kv_gbps": achieved,
         "kv_gbps_logical": logical,
         "kv_frac_of_peak": achieved / PEAK_HBM_GBPS,
