@@ -101,3 +101,15 @@ def test_unique_bytes_count_shared_prefix_rows_once():
     assert w.kv_bytes() == int(w.seq_lens.sum()) * per_token
     plain = wl.opt13b_fp16(num_seqs=4, len_range=(32, 200))
     assert plain.unique_kv_bytes() == plain.kv_bytes()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The library has no multi-GPU path: bench.py --gpus 2 says so and
+    exits non-zero, before touching a GPU."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in r.stderr and r.stdout == ""
