@@ -77,7 +77,7 @@ DEFAULT_SCHEDULE = {
     "opt13b_fp16": "balanced",
     "long_gqa_bf16": "balanced",
     "long_gqa_fp8": "balanced",
-    "llama13b_bf16": 512,
+    "llama13b_bf16": "balanced",
     "shared_prefix_fp16": 1024,          # grouped call (512 for --no-grouped)
     "shared_prefix_cow_fp16": 1024,
     "opt13b_fp8": 512,
