@@ -160,13 +160,66 @@ void paged_decode_grouped_kernel(const AttnParams a, int group_items) {
         decode_partition<SeqWalker>(a, item - group_items);
 }
 
+// Log-sum-exp fold of one output row's partial records (D floats of
+// unnormalised accumulator plus (max, sum) in base-2 units each). The wave
+// reads RPW records side by side: LPR = D / 4 lanes cover a record row with
+// one 16-byte load each, and lane group k folds records k, k + RPW, ... in
+// order with a running max,
+//   M' = max(M, m_r),  o' = o 2^(M - M') + acc_r 2^(m_r - M'),
+//   l' = l 2^(M - M') + l_r 2^(m_r - M'),
+// issuing the loads of many records before the first result is needed. The
+// groups are then merged pairwise by the same rule and out = o / l is written
+// by group 0. row_of(r) gives the workspace row of record r (0 <= r < nrec).
+template <int D, class RowOf>
+__device__ __forceinline__ void fold_records(const AttnParams& a, int nrec, RowOf row_of,
+                                             size_t orow) {
+    constexpr int LPR = D / 4, RPW = 64 / LPR;
+    static_assert(LPR * RPW == 64, "record rows of 16 to 64 lanes");
+    const int lane = threadIdx.x & 63, grp = lane / LPR, sub = lane % LPR;
+    float mrun = -__builtin_inff(), lsum = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int r = grp; r < nrec; r += RPW) {
+        const size_t row = row_of(r);
+        const float mr = a.ws_ml[2 * row], lr = a.ws_ml[2 * row + 1];
+        const f32x4 x = *reinterpret_cast<const f32x4*>(a.ws_acc + row * D + 4 * sub);
+        const float mnew = __builtin_fmaxf(mrun, mr);
+        const float keep = (mrun == -__builtin_inff()) ? 0.f : fast_exp2(mrun - mnew);
+        const float take = (mr == -__builtin_inff()) ? 0.f : fast_exp2(mr - mnew);
+        lsum = __builtin_fmaf(take, lr, lsum * keep);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = __builtin_fmaf(take, x[k], o[k] * keep);
+        mrun = mnew;
+    }
+#pragma unroll
+    for (int step = LPR; step < 64; step <<= 1) {
+        const float mo = __shfl_xor(mrun, step, 64), lo = __shfl_xor(lsum, step, 64);
+        const float mnew = __builtin_fmaxf(mrun, mo);
+        const float ka = (mrun == -__builtin_inff()) ? 0.f : fast_exp2(mrun - mnew);
+        const float kb = (mo == -__builtin_inff()) ? 0.f : fast_exp2(mo - mnew);
+        lsum = lsum * ka + lo * kb;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = o[k] * ka + __shfl_xor(o[k], step, 64) * kb;
+        mrun = mnew;
+    }
+    if (grp != 0) return;
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;   // 0: a query before the start
+    const size_t idx = orow * D + 4 * sub;
+    if (a.out_dtype == PKV_F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + idx) = o * inv;
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) store_out(a.out, a.out_dtype, idx + k, o[k] * inv);
+}
+
 // Merge the partitions of every (segment, column) that has more than one:
-//   M = max_p m_p,  out = sum_p exp2(m_p - M) acc_p / sum_p exp2(m_p - M) l_p
-// One wave per (sequence, kv head, column); lane j owns dims j, j + 64, ...
+//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p
+// One wave per (sequence, kv head, column), folding its partitions with
+// fold_records.
 template <int D>
 __global__ __launch_bounds__(64 * kWaves)
 void lse_reduce_kernel(const AttnParams a) {
-    const int lane = threadIdx.x & 63;
     const int cols = a.num_queries * a.group;
     const int item = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (item >= a.num_seqs * a.num_kv_heads * cols) return;
@@ -177,24 +230,7 @@ void lse_reduce_kernel(const AttnParams a) {
     const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
     if (nparts <= 1) return;
     const size_t prow0 = (size_t)item * a.max_parts;
-    float mmax = -__builtin_inff();
-    for (int p = 0; p < nparts; ++p) mmax = __builtin_fmaxf(mmax, a.ws_ml[2 * (prow0 + p)]);
-    constexpr int PER = D / 64;
-    float o[PER], lsum = 0.f;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = 0.f;
-    for (int p = 0; p < nparts; ++p) {
-        const float mp = a.ws_ml[2 * (prow0 + p)];
-        const float w = (mp == -__builtin_inff()) ? 0.f : fast_exp2(mp - mmax);
-        lsum = __builtin_fmaf(w, a.ws_ml[2 * (prow0 + p) + 1], lsum);
-        const float* acc = a.ws_acc + (prow0 + p) * D;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) o[e] = __builtin_fmaf(w, acc[lane + 64 * e], o[e]);
-    }
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;   // 0: a query before the start
-    const size_t orow = out_row(a, seq, g, n);
-#pragma unroll
-    for (int e = 0; e < PER; ++e) store_out(a.out, a.out_dtype, orow * D + lane + 64 * e, o[e] * inv);
+    fold_records<D>(a, nparts, [&](int p) { return prow0 + p; }, out_row(a, seq, g, n));
 }
 
 // ---------------------------------------------------------------------------
@@ -329,15 +365,10 @@ void paged_decode_balanced_kernel(const AttnParams a) {
 // segment that ends in wave w's run, if any (ws_info[2w] = seq * Hkv + g,
 // ws_info[2w + 1] = wf, the first wave holding a piece). Wave wf wrote
 // record 2 wf + 1, waves wf+1 .. w record 2 v; a record holds one row per
-// column. The records are folded in order with the log-sum-exp rule,
-// keeping a running max:
-//   M' = max(M, m_r),  o' = o e^(M - M') + acc_r e^(m_r - M'),
-//   l' = l e^(M - M') + l_r e^(m_r - M'),  out = o / l  (base-2 exponentials).
-// Lane l owns dims l, l + 64, ...; several records are in flight at once.
+// column. The records are folded with the log-sum-exp rule (fold_records).
 template <int D>
 __global__ __launch_bounds__(64 * kWaves)
 void balanced_reduce_kernel(const AttnParams a) {
-    const int lane = threadIdx.x & 63;
     const int cols = a.num_queries * a.group;
     const int item = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (item >= a.num_items * cols) return;
@@ -345,27 +376,9 @@ void balanced_reduce_kernel(const AttnParams a) {
     const int seg = a.ws_info[2 * w];
     if (seg < 0) return;
     const int wf = a.ws_info[2 * w + 1];
-    constexpr int PER = D / 64;
-    float mrun = -__builtin_inff(), lsum = 0.f, o[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] = 0.f;
-#pragma unroll 8
-    for (int v = wf; v <= w; ++v) {
-        const size_t row = (2 * (size_t)v + (v == wf ? 1 : 0)) * cols + n;
-        const float mr = a.ws_ml[2 * row];
-        const float mnew = __builtin_fmaxf(mrun, mr);
-        const float keep = (mrun == -__builtin_inff()) ? 0.f : fast_exp2(mrun - mnew);
-        const float take = (mr == -__builtin_inff()) ? 0.f : fast_exp2(mr - mnew);
-        lsum = __builtin_fmaf(take, a.ws_ml[2 * row + 1], lsum * keep);
-#pragma unroll
-        for (int k = 0; k < PER; ++k)
-            o[k] = __builtin_fmaf(take, a.ws_acc[row * D + lane + 64 * k], o[k] * keep);
-        mrun = mnew;
-    }
-    const size_t orow = out_row(a, seg / a.num_kv_heads, seg % a.num_kv_heads, n);
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;   // 0: a query before the start
-#pragma unroll
-    for (int k = 0; k < PER; ++k) store_out(a.out, a.out_dtype, orow * D + lane + 64 * k, o[k] * inv);
+    fold_records<D>(a, w - wf + 1,
+                    [&](int r) { return (2 * (size_t)(wf + r) + (r == 0 ? 1 : 0)) * cols + n; },
+                    out_row(a, seg / a.num_kv_heads, seg % a.num_kv_heads, n));
 }
 
 // Waves of a balanced kernel instance that fit on one compute unit at once
