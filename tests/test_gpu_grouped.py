@@ -108,14 +108,17 @@ def test_grouped_query_heads(group, group_size):
     assert err <= 2e-3, f"max abs error {err:.3e}"
 
 
+@pytest.mark.parametrize("partition,kv_reuse", [(1024, False), (512, True)])
 @pytest.mark.parametrize("name", ["shared_prefix_fp16", "shared_prefix_cow_fp16"])
-def test_full_size_matches_oracle(name):
-    """The 32 x 8 sampling workloads in the timed configuration (512-token
-    partitions, cached loads)."""
+def test_full_size_matches_oracle(name, partition, kv_reuse):
+    """The 32 x 8 sampling workloads in the timed configuration (1024-token
+    partitions, streaming loads) and with 512-token partitions and cached
+    loads."""
     w = wl.make(name)
     d = Device(w)
     d.copy_and_append()
-    out = grouped(d, w.info["samples"], wl.shared_tokens(w, w.info["samples"]), 512)
+    out = grouped(d, w.info["samples"], wl.shared_tokens(w, w.info["samples"]), partition,
+                  kv_reuse=kv_reuse)
     kb, vb = expected_pools(w)
     assert np.array_equal(bits(d.k_pool), kb) and np.array_equal(bits(d.v_pool), vb)
     del d
