@@ -137,6 +137,25 @@ PKV_API int pkv_copy_blocks(void* k_pool, void* v_pool,
 #define PKV_KV_REUSE 1
 
 /*
+ * Launch stages, OR-ed into kv_policy of any attention entry point. Under a
+ * split schedule (fixed partitions or PKV_PARTITION_BALANCED) a call is two
+ * launches: the walk over the K/V blocks, which writes the rows of segments
+ * it finishes and leaves partial results of split segments in the
+ * workspace, and the log-sum-exp merge of those partial results, which
+ * writes the remaining rows. By default one call enqueues both.
+ *   PKV_STAGE_WALK   enqueue only the walk;
+ *   PKV_STAGE_MERGE  enqueue only the merge. Call it after a PKV_STAGE_WALK
+ *                    call with the same arguments and the same workspace,
+ *                    untouched in between, on the same stream; out is
+ *                    complete after it. Under a single pass there is
+ *                    nothing to merge and it enqueues nothing.
+ * Setting both is PKV_ERR_INVALID. For callers that place other work, or
+ * timing events, between the two launches; results are identical bits.
+ */
+#define PKV_STAGE_WALK 0x10
+#define PKV_STAGE_MERGE 0x20
+
+/*
  * Bytes of workspace pkv_paged_attention_decode needs for the given sizes and
  * partition_size (0 when it needs none: partition_size == 0, or every
  * sequence fits one partition). Returns 0 for invalid sizes as well. For
@@ -178,8 +197,10 @@ PKV_API size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, i
  *                           (parallel sampling) are read once from HBM and
  *                           then from cache;
  *   PKV_PARTITION_BALANCED  a fixed set of persistent waves (4 or 8 per
- *                           compute unit, depending on the kernel; at most
- *                           4096) each takes an equal share of
+ *                           compute unit, depending on the kernel, or as
+ *                           many as fit when the (sequence, kv head) pairs
+ *                           outnumber twice that; at most 4096) each takes
+ *                           an equal share of
  *                           all tokens of the batch, whatever the lengths;
  *                           pieces of a sequence split between waves are
  *                           merged by a log-sum-exp reduce. The split points
@@ -190,8 +211,11 @@ PKV_API size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, i
  * overwritten) holds the partial results. Work enqueued on `stream` by
  * different calls must not share a workspace unless ordered by the stream.
  *
- * kv_policy is PKV_KV_STREAM or PKV_KV_REUSE (see above; PKV_ERR_INVALID
- * otherwise).
+ * A PKV_STAGE_MERGE call is the exception: it reads the workspace its
+ * PKV_STAGE_WALK call left.
+ *
+ * kv_policy is PKV_KV_STREAM or PKV_KV_REUSE, optionally with one stage
+ * flag (see above; PKV_ERR_INVALID otherwise).
  */
 PKV_API int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype,
                                const void* q,

@@ -190,10 +190,13 @@ def swap_blocks(src_k, src_v, dst_k, dst_v, block_mapping, stream=None) -> None:
 
 PARTITION_BALANCED = -1     # PKV_PARTITION_BALANCED
 KV_STREAM, KV_REUSE = 0, 1  # PKV_KV_STREAM, PKV_KV_REUSE
+STAGES = {"both": 0, "walk": 0x10, "merge": 0x20}   # PKV_STAGE_WALK, PKV_STAGE_MERGE
 
 
-def _policy(kv_reuse: bool) -> int:
-    return KV_REUSE if kv_reuse else KV_STREAM
+def _policy(kv_reuse: bool, stage: str = "both") -> int:
+    if stage not in STAGES:
+        raise ValueError(f"stage must be one of {sorted(STAGES)}")
+    return (KV_REUSE if kv_reuse else KV_STREAM) | STAGES[stage]
 
 
 def kv_cache_append_fp8(k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens,
@@ -229,13 +232,18 @@ def paged_attention_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, 
 
 def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len, scale,
                            partition_size=PARTITION_BALANCED, workspace=None,
-                           stream=None, kv_reuse: bool = False) -> torch.Tensor:
+                           stream=None, kv_reuse: bool = False,
+                           stage: str = "both") -> torch.Tensor:
     """pkv_paged_attention_decode into `out` [B][H][D] (float32, float16 or
     bfloat16). partition_size: 0 (one pass per sequence), a multiple of 64
     (fixed partitions) or PARTITION_BALANCED (the default). `workspace` (a
     uint8 device tensor) is allocated here when the call needs one and none
     is given. kv_reuse: the batch's sequences share blocks (PKV_KV_REUSE:
-    cached K/V loads); by default K/V stream through (PKV_KV_STREAM)."""
+    cached K/V loads); by default K/V stream through (PKV_KV_STREAM).
+    stage: "both" (default), "walk" (only the walk over the blocks; partial
+    results stay in `workspace`) or "merge" (only the merge, after a "walk"
+    call with the same arguments and workspace): PKV_STAGE_WALK /
+    PKV_STAGE_MERGE."""
     nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
     if code == FP8_E4M3:
         raise TypeError("uint8 (FP8) pools are read by paged_attention_decode_fp8")
@@ -256,7 +264,7 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, max_s
         _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32),
         block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len),
         b, h, hkv, d, bs, nb, float(scale), int(partition_size), ws_ptr, ws_bytes, code,
-        _policy(kv_reuse), _stream(stream)))
+        _policy(kv_reuse, stage), _stream(stream)))
     return out
 
 
@@ -291,11 +299,12 @@ def probe_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
 def paged_attention_decode_grouped(out, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len,
                                    scale, group_size, shared_tokens, partition_size=512,
                                    workspace=None, stream=None,
-                                   kv_reuse: bool = False) -> torch.Tensor:
+                                   kv_reuse: bool = False, stage: str = "both") -> torch.Tensor:
     """pkv_paged_attention_decode_grouped into `out` [B][H][D]: sequences
     k*group_size .. (k+1)*group_size - 1 share the blocks of their first
     shared_tokens[k] tokens (int32 device tensor [B / group_size]); shared
-    partitions are read once per group."""
+    partitions are read once per group. kv_reuse and stage as for
+    paged_attention_decode."""
     nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
     if code == FP8_E4M3:
         raise TypeError("FP8 pools are not supported by paged_attention_decode_grouped")
@@ -321,16 +330,17 @@ def paged_attention_decode_grouped(out, q, k_pool, v_pool, block_tables, seq_len
         block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len),
         b, h, hkv, d, bs, nb, float(scale), int(partition_size), int(group_size),
         _dev(shared_tokens, "shared_tokens", torch.int32), ws_ptr, ws_bytes, code,
-        _policy(kv_reuse), _stream(stream)))
+        _policy(kv_reuse, stage), _stream(stream)))
     return out
 
 
 def paged_attention_decode_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens,
                                max_seq_len, scale, partition_size=PARTITION_BALANCED,
-                               workspace=None, stream=None, kv_reuse: bool = False) -> torch.Tensor:
+                               workspace=None, stream=None, kv_reuse: bool = False,
+                               stage: str = "both") -> torch.Tensor:
     """pkv_paged_attention_decode_fp8 into `out` [B][H][D] over uint8 E4M3
     pools with per-head float32 scales; q is float32, float16 or bfloat16.
-    kv_reuse as for paged_attention_decode."""
+    kv_reuse and stage as for paged_attention_decode."""
     nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
     if code != FP8_E4M3:
         raise TypeError("paged_attention_decode_fp8 needs uint8 (FP8) pools")
@@ -352,7 +362,7 @@ def paged_attention_decode_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block
         _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), ks, vs,
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), b, h, hkv, d, bs, nb,
-        float(scale), int(partition_size), ws_ptr, ws_bytes, _policy(kv_reuse), _stream(stream)))
+        float(scale), int(partition_size), ws_ptr, ws_bytes, _policy(kv_reuse, stage), _stream(stream)))
     return out
 
 
@@ -380,10 +390,10 @@ def kv_cache_append_multi(k_new, v_new, k_pool, v_pool, block_tables, seq_lens,
 
 def paged_attention_multi(out, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len, scale,
                           partition_size=PARTITION_BALANCED, workspace=None,
-                          stream=None, kv_reuse: bool = False) -> torch.Tensor:
+                          stream=None, kv_reuse: bool = False, stage: str = "both") -> torch.Tensor:
     """pkv_paged_attention_multi into `out` [B][nq][H][D]: new token j of
     sequence i (position seq_lens[i] - nq + j) attends causally to the cache.
-    kv_reuse as for paged_attention_decode."""
+    kv_reuse and stage as for paged_attention_decode."""
     nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
     if code == FP8_E4M3:
         raise TypeError("FP8 pools are not supported by paged_attention_multi")
@@ -404,5 +414,5 @@ def paged_attention_multi(out, q, k_pool, v_pool, block_tables, seq_lens, max_se
         _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32),
         block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len),
         b, nq, h, hkv, d, bs, nb, float(scale), int(partition_size), ws_ptr, ws_bytes, code,
-        _policy(kv_reuse), _stream(stream)))
+        _policy(kv_reuse, stage), _stream(stream)))
     return out

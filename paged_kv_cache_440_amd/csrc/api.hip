@@ -102,7 +102,12 @@ int prepare_attention(pkv::AttnParams& a, void* out, int out_dtype, const void* 
                       int block_size, int num_blocks, float scale, int partition_size,
                       void* workspace, size_t workspace_bytes, int kv_policy,
                       int num_queries = 1) {
+    const int stage_bits = kv_policy & (PKV_STAGE_WALK | PKV_STAGE_MERGE);
+    kv_policy &= ~(PKV_STAGE_WALK | PKV_STAGE_MERGE);
+    if (stage_bits == (PKV_STAGE_WALK | PKV_STAGE_MERGE)) return PKV_ERR_INVALID;
     if (kv_policy != PKV_KV_STREAM && kv_policy != PKV_KV_REUSE) return PKV_ERR_INVALID;
+    a.stage = stage_bits == PKV_STAGE_WALK ? pkv::kStageWalk
+            : stage_bits == PKV_STAGE_MERGE ? pkv::kStageMerge : pkv::kStageBoth;
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0 ||
         partition_size < PKV_PARTITION_BALANCED || !valid_dtype(out_dtype) || !isfinite(scale))

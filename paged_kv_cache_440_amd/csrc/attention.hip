@@ -420,10 +420,12 @@ hipError_t launch_balanced(const AttnParams& a_in, hipStream_t stream) {
     const long long w = (long long)a.num_items * per_cu;
     a.num_items = (int)(w < kMaxBalancedWaves ? w : kMaxBalancedWaves);
     const int cols = a.num_queries * G;
-    hipLaunchKernelGGL((paged_decode_balanced_kernel<Walker>),
-                       dim3((a.num_items + kWaves - 1) / kWaves), dim3(64 * kWaves), 0, stream, a);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (stage_walks(a.stage)) {
+        hipLaunchKernelGGL((paged_decode_balanced_kernel<Walker>),
+                           dim3((a.num_items + kWaves - 1) / kWaves), dim3(64 * kWaves), 0, stream, a);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess || !stage_merges(a.stage)) return err;
+    }
     hipLaunchKernelGGL((balanced_reduce_kernel<D>), dim3((a.num_items * cols + kWaves - 1) / kWaves),
                        dim3(64 * kWaves), 0, stream, a);
     return hipGetLastError();
@@ -434,10 +436,13 @@ template <class Walker>
 hipError_t launch_partitioned(const AttnParams& a, hipStream_t stream) {
     constexpr int D = Walker::D, G = Walker::G;
     const int cols = a.num_queries * G;
-    hipLaunchKernelGGL((paged_decode_kernel<Walker>), dim3((a.num_items + kWaves - 1) / kWaves),
-                       dim3(64 * kWaves), 0, stream, a);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess || a.max_parts <= 1) return err;
+    if (stage_walks(a.stage)) {
+        hipLaunchKernelGGL((paged_decode_kernel<Walker>), dim3((a.num_items + kWaves - 1) / kWaves),
+                           dim3(64 * kWaves), 0, stream, a);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    if (a.max_parts <= 1 || !stage_merges(a.stage)) return hipSuccess;
     hipLaunchKernelGGL((lse_reduce_kernel<D>),
                        dim3((a.num_seqs * a.num_kv_heads * cols + kWaves - 1) / kWaves),
                        dim3(64 * kWaves), 0, stream, a);
@@ -471,12 +476,14 @@ hipError_t launch_grouped_typed(const AttnParams& a, hipStream_t stream) {
         (long long)(a.num_seqs / a.group_size) * a.num_kv_heads * a.max_parts;
     const long long total = group_items + a.num_items;
     if (total > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((paged_decode_grouped_kernel<MfmaWalker<S, G, STREAM>,
-                                                    DecodeWalker<S, 128, G, STREAM>>),
-                       dim3((unsigned)((total + kWaves - 1) / kWaves)), dim3(64 * kWaves), 0,
-                       stream, a, (int)group_items);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (stage_walks(a.stage)) {
+        hipLaunchKernelGGL((paged_decode_grouped_kernel<MfmaWalker<S, G, STREAM>,
+                                                        DecodeWalker<S, 128, G, STREAM>>),
+                           dim3((unsigned)((total + kWaves - 1) / kWaves)), dim3(64 * kWaves), 0,
+                           stream, a, (int)group_items);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess || !stage_merges(a.stage)) return err;
+    }
     hipLaunchKernelGGL((lse_reduce_kernel<128>),
                        dim3((a.num_seqs * a.num_kv_heads * G + kWaves - 1) / kWaves),
                        dim3(64 * kWaves), 0, stream, a);

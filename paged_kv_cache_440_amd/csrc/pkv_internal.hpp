@@ -40,6 +40,7 @@ struct AttnParams {
                                    // launcher, the persistent wave count in the kernels
     int balanced;                  // 1: balanced schedule (see attention.hip)
     int kv_stream;                 // 1: non-temporal K/V loads (PKV_KV_STREAM), 0: cached
+    int stage;                     // host side: kStageBoth, kStageWalk or kStageMerge
     // sampling groups (pkv_paged_attention_decode_grouped): sequences
     // k*group_size .. (k+1)*group_size - 1 share their first shared_tokens[k]
     // tokens' blocks; shared_tokens is null for every other call
@@ -54,6 +55,11 @@ struct AttnParams {
     const float* v_scales;
     int q_dtype;
 };
+
+// Launches a split attention call enqueues (PKV_STAGE_WALK / PKV_STAGE_MERGE).
+constexpr int kStageBoth = 0, kStageWalk = 1, kStageMerge = 2;
+__host__ __device__ inline bool stage_walks(int stage) { return stage != kStageMerge; }
+__host__ __device__ inline bool stage_merges(int stage) { return stage != kStageWalk; }
 
 // Persistent waves of the balanced schedule: each walker's
 // kBalancedWavesPerCU per compute unit (fewer if fewer fit), at most

@@ -102,6 +102,11 @@ def attn(lib, **kw):
     (dict(policy=-1), INVALID),
     (dict(B=0), OK),                        # nothing to do, nothing enqueued
     (dict(B=0, policy=1), OK),
+    (dict(B=0, policy=0x10), OK),           # PKV_STAGE_WALK
+    (dict(B=0, policy=0x21), OK),           # PKV_STAGE_MERGE with PKV_KV_REUSE
+    (dict(policy=0x30), INVALID),           # both stages
+    (dict(policy=0x12), INVALID),           # a stage with an unknown policy
+    (dict(policy=0x40), INVALID),           # an unknown flag
 ])
 def test_attention_validation(lib, kw, status):
     assert attn(lib, **kw) == status

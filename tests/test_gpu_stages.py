@@ -1,0 +1,110 @@
+"""The two launches of a split attention call, enqueued separately
+(PKV_STAGE_WALK, then PKV_STAGE_MERGE), give the bits of the one-call form,
+for every attention entry point and schedule. The workspace between the two
+calls is the caller's: here a fresh, poisoned one for the split form."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_440_amd as pkv
+from paged_kv_cache_440_amd import workloads as wl
+from paged_kv_cache_440_amd._lib import PARTITION_BALANCED as BAL
+
+from .gpu_support import Device, bits
+
+pytestmark = pytest.mark.gpu
+
+
+def workspace(w, partition, poison):
+    need = pkv.paged_attention_workspace_size(w.num_seqs, w.num_heads * w.num_queries,
+                                              w.num_kv_heads, w.head_dim, w.max_seq_len,
+                                              partition)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    ws.fill_(poison)
+    return ws
+
+
+def both_and_split(call, w, partition):
+    """call(out, workspace, stage) -> None; returns (one-call, split) outputs."""
+    outs = []
+    for split in (False, True):
+        out = torch.full(tuple(w.q.shape), float("nan"), dtype=torch.float32, device="cuda")
+        ws = workspace(w, partition, 0x7F if split else 0)
+        if split:
+            call(out, ws, "walk")
+            call(out, ws, "merge")
+        else:
+            call(out, ws, "both")
+        outs.append(out)
+    torch.cuda.synchronize()
+    return outs
+
+
+def assert_same_bits(a, b):
+    assert not torch.isnan(a).any()
+    assert np.array_equal(bits(a), bits(b))
+
+
+@pytest.mark.parametrize("partition", [0, 64, 512, BAL])
+@pytest.mark.parametrize("name,make", [
+    ("opt13b_fp16", lambda: wl.opt13b_fp16(num_seqs=8, len_range=(1, 1500))),
+    ("long_gqa_bf16", lambda: wl.long_gqa_bf16(num_seqs=2, len_range=(700, 3000))),
+])
+def test_decode(name, make, partition):
+    w = make()
+    d = Device(w)
+    d.copy_and_append()
+
+    def call(out, ws, stage):
+        pkv.paged_attention_decode(out, d.q, d.k_pool, d.v_pool, d.tables, d.lens, w.max_seq_len,
+                                   w.scale, partition_size=partition, workspace=ws, stage=stage)
+
+    assert_same_bits(*both_and_split(call, w, partition))
+
+
+@pytest.mark.parametrize("partition", [512, BAL])
+@pytest.mark.parametrize("make", [
+    lambda: wl.opt13b_fp8(num_seqs=8, len_range=(1, 1500)),
+    lambda: wl.long_gqa_fp8(num_seqs=2, len_range=(700, 3000)),
+])
+def test_decode_fp8(make, partition):
+    w = make()
+    d = Device(w)
+    d.copy_and_append()
+
+    def call(out, ws, stage):
+        pkv.paged_attention_decode_fp8(out, d.q, d.k_pool, d.v_pool, d.k_scales, d.v_scales,
+                                       d.tables, d.lens, w.max_seq_len, w.scale,
+                                       partition_size=partition, workspace=ws, stage=stage)
+
+    assert_same_bits(*both_and_split(call, w, partition))
+
+
+@pytest.mark.parametrize("partition", [64, BAL])
+def test_multi_query(partition):
+    w = wl.opt13b_spec4_fp16(num_seqs=8, len_range=(1, 1500))
+    d = Device(w)
+    pkv.kv_cache_append_multi(d.k_new, d.v_new, d.k_pool, d.v_pool, d.tables, d.lens)
+
+    def call(out, ws, stage):
+        pkv.paged_attention_multi(out, d.q, d.k_pool, d.v_pool, d.tables, d.lens, w.max_seq_len,
+                                  w.scale, partition_size=partition, workspace=ws, stage=stage)
+
+    assert_same_bits(*both_and_split(call, w, partition))
+
+
+@pytest.mark.parametrize("partition", [64, 512])
+def test_grouped(partition):
+    w = wl.shared_prefix_cow_fp16(num_prompts=2, samples=4, max_divergent=40, num_heads=8)
+    d = Device(w)
+    d.copy_and_append()
+    samples = w.info["samples"]
+    shared = torch.from_numpy(np.asarray(wl.shared_tokens(w, samples), np.int32)).cuda()
+
+    def call(out, ws, stage):
+        pkv.paged_attention_decode_grouped(out, d.q, d.k_pool, d.v_pool, d.tables, d.lens,
+                                           w.max_seq_len, w.scale, samples, shared,
+                                           partition_size=partition, workspace=ws, stage=stage)
+
+    assert_same_bits(*both_and_split(call, w, partition))
