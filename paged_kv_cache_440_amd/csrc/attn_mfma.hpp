@@ -235,11 +235,14 @@ struct MfmaWalker {
         return p < (uint32_t)max_phys ? p : (uint32_t)(max_phys - 1);
     }
 
-    // K: kt[t][s] = row (c0 + 16t + n), bytes 64s + 16q .. +15.
+    // K: kt[t][s] = row (c0 + 16t + n), bytes 64s + 16q .. +15. Rows at or
+    // past the range end (masked by softmax_pv) re-read the range's last row,
+    // which is in cache, instead of fetching unrelated blocks from HBM.
     __device__ __forceinline__ void load_k(int c0, u32x4 (&kt)[2][4]) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int tok = c0 + 16 * t + n;
+            int tok = c0 + 16 * t + n;
+            tok = tok < t_end ? tok : t_end - 1;
             const char* p = kbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes +
                             kvhead_off + (uint32_t)((tok & bs_mask) * ROW + 16 * q);
 #pragma unroll
@@ -248,15 +251,23 @@ struct MfmaWalker {
     }
 
     // V: vt[4h + j] = row (c0 + 16h + 4q + j), bytes 16n .. 16n+15. Four
-    // aligned consecutive tokens never straddle a block (bs >= 8).
+    // aligned consecutive tokens never straddle a block (bs >= 8). Rows at or
+    // past the range end (zeroed by softmax_pv) re-read the range's last row,
+    // which lies in the same block as the first of the four rows once that
+    // one is clamped too.
     __device__ __forceinline__ void load_v(int c0, u32x4 (&vt)[8]) {
+        const int last = t_end - 1;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int tok = c0 + 16 * h + 4 * q;
-            const char* p = vbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes +
-                            kvhead_off + (uint32_t)((tok & bs_mask) * ROW + 16 * n);
+            const int tb = c0 + 16 * h + 4 * q;
+            const int t0 = tb < last ? tb : last;
+            const char* p = vbase + (size_t)phys((t0 >> log2_bs) - wb) * head_stride_bytes +
+                            kvhead_off + (uint32_t)(16 * n);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vt[4 * h + j] = load16_kv<STREAM>(p + ROW * j);
+            for (int j = 0; j < 4; ++j) {
+                const int tj = tb + j < last ? tb + j : last;
+                vt[4 * h + j] = load16_kv<STREAM>(p + (uint32_t)((tj & bs_mask) * ROW));
+            }
         }
     }
 
