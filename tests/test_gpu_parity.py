@@ -305,6 +305,29 @@ def test_balanced_runs_cross_many_segments():
     assert (out.cpu()[np.asarray(lens) == 0] == 0).all()
 
 
+@pytest.mark.parametrize("num_seqs", [512, 513, 1300])
+def test_balanced_batches_beyond_one_length_block(num_seqs):
+    """Balanced schedule over batches that fill one block of 512 lengths
+    exactly, spill one sequence past it, and span three blocks, with empty
+    rows inside and at the block edges: every wave finds its first sequence
+    in the right block and place."""
+    rng = np.random.default_rng(num_seqs)
+    lens = rng.integers(1, 70, size=num_seqs)
+    lens[rng.choice(num_seqs, size=num_seqs // 10, replace=False)] = 0
+    lens[[511, num_seqs - 1]] = 0
+    if num_seqs > 512:
+        lens[512] = 0
+    lens = lens.tolist()
+    w = wl.build_independent("many", lens, dtype=torch.float16, num_heads=2, num_kv_heads=2,
+                             head_dim=64, block_size=16, dist="normal", seed=14)
+    poison_unwritten_slots(w)
+    d = Device(w)
+    d.copy_and_append()
+    out = d.attention(partition_size=BAL)
+    assert max_err(out, expected_attention(w, *expected_pools(w))) <= TOL[w.dtype]
+    assert (out.cpu()[np.asarray(lens) == 0] == 0).all()
+
+
 def test_balanced_one_segment_over_many_waves():
     """One long sequence and one kv head: the segment is cut into one run per
     wave (32 tokens each) and merged from about a thousand records."""
