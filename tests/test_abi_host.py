@@ -341,3 +341,12 @@ def attn_grouped(lib, **kw):
 ])
 def test_attention_grouped_validation(lib, kw, status):
     assert attn_grouped(lib, **kw) == status
+
+
+def test_stage_keyword_maps_to_the_flags():
+    """The bindings' stage keyword ORs PKV_STAGE_WALK / PKV_STAGE_MERGE into
+    kv_policy and refuses anything else before reaching the library."""
+    assert _lib._policy(False) == 0 and _lib._policy(True) == 1
+    assert _lib._policy(False, "walk") == 0x10 and _lib._policy(True, "merge") == 0x21
+    with pytest.raises(ValueError):
+        _lib._policy(False, "reduce")
