@@ -328,6 +328,33 @@ def test_balanced_batches_beyond_one_length_block(num_seqs):
     assert (out.cpu()[np.asarray(lens) == 0] == 0).all()
 
 
+@pytest.mark.parametrize("partition", [0, 64, 512, BAL])
+@pytest.mark.parametrize("dtype,group,fp8", [
+    (torch.float16, 1, False),       # vector walker
+    (torch.bfloat16, 8, False),      # matrix-core walker
+    (torch.float32, 2, False),       # vector walker, fp32
+    (torch.float16, 1, True),        # FP8 vector walker
+    (torch.bfloat16, 4, True),       # FP8 matrix-core walker
+])
+def test_largest_block_size(dtype, group, fp8, partition):
+    """256-token blocks, the largest the library takes: lengths on and
+    around block edges, and one sequence past a 64-block table window
+    (16,384 tokens), under every schedule."""
+    lens = [1, 255, 256, 257, 0, 700, 16384 + 300, 40]
+    w = wl.build_independent("bs256", lens, dtype=dtype, num_heads=2 * group, num_kv_heads=2,
+                             head_dim=128, block_size=256, dist="normal", seed=15,
+                             fp8_spread=8.0 if fp8 else None)
+    poison_unwritten_slots(w)
+    d = Device(w)
+    d.copy_and_append()
+    out = d.attention(partition_size=partition)
+    kb, vb = expected_pools(w)
+    assert np.array_equal(bits(d.k_pool), kb) and np.array_equal(bits(d.v_pool), vb)
+    tol_w = 2e-3 if fp8 else TOL[w.dtype]
+    assert max_err(out, expected_attention(w, kb, vb)) <= tol_w
+    assert (out.cpu()[np.asarray(lens) == 0] == 0).all()
+
+
 def test_balanced_one_segment_over_many_waves():
     """One long sequence and one kv head: the segment is cut into one run per
     wave (32 tokens each) and merged from about a thousand records."""
