@@ -10,7 +10,9 @@ one of them (tests/test_oracle_mutants.py plants such mistakes and checks):
     huge score gap returns the arg-max value;
   * invariants of paging: relabelling physical blocks, a contiguous table,
     another block size, or aliased (shared) blocks leave the result identical;
-  * 50-digit mpmath evaluation on tiny inputs.
+  * 50-digit mpmath evaluation on tiny inputs;
+  * block moves between two pools of different sizes (swapping) checked
+    against blocks whose every element spells out its own block id.
 """
 
 import json
@@ -23,7 +25,8 @@ import pytest
 import torch
 
 from oracle import (block_and_slot, dense_decode_attention, gather_sequence,
-                    paged_decode_attention, pool_after_append, pool_after_copy)
+                    paged_decode_attention, pool_after_append, pool_after_copy,
+                    pool_after_swap)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -374,3 +377,35 @@ def test_copy_applies_pairs_in_order_and_touches_only_destinations():
         assert np.array_equal(k2[b], k[b]) and np.array_equal(v2[b], v[b])
     k3, v3 = pool_after_copy(k, v, np.zeros((0, 2), dtype=np.int32))
     assert np.array_equal(k3, k) and np.array_equal(v3, v)
+
+
+def _tagged_pool(num_blocks, hkv, bs, d, base):
+    """int32 pool whose element [b][g][s][e] is base + 10000 b + 1000 g + 10 s + e
+    (e < 10): every element names its block, head, slot and position."""
+    b, g, s, e = np.meshgrid(np.arange(num_blocks), np.arange(hkv), np.arange(bs), np.arange(d),
+                             indexing="ij")
+    return (base + 10000 * b + 1000 * g + 10 * s + e).astype(np.int32)
+
+
+def test_swap_moves_tagged_blocks_between_pools_of_different_sizes():
+    # supersilo.blog summary, "적용 범위와 관련 연구": preempted sequences move to
+    # CPU memory and back, i.e. whole blocks go from one pool to another
+    hkv, bs, d = 3, 4, 6
+    src_k, src_v = _tagged_pool(7, hkv, bs, d, 0), _tagged_pool(7, hkv, bs, d, -500000)
+    dst_k, dst_v = _tagged_pool(11, hkv, bs, d, 900000), _tagged_pool(11, hkv, bs, d, 700000)
+    saved = [x.copy() for x in (src_k, src_v, dst_k, dst_v)]
+    pairs = [(5, 0), (2, 9), (6, 3), (0, 10)]          # (block of src, block of dst)
+    k2, v2 = pool_after_swap(src_k, src_v, dst_k, dst_v, pairs)
+    g, s, e = np.meshgrid(np.arange(hkv), np.arange(bs), np.arange(d), indexing="ij")
+    for sb, db in pairs:
+        # the destination block now spells the source block's id, in K and in V
+        assert np.array_equal(k2[db], 10000 * sb + 1000 * g + 10 * s + e)
+        assert np.array_equal(v2[db], -500000 + 10000 * sb + 1000 * g + 10 * s + e)
+    for db in set(range(11)) - {d_ for _, d_ in pairs}:
+        assert np.array_equal(k2[db], saved[2][db]) and np.array_equal(v2[db], saved[3][db])
+    # inputs are untouched (the result is a copy), sources included
+    for x, y in zip((src_k, src_v, dst_k, dst_v), saved):
+        assert np.array_equal(x, y)
+    # no pairs: the destination comes back unchanged
+    k3, v3 = pool_after_swap(src_k, src_v, dst_k, dst_v, np.zeros((0, 2), dtype=np.int32))
+    assert np.array_equal(k3, dst_k) and np.array_equal(v3, dst_v)

@@ -6,7 +6,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import fp8_decode, fp8_encode, fp8_quantize, pool_after_append_fp8
+from oracle import (fp8_decode, fp8_dequantize_pool, fp8_encode, fp8_quantize,
+                    pool_after_append_fp8)
 from oracle.fp8 import _encode_one
 
 ALL = np.arange(256, dtype=np.uint8)
@@ -108,3 +109,24 @@ def test_append_fp8_writes_only_the_new_slots():
     for g in range(hkv):
         assert np.array_equal(k2[3, g, 4], torch_encode(kn[0, g] / ks[g]))
         assert np.array_equal(v2[2, g, 15], torch_encode(vn[1, g] / vs[g]))
+
+
+def test_dequantize_pool_scales_each_head_by_its_own_factor():
+    # A pool of codes read back as values: code value (torch's own
+    # float8_e4m3fn conversion) times the scale of the code's kv head. The
+    # pool is 4 x 4 x 4 x 16 so that a scale applied along the block or slot
+    # axis still broadcasts and has to be caught by its values; the scales are
+    # distinct powers of two, so every product is exact.
+    rng = np.random.default_rng(31)
+    codes = rng.integers(0, 256, size=(4, 4, 4, 16)).astype(np.uint8)
+    codes[codes & 0x7F == 0x7F] = 0x38                       # no NaN codes here
+    codes[1, :, 2, 5] = 0x38                                 # 1.0 in every head
+    scales = np.array([2.0 ** -3, 2.0 ** 1, 2.0 ** 5, 2.0 ** -7], dtype=np.float32)
+    got = fp8_dequantize_pool(codes, scales)
+    ref = torch_decode(codes)
+    for g in range(4):
+        assert np.array_equal(got[:, g], ref[:, g] * float(scales[g]))
+        assert got[1, g, 2, 5] == float(scales[g])
+    # the NaN code stays NaN, whatever the head's scale
+    nan_pool = np.full((1, 4, 1, 2), 0x7F, dtype=np.uint8)
+    assert np.isnan(fp8_dequantize_pool(nan_pool, scales)).all()

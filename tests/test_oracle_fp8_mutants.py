@@ -48,12 +48,26 @@ def _encode_variant(tie_to_upper=False, saturate=True, keep_sign=True):
     return encode
 
 
+def _dequant_scale_axis(axis=1, head0=False):
+    def dequantize_pool(pool, scales):
+        sc = np.asarray(scales, dtype=np.float64)
+        if head0:
+            sc = np.full_like(sc, sc[0])
+        shape = [1, 1, 1, 1]
+        shape[axis] = -1
+        return f8.decode(pool) * sc.reshape(shape)
+    return dequantize_pool
+
+
 MUTANTS = {
     "exponent_bias_8": {"fp8_decode": _decode_with(_value_with(bias=8))},
     "subnormal_scale_2^-7": {"fp8_decode": _decode_with(_value_with(sub_exp=-7))},
     "ties_to_upper": {"fp8_encode": _encode_variant(tie_to_upper=True)},
     "overflow_to_nan": {"fp8_encode": _encode_variant(saturate=False)},
     "sign_dropped": {"fp8_encode": _encode_variant(keep_sign=False)},
+    "dequant_head0_scale_everywhere": {"fp8_dequantize_pool": _dequant_scale_axis(head0=True)},
+    "dequant_scale_on_block_axis": {"fp8_dequantize_pool": _dequant_scale_axis(axis=0)},
+    "dequant_scale_on_slot_axis": {"fp8_dequantize_pool": _dequant_scale_axis(axis=2)},
 }
 
 

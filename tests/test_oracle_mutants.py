@@ -67,6 +67,29 @@ def _copy_backwards(k_pool, v_pool, pairs):
                                     [(d, s) for s, d in np.asarray(pairs).reshape(-1, 2)])
 
 
+def _swap_pairs_reversed(src_k, src_v, dst_k, dst_v, pairs):
+    k_out, v_out = dst_k.copy(), dst_v.copy()
+    for s, d in np.asarray(pairs).reshape(-1, 2):
+        k_out[int(s)] = src_k[int(d)]
+        v_out[int(s)] = src_v[int(d)]
+    return k_out, v_out
+
+
+def _swap_k_and_v_crossed(src_k, src_v, dst_k, dst_v, pairs):
+    k_out, v_out = dst_k.copy(), dst_v.copy()
+    for s, d in np.asarray(pairs).reshape(-1, 2):
+        k_out[int(d)] = src_v[int(s)]
+        v_out[int(d)] = src_k[int(s)]
+    return k_out, v_out
+
+
+def _swap_in_place(src_k, src_v, dst_k, dst_v, pairs):
+    for s, d in np.asarray(pairs).reshape(-1, 2):
+        dst_k[int(d)] = src_k[int(s)]
+        dst_v[int(d)] = src_v[int(s)]
+    return dst_k, dst_v
+
+
 _ORIG = {name: getattr(pa, name) for name in
          ("dense_decode_attention", "paged_decode_attention", "block_and_slot",
           "pool_after_append", "pool_after_copy")}
@@ -83,6 +106,9 @@ MUTANTS = {
     "slot_reversed": ("block_and_slot", _slot_reversed),
     "append_one_late": ("pool_after_append", _append_one_late),
     "copy_backwards": ("pool_after_copy", _copy_backwards),
+    "swap_pairs_reversed": ("pool_after_swap", _swap_pairs_reversed),
+    "swap_k_and_v_crossed": ("pool_after_swap", _swap_k_and_v_crossed),
+    "swap_writes_its_input": ("pool_after_swap", _swap_in_place),
 }
 
 
