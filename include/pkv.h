@@ -46,12 +46,14 @@
  *   [0, num_blocks) is clamped into range by attention (its result is then
  *   meaningless) and skipped by append and copy; a length above
  *   max_blocks_per_seq * block_size (or above max_seq_len, for attention) is
- *   clamped to it.
+ *   clamped to it. Each of these events can be reported through an error
+ *   word (pkv_set_error_word, below).
  * Errors.  Every entry point returns a pkv_status. Host-checkable problems
  *   return a negative status before anything is enqueued; PKV_ERR_HIP means the
  *   HIP runtime rejected a launch. No C++ exception crosses this interface.
- * Threads.  Calls are reentrant. The only global state is a per-device cache
- *   of the compute-unit count, filled on first use and thread-safe.
+ * Threads.  Calls are reentrant. The only global state is per device: a
+ *   cache of the compute-unit count, filled on first use, and the registered
+ *   error word; both are thread-safe.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -342,6 +344,41 @@ PKV_API int pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype,
                                float scale, int partition_size,
                                void* workspace, size_t workspace_bytes, int kv_policy,
                                void* stream);
+
+/*
+ * Error word: reports of device-resident values outside the contract above.
+ * The block table is the paged kernel's extra indirection ([summary] section
+ * "PagedAttention의 설계"; section "커널 비용과 블록 크기" counts the table
+ * lookups as its added cost), so a corrupted entry is a likely failure, and
+ * the kernels' clamps keep it from faulting but not from giving wrong numbers.
+ *
+ * pkv_set_error_word registers, for the CURRENT device, a caller-owned
+ * device int32 (4-byte aligned) into which every later call's kernels on
+ * that device OR these bits:
+ *   PKV_ERRBIT_TABLE   attention met a table entry of a valid logical block
+ *                      (block < ceil(L / block_size)) outside [0, num_blocks);
+ *                      it read a clamped block instead, so that row's output
+ *                      is meaningless
+ *   PKV_ERRBIT_LENGTH  attention met a length below 0 or above max_seq_len
+ *                      and clamped it
+ *   PKV_ERRBIT_APPEND  an append skipped a new token whose logical block is
+ *                      at or past max_blocks_per_seq or whose table entry is
+ *                      outside [0, num_blocks)
+ *   PKV_ERRBIT_COPY    a block copy or swap skipped a pair with an id outside
+ *                      its pool
+ * Bits are set with device atomics from the kernels and never cleared by the
+ * library: the caller zeroes the word, runs its calls, synchronises and reads
+ * it. NULL (the default) switches the reports off. Calls already enqueued
+ * keep the word they were enqueued with, so the word must stay allocated
+ * until they finish. Calls on one device share its word. Returns
+ * PKV_ERR_INVALID for a misaligned pointer, PKV_ERR_HIP if there is no
+ * current device.
+ */
+#define PKV_ERRBIT_TABLE 0x1
+#define PKV_ERRBIT_LENGTH 0x2
+#define PKV_ERRBIT_APPEND 0x4
+#define PKV_ERRBIT_COPY 0x8
+PKV_API int pkv_set_error_word(int32_t* error_word);
 
 /* Static, NUL-terminated description of a pkv_status value. */
 PKV_API const char* pkv_status_string(int status);

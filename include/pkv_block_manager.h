@@ -94,7 +94,10 @@ PKV_API int pkv_bm_append_batch(pkv_block_manager* bm, const int64_t* seq_ids, i
 
 /* Drop the sequence: every block's reference count goes down by one, and
  * blocks no longer referenced return to the free stack (the host stack for a
- * swapped-out sequence). */
+ * swapped-out sequence). PKV_ERR_INVALID, and no change, while
+ * copy-on-write pairs are queued (take them first): a block released here
+ * could otherwise be handed out again before those copies run, as a second
+ * copy's destination or as a destination that is still a copy's source. */
 PKV_API int pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id);
 
 /* Swap the resident sequences seq_ids[0..n) (distinct) out to host blocks.

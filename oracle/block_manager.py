@@ -37,6 +37,12 @@ pages give no mechanism; the reading taken here:
   can be freed;
 * copy-on-write copies still queued would be overtaken by the swap's own
   copies, so a swap is refused until they have been taken.
+
+Freeing a sequence is refused while copy-on-write copies are queued (the
+pages say nothing on it): a block it releases could be handed out again
+before the copies run, as the destination of a second copy of the same step
+(two copies writing one block) or as a destination while it is still a
+queued copy's source (the copies of one step run concurrently).
 """
 
 
@@ -93,6 +99,10 @@ class BlockManagerOracle:
         return table[-1], offset
 
     def free_sequence(self, seq):
+        # refused while copy-on-write copies are queued: a freed block could
+        # be handed out again, before the copies run, as the destination of
+        # a second copy or as a destination while still a copy's source
+        assert not self.copies, "queued copy-on-write copies must be taken first"
         ref, free = (self.host_ref, self.host_free) if seq in self.swapped else (self.ref, self.free)
         for b in self.tables.pop(seq):
             ref[b] -= 1

@@ -27,6 +27,11 @@ _API = (
     "KV_STREAM",
     "KV_REUSE",
     "PkvError",
+    "set_error_word",
+    "ERRBIT_TABLE",
+    "ERRBIT_LENGTH",
+    "ERRBIT_APPEND",
+    "ERRBIT_COPY",
 )
 
 __all__ = list(_API)

@@ -65,6 +65,8 @@ def library() -> ctypes.CDLL:
     lib.pkv_paged_attention_decode_grouped.restype = I
     lib.pkv_swap_blocks.argtypes = [P, P, I, P, P, I, P, I, I, I, I, I, P]
     lib.pkv_swap_blocks.restype = I
+    lib.pkv_set_error_word.argtypes = [P]
+    lib.pkv_set_error_word.restype = I
     lib.pkv_status_string.argtypes = [I]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_probe_read.argtypes = [P, Z, P, P]
@@ -84,6 +86,23 @@ def status_string(status: int) -> str:
 def _check(fn: str, status: int) -> None:
     if status != 0:
         raise PkvError(fn, status, status_string(status))
+
+
+ERRBIT_TABLE, ERRBIT_LENGTH, ERRBIT_APPEND, ERRBIT_COPY = 0x1, 0x2, 0x4, 0x8   # PKV_ERRBIT_*
+
+
+def set_error_word(word) -> None:
+    """pkv_set_error_word: `word` (an int32 device tensor of one element, on
+    the current device) receives PKV_ERRBIT_* bits from later calls' kernels
+    when they meet out-of-range table entries, lengths, append targets or copy
+    pairs; None switches the reports off. The caller zeroes and reads it, and
+    keeps it alive while calls that may write it are in flight."""
+    ptr = 0
+    if word is not None:
+        if word.numel() != 1:
+            raise ValueError("the error word is one int32 element")
+        ptr = _dev(word, "error word", torch.int32)
+    _check("pkv_set_error_word", library().pkv_set_error_word(ptr))
 
 
 def _stream(stream) -> int:
@@ -193,6 +212,29 @@ KV_STREAM, KV_REUSE = 0, 1  # PKV_KV_STREAM, PKV_KV_REUSE
 STAGES = {"both": 0, "walk": 0x10, "merge": 0x20}   # PKV_STAGE_WALK, PKV_STAGE_MERGE
 
 
+def _workspace(need: int, workspace, device, stream, stage: str):
+    """The workspace a call uses: the caller's, or a fresh one when the call
+    needs one and none is given. A fresh one is only safe for a call that
+    enqueues both launches: a "walk" call leaves partial results in it for a
+    later "merge" call, so that pair must share a workspace the caller keeps.
+    The fresh buffer is tied to the stream the kernels run on
+    (record_stream), so the caching allocator does not hand its memory to
+    another tensor while they still use it."""
+    if workspace is not None or not need:
+        return workspace
+    if stage != "both":
+        raise ValueError(f"stage={stage!r} needs a caller-owned workspace (the walk leaves its "
+                         "partial results there for the merge); allocate "
+                         "paged_attention_workspace_size(...) bytes and pass the same tensor "
+                         "to both calls")
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if stream is not None:
+        s = stream if isinstance(stream, torch.cuda.Stream) else \
+            torch.cuda.ExternalStream(int(stream), device=device)
+        ws.record_stream(s)
+    return ws
+
+
 def _policy(kv_reuse: bool, stage: str = "both") -> int:
     if stage not in STAGES:
         raise ValueError(f"stage must be one of {sorted(STAGES)}")
@@ -255,8 +297,7 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, max_s
     if block_tables.dim() != 2 or block_tables.shape[0] != b or seq_lens.shape != (b,):
         raise ValueError("block_tables must be [num_seqs][max_blocks], seq_lens [num_seqs]")
     need = paged_attention_workspace_size(b, h, hkv, d, max_seq_len, partition_size)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(need, workspace, q.device, stream, stage)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else 0
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("pkv_paged_attention_decode", library().pkv_paged_attention_decode(
@@ -320,8 +361,7 @@ def paged_attention_decode_grouped(out, q, k_pool, v_pool, block_tables, seq_len
     if block_tables.dim() != 2 or block_tables.shape[0] != b or seq_lens.shape != (b,):
         raise ValueError("block_tables must be [num_seqs][max_blocks], seq_lens [num_seqs]")
     need = paged_attention_workspace_size(b, h, hkv, d, max_seq_len, partition_size)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(need, workspace, q.device, stream, stage)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else 0
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("pkv_paged_attention_decode_grouped", library().pkv_paged_attention_decode_grouped(
@@ -353,8 +393,7 @@ def paged_attention_decode_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block
         raise ValueError("block_tables must be [num_seqs][max_blocks], seq_lens [num_seqs]")
     ks, vs = _scales(k_scales, v_scales, hkv)
     need = paged_attention_workspace_size(b, h, hkv, d, max_seq_len, partition_size)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(need, workspace, q.device, stream, stage)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else 0
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("pkv_paged_attention_decode_fp8", library().pkv_paged_attention_decode_fp8(
@@ -405,8 +444,7 @@ def paged_attention_multi(out, q, k_pool, v_pool, block_tables, seq_lens, max_se
     if block_tables.dim() != 2 or block_tables.shape[0] != b or seq_lens.shape != (b,):
         raise ValueError("block_tables must be [num_seqs][max_blocks], seq_lens [num_seqs]")
     need = paged_attention_workspace_size(b, h * nq, hkv, d, max_seq_len, partition_size)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(need, workspace, q.device, stream, stage)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else 0
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("pkv_paged_attention_multi", library().pkv_paged_attention_multi(

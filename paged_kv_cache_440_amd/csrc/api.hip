@@ -60,6 +60,9 @@ int compute_units() {
     return n;
 }
 
+// The error word registered per device (pkv_set_error_word).
+std::atomic<int*> g_error_word[64];
+
 // The address a kernel on `device` uses for `bytes` bytes at p: p itself for
 // memory of that device, the mapped address for pinned host memory. Pageable
 // host memory, other devices' memory and ranges that run past the end of
@@ -171,10 +174,17 @@ int prepare_attention(pkv::AttnParams& a, void* out, int out_dtype, const void* 
     a.num_items = (int)items;
     a.balanced = balanced ? 1 : 0;
     a.kv_stream = kv_policy == PKV_KV_STREAM ? 1 : 0;
+    a.err = pkv::error_word();
     return PKV_OK;
 }
 
 }  // namespace
+
+int* pkv::error_word() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    return g_error_word[dev].load(std::memory_order_acquire);
+}
 
 extern "C" {
 
@@ -188,6 +198,14 @@ const char* pkv_status_string(int status) {
         case PKV_ERR_NO_BLOCKS: return "no free block in the pool";
         default: return "unknown status";
     }
+}
+
+int pkv_set_error_word(int32_t* error_word) {
+    if ((reinterpret_cast<uintptr_t>(error_word) & 3u) != 0) return PKV_ERR_INVALID;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PKV_ERR_HIP;
+    g_error_word[dev].store(reinterpret_cast<int*>(error_word), std::memory_order_release);
+    return PKV_OK;
 }
 
 int pkv_kv_cache_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
@@ -219,6 +237,7 @@ int pkv_kv_cache_append(const void* k_new, const void* v_new, void* k_pool, void
     a.log2_bs = block_log2(block_size);
     a.num_blocks = num_blocks;
     a.num_queries = 1;
+    a.err = pkv::error_word();
     return pkv::launch_append(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -253,6 +272,7 @@ int pkv_kv_cache_append_multi(const void* k_new, const void* v_new, void* k_pool
     a.log2_bs = block_log2(block_size);
     a.num_blocks = num_blocks;
     a.num_queries = num_queries;
+    a.err = pkv::error_word();
     return pkv::launch_append(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -289,6 +309,8 @@ int pkv_kv_cache_append_fp8(const void* k_new, const void* v_new, pkv_dtype new_
     a.head_dim = head_dim;
     a.log2_bs = block_log2(block_size);
     a.num_blocks = num_blocks;
+    a.num_queries = 1;
+    a.err = pkv::error_word();
     return pkv::launch_append_fp8(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -312,6 +334,7 @@ int pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapping, in
     a.num_pairs = num_pairs;
     a.block_bytes = block_bytes;
     a.src_num_blocks = a.dst_num_blocks = num_blocks;
+    a.err = pkv::error_word();
     return pkv::launch_copy_blocks(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -353,6 +376,7 @@ int pkv_swap_blocks(const void* src_k, const void* src_v, int src_num_blocks, vo
     a.block_bytes = block_bytes;
     a.src_num_blocks = src_num_blocks;
     a.dst_num_blocks = dst_num_blocks;
+    a.err = pkv::error_word();
     return pkv::launch_copy_blocks(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -44,9 +44,15 @@ void append_kernel(const AppendParams a, long long total) {
     const int pos = L - a.num_queries + j;
     if (L <= 0 || pos < 0) return;
     const int blk = pos >> a.log2_bs;
-    if (blk >= a.max_blocks) return;
+    if (blk >= a.max_blocks) {
+        report_if(a.err, piece == 0, PKV_ERRBIT_APPEND);
+        return;
+    }
     const int phys = a.block_tables[(size_t)seq * a.max_blocks + blk];
-    if (phys < 0 || phys >= a.num_blocks) return;
+    if (phys < 0 || phys >= a.num_blocks) {
+        report_if(a.err, piece == 0, PKV_ERRBIT_APPEND);
+        return;
+    }
     const int slot = pos & ((1 << a.log2_bs) - 1);
     const size_t row = (((size_t)phys * a.num_kv_heads + g) << a.log2_bs) + (size_t)slot;
     const size_t dst = row * a.row_bytes + (size_t)piece * 16;
@@ -122,9 +128,15 @@ void append_fp8_kernel(const AppendFp8Params a, long long total) {
     if (L <= 0) return;
     const int pos = L - 1;
     const int blk = pos >> a.log2_bs;
-    if (blk >= a.max_blocks) return;
+    if (blk >= a.max_blocks) {
+        report_if(a.err, grp == 0, PKV_ERRBIT_APPEND);
+        return;
+    }
     const int phys = a.block_tables[(size_t)seq * a.max_blocks + blk];
-    if (phys < 0 || phys >= a.num_blocks) return;
+    if (phys < 0 || phys >= a.num_blocks) {
+        report_if(a.err, grp == 0, PKV_ERRBIT_APPEND);
+        return;
+    }
     const int slot = pos & ((1 << a.log2_bs) - 1);
     const float scale = (which ? a.v_scales : a.k_scales)[g];
     const char* src = reinterpret_cast<const char*>(which ? a.v_new : a.k_new) +
@@ -154,7 +166,10 @@ void copy_blocks_kernel(const CopyParams a, int chunks_per_block) {
     const int which = r & 1;
     const int src = a.mapping[2 * pair];
     const int dst = a.mapping[2 * pair + 1];
-    if (src < 0 || src >= a.src_num_blocks || dst < 0 || dst >= a.dst_num_blocks) return;
+    if (src < 0 || src >= a.src_num_blocks || dst < 0 || dst >= a.dst_num_blocks) {
+        report_if(a.err, threadIdx.x == 0 && chunk == 0, PKV_ERRBIT_COPY);
+        return;
+    }
     const char* s = reinterpret_cast<const char*>(which ? a.src_v : a.src_k) +
                     (size_t)src * a.block_bytes;
     char* d = reinterpret_cast<char*>(which ? a.dst_v : a.dst_k) + (size_t)dst * a.block_bytes;

@@ -76,7 +76,10 @@ __device__ __forceinline__ void decode_partition(const AttnParams& a, int item) 
         part = rest / a.num_kv_heads;
     }
 
-    const int L = clamp_len(a, a.seq_lens[seq]);
+    const int raw_len = a.seq_lens[seq];
+    report_if(a.err, lane == 0 && g == 0 && part == 0 && (raw_len < 0 || raw_len > a.max_tokens),
+              PKV_ERRBIT_LENGTH);
+    const int L = clamp_len(a, raw_len);
     if (L == 0) {                                   // padding row: zero output
         if (part == 0) write_zero_rows<D>(a, seq, g, lane);
         return;
@@ -288,9 +291,12 @@ void paged_decode_balanced_kernel(const AttnParams a) {
     const int W = a.num_items;
     // padding sequences (length 0) own no units: wave w zeroes the rows of
     // sequences w, w + W, ...
-    for (int i = w; i < a.num_seqs; i += W)
-        if (clamp_len(a, a.seq_lens[i]) == 0)
+    for (int i = w; i < a.num_seqs; i += W) {
+        const int raw_len = a.seq_lens[i];
+        report_if(a.err, lane == 0 && (raw_len < 0 || raw_len > a.max_tokens), PKV_ERRBIT_LENGTH);
+        if (clamp_len(a, raw_len) == 0)
             for (int g = 0; g < a.num_kv_heads; ++g) write_zero_rows<Walker::D>(a, i, g, lane);
+    }
     const long long total = units_before(a, a.num_seqs);
     const long long q = (total + W - 1) / W;
     const long long u0 = (long long)w * q;

@@ -85,6 +85,7 @@ struct Fp8VecWalker {
     const int* trow;
     size_t head_stride_bytes, kvhead_off;
     int log2_bs, bs_mask, nblk_valid, max_phys;
+    int* err;           // error word, or null
     int lane, tok, piece;
     int t_end, last_group;
 
@@ -99,6 +100,7 @@ struct Fp8VecWalker {
         bs_mask = (1 << a.log2_bs) - 1;
         nblk_valid = (L + bs_mask) >> a.log2_bs;
         max_phys = a.num_blocks;
+        err = a.err;
         trow = a.block_tables + (size_t)seq * a.max_blocks;
         head_stride_bytes = (size_t)a.num_kv_heads * ((size_t)ROW << a.log2_bs);
         kvhead_off = (size_t)g * ((size_t)ROW << a.log2_bs);
@@ -129,6 +131,9 @@ struct Fp8VecWalker {
     __device__ __forceinline__ void load_window(int first_block) {
         wb = first_block;
         tv = (wb + lane < nblk_valid) ? trow[wb + lane] : 0;
+        // an entry of a valid block outside the pool is read clamped; say so
+        report_wave(err, wb + lane < nblk_valid && (uint32_t)tv >= (uint32_t)max_phys,
+                    PKV_ERRBIT_TABLE);
     }
 
     __device__ __forceinline__ uint32_t phys(int blk) {
@@ -299,13 +304,17 @@ struct Fp8VecWalker {
 
 // ---------------------------------------------------------------------------
 // Matrix-core walker (2, 4 or 8 query heads per kv head, q in fp16 or bf16).
-// Same contractions and layouts as MfmaWalker<F16> (attn_mfma.hpp); the
-// codes are widened to fp16 (exact) on the way into the operands, two per
-// v_cvt_scalef32_pk_f16_fp8, and q is converted to fp16 once per segment.
-//   K, step s of group q: dims 16q + 8s' .. (s = 2h + s', h = 0, 1 picks
-//     bytes 16q or 64 + 16q of the row): one 16-byte load gives two steps.
+// Same contractions and layouts as MfmaWalker (attn_mfma.hpp), on the matrix
+// cores of q's own type: the codes are widened to that type (exact: every
+// E4M3 value is an fp16 and a bf16 value) on the way into the operands, two
+// per v_cvt_scalef32_pk_{f16,bf16}_fp8, and q rows load straight from memory.
+//   K, step s of group q: dims 64h + 16q + 8s' .. +7 (s = 2h + s', h = 0, 1
+//     picks bytes 16q or 64 + 16q of the row): one 16-byte load of codes
+//     gives two steps, and the same dims of q are 16 consecutive bytes.
 //   V: lane (n, q) loads the 8 codes of dims 8n .. 8n+7 of each of its
 //     tokens (an 8-byte load); tile c takes code c of the eight tokens.
+// Rows at or past the range end (masked in softmax_pv) re-read the range's
+// last row, which is in cache, as in the 16-bit walker.
 template <typename Q, int G_, bool STREAM>
 struct Fp8MfmaWalker {
     static constexpr bool kStream = STREAM;     // K/V load policy
@@ -318,7 +327,7 @@ struct Fp8MfmaWalker {
 
     f32x4 acc[8];
     float m, l, vscale, kfac;
-    u32x4 qb[4];        // fp16 B operand of Q^T for the four k-steps
+    u32x4 qb[4];        // B operand of Q^T (q's type) for the four k-steps
 
     int wb, tv;
     const char* kbase;
@@ -326,6 +335,7 @@ struct Fp8MfmaWalker {
     const int* trow;
     size_t head_stride_bytes, kvhead_off;
     int log2_bs, bs_mask, nblk_valid, max_phys;
+    int* err;           // error word, or null
     int lane, n, q;
     int t_end;
 
@@ -340,6 +350,7 @@ struct Fp8MfmaWalker {
         bs_mask = (1 << a.log2_bs) - 1;
         nblk_valid = (L + bs_mask) >> a.log2_bs;
         max_phys = a.num_blocks;
+        err = a.err;
         trow = a.block_tables + (size_t)seq * a.max_blocks;
         head_stride_bytes = (size_t)a.num_kv_heads * ((size_t)ROW << a.log2_bs);
         kvhead_off = (size_t)g * ((size_t)ROW << a.log2_bs);
@@ -351,17 +362,9 @@ struct Fp8MfmaWalker {
                            ((size_t)seq * a.num_kv_heads * G + (size_t)g * G + n) * D * Q::bytes;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            // step s = 2h + s2: dims 64h + 16q + 8 s2 .. +7
+            // step s = 2h + s2: dims 64h + 16q + 8 s2 .. +7, 16 bytes of q
             const int d0 = 64 * (s >> 1) + 16 * q + 8 * (s & 1);
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (n < G) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x0 = q_elem<Q>(qrow, d0 + 2 * i), x1 = q_elem<Q>(qrow, d0 + 2 * i + 1);
-                    w[i] = to16(F16{}, x0) | (to16(F16{}, x1) << 16);
-                }
-            }
-            qb[s] = w;
+            qb[s] = n < G ? load16(qrow + 2 * d0) : u32x4{0u, 0u, 0u, 0u};
         }
         m = -__builtin_inff();
         l = 0.f;
@@ -372,6 +375,9 @@ struct Fp8MfmaWalker {
     __device__ __forceinline__ void load_window(int first_block) {
         wb = first_block;
         tv = (wb + lane < nblk_valid) ? trow[wb + lane] : 0;
+        // an entry of a valid block outside the pool is read clamped; say so
+        report_wave(err, wb + lane < nblk_valid && (uint32_t)tv >= (uint32_t)max_phys,
+                    PKV_ERRBIT_TABLE);
     }
 
     __device__ __forceinline__ uint32_t phys(int blk) {
@@ -383,7 +389,8 @@ struct Fp8MfmaWalker {
     __device__ __forceinline__ void load_k(int c0, u32x4 (&kt)[2][2]) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int tok = c0 + 16 * t + n;
+            int tok = c0 + 16 * t + n;
+            tok = tok < t_end ? tok : t_end - 1;
             const char* p = kbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes +
                             kvhead_off + (uint32_t)((tok & bs_mask) * ROW + 16 * q);
             kt[t][0] = load16_kv<STREAM>(p);
@@ -391,30 +398,29 @@ struct Fp8MfmaWalker {
         }
     }
 
-    // V: vt[4h + j] = row (c0 + 16h + 4q + j), bytes 8n .. 8n+7
+    // V: vt[4h + j] = row (c0 + 16h + 4q + j), bytes 8n .. 8n+7. Four
+    // aligned consecutive tokens never straddle a block (bs >= 8); clamped
+    // rows stay in the block of the first one once it is clamped too.
     __device__ __forceinline__ void load_v(int c0, u32x2 (&vt)[8]) {
+        const int last = t_end - 1;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int tok = c0 + 16 * h + 4 * q;
-            const char* p = vbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes +
-                            kvhead_off + (uint32_t)((tok & bs_mask) * ROW + 8 * n);
+            const int tb = c0 + 16 * h + 4 * q;
+            const int t0 = tb < last ? tb : last;
+            const char* p = vbase + (size_t)phys((t0 >> log2_bs) - wb) * head_stride_bytes +
+                            kvhead_off + (uint32_t)(8 * n);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vt[4 * h + j] = load8_kv<STREAM>(p + ROW * j);
+            for (int j = 0; j < 4; ++j) {
+                const int tj = tb + j < last ? tb + j : last;
+                vt[4 * h + j] = load8_kv<STREAM>(p + (uint32_t)((tj & bs_mask) * ROW));
+            }
         }
     }
 
-    // two codes (bytes 2h, 2h + 1 of w) -> two fp16 values, packed, in one
-    // gfx950 conversion (scale 1: every E4M3 value is an fp16 value, exact)
-    template <bool H>
-    __device__ __forceinline__ static uint32_t pair_to_f16(uint32_t w) {
-        return __builtin_bit_cast(uint32_t,
-                                  __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, H));
-    }
-
-    // 8 codes (two dwords) -> the fp16 A operand of one k-step
-    __device__ __forceinline__ u32x4 codes_to_f16(uint32_t w0, uint32_t w1) {
-        return u32x4{pair_to_f16<false>(w0), pair_to_f16<true>(w0), pair_to_f16<false>(w1),
-                     pair_to_f16<true>(w1)};
+    // 8 codes (two dwords) -> the A operand (q's type) of one k-step
+    __device__ __forceinline__ static u32x4 codes_to_16(uint32_t w0, uint32_t w1) {
+        return u32x4{fp8_pair<Q, false>(w0), fp8_pair<Q, true>(w0), fp8_pair<Q, false>(w1),
+                     fp8_pair<Q, true>(w1)};
     }
 
     __device__ __forceinline__ void scores(const u32x4 (&kt)[2][2], float scale_log2,
@@ -425,9 +431,9 @@ struct Fp8MfmaWalker {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 const int s = 2 * h + s2;
-                s0 = mfma_16x16x32(F16{}, codes_to_f16(kt[0][h][2 * s2], kt[0][h][2 * s2 + 1]),
+                s0 = mfma_16x16x32(Q{}, codes_to_16(kt[0][h][2 * s2], kt[0][h][2 * s2 + 1]),
                                    qb[s], s0);
-                s1 = mfma_16x16x32(F16{}, codes_to_f16(kt[1][h][2 * s2], kt[1][h][2 * s2 + 1]),
+                s1 = mfma_16x16x32(Q{}, codes_to_16(kt[1][h][2 * s2], kt[1][h][2 * s2 + 1]),
                                    qb[s], s1);
             }
         }
@@ -467,20 +473,20 @@ struct Fp8MfmaWalker {
         u32x4 bhi, blo;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const uint32_t h0 = to16(F16{}, p[2 * w]), h1 = to16(F16{}, p[2 * w + 1]);
-            const uint32_t r0 = to16(F16{}, p[2 * w] - from16(F16{}, h0));
-            const uint32_t r1 = to16(F16{}, p[2 * w + 1] - from16(F16{}, h1));
+            const uint32_t h0 = to16(Q{}, p[2 * w]), h1 = to16(Q{}, p[2 * w + 1]);
+            const uint32_t r0 = to16(Q{}, p[2 * w] - from16(Q{}, h0));
+            const uint32_t r1 = to16(Q{}, p[2 * w + 1] - from16(Q{}, h1));
             bhi[w] = h0 | (h1 << 16);
             blo[w] = r0 | (r1 << 16);
         }
-        // widen the eight V pieces: hv[j][k] = codes 2k, 2k+1 of token j as fp16
+        // widen the eight V pieces: hv[j][k] = codes 2k, 2k+1 of token j in q's type
         uint32_t hv[8][4];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            hv[j][0] = pair_to_f16<false>(vt[j][0]);
-            hv[j][1] = pair_to_f16<true>(vt[j][0]);
-            hv[j][2] = pair_to_f16<false>(vt[j][1]);
-            hv[j][3] = pair_to_f16<true>(vt[j][1]);
+            hv[j][0] = fp8_pair<Q, false>(vt[j][0]);
+            hv[j][1] = fp8_pair<Q, true>(vt[j][0]);
+            hv[j][2] = fp8_pair<Q, false>(vt[j][1]);
+            hv[j][3] = fp8_pair<Q, true>(vt[j][1]);
         }
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -492,8 +498,8 @@ struct Fp8MfmaWalker {
                 av[w] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
             }
             f32x4 o = acc[c] * alpha;
-            o = mfma_16x16x32(F16{}, av, bhi, o);
-            acc[c] = mfma_16x16x32(F16{}, av, blo, o);
+            o = mfma_16x16x32(Q{}, av, bhi, o);
+            acc[c] = mfma_16x16x32(Q{}, av, blo, o);
         }
     }
 

@@ -155,6 +155,7 @@ struct MfmaWalker {
     size_t head_stride_bytes;
     size_t kvhead_off;
     int log2_bs, bs_mask, nblk_valid, max_phys;
+    int* err;           // error word, or null
     int lane, n, q;
     int t_end;
     int ncols;          // real columns: num_queries * G (the rest are zero padding)
@@ -173,6 +174,7 @@ struct MfmaWalker {
         bs_mask = (1 << a.log2_bs) - 1;
         nblk_valid = (L + bs_mask) >> a.log2_bs;
         max_phys = a.num_blocks;
+        err = a.err;
         trow = a.block_tables + (size_t)seq * a.max_blocks;
         head_stride_bytes = (size_t)a.num_kv_heads * ((size_t)ROW << a.log2_bs);
         kvhead_off = (size_t)g * ((size_t)ROW << a.log2_bs);
@@ -206,6 +208,7 @@ struct MfmaWalker {
         bs_mask = (1 << a.log2_bs) - 1;
         nblk_valid = (L + bs_mask) >> a.log2_bs;
         max_phys = a.num_blocks;
+        err = a.err;
         trow = a.block_tables + (size_t)table_seq * a.max_blocks;
         head_stride_bytes = (size_t)a.num_kv_heads * ((size_t)ROW << a.log2_bs);
         kvhead_off = (size_t)g * ((size_t)ROW << a.log2_bs);
@@ -227,6 +230,9 @@ struct MfmaWalker {
     __device__ __forceinline__ void load_window(int first_block) {
         wb = first_block;
         tv = (wb + lane < nblk_valid) ? trow[wb + lane] : 0;
+        // an entry of a valid block outside the pool is read clamped; say so
+        report_wave(err, wb + lane < nblk_valid && (uint32_t)tv >= (uint32_t)max_phys,
+                    PKV_ERRBIT_TABLE);
     }
 
     // physical block of window block blk (per lane, 0 <= blk < 64)

@@ -68,6 +68,7 @@ struct VecWalker {
     size_t head_stride_bytes;   // bytes from one physical block to the next
     size_t kvhead_off;          // bytes of kv head g inside a block
     int log2_bs, bs_mask, nblk_valid, max_phys;
+    int* err;           // error word, or null
     int lane, tok, piece;
     int t_end, last_group;
 
@@ -83,6 +84,9 @@ struct VecWalker {
     __device__ __forceinline__ void load_window(int first_block) {
         wb = first_block;
         tv = (wb + lane < nblk_valid) ? trow[wb + lane] : 0;
+        // an entry of a valid block outside the pool is read clamped; say so
+        report_wave(err, wb + lane < nblk_valid && (uint32_t)tv >= (uint32_t)max_phys,
+                    PKV_ERRBIT_TABLE);
     }
 
     // physical block of logical block blk (wave-uniform, inside the window)
@@ -161,6 +165,7 @@ struct VecWalker {
         bs_mask = (1 << a.log2_bs) - 1;
         nblk_valid = (L + bs_mask) >> a.log2_bs;
         max_phys = a.num_blocks;
+        err = a.err;
         trow = a.block_tables + (size_t)seq * a.max_blocks;
         head_stride_bytes = (size_t)a.num_kv_heads * ((size_t)Gm::ROW << a.log2_bs);
         kvhead_off = (size_t)g * ((size_t)Gm::ROW << a.log2_bs);

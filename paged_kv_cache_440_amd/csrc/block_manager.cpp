@@ -221,6 +221,11 @@ int pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id) {
     if (!bm) return PKV_ERR_INVALID;
     auto it = bm->seqs.find(seq_id);
     if (it == bm->seqs.end()) return PKV_ERR_INVALID;
+    // A queued copy's destination or source could return to the free stack
+    // here and be handed out again before the copy runs: as a second copy's
+    // destination (two pairs writing one block) or as a destination while
+    // still a source (pairs of one copy_blocks call run concurrently).
+    if (!bm->copies.empty()) return PKV_ERR_INVALID;
     if (it->second.swapped) {
         for (int32_t b : it->second.table)
             if (--bm->host_refcount[b] == 0) bm->host_free.push_back(b);

@@ -169,4 +169,17 @@ __device__ __forceinline__ float strided_max(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// OR `bits` into the caller's error word from every lane where `bad` holds
+// (a global atomic through the vector memory path; err may be null).
+__device__ __forceinline__ void report_if(int* err, bool bad, int bits) {
+    if (err != nullptr && bad) atomicOr(err, bits);
+}
+
+// The same for a wave: one atomic, from the lowest lane where `bad` holds.
+__device__ __forceinline__ void report_wave(int* err, bool bad, int bits) {
+    if (err == nullptr) return;
+    const unsigned long long any = __ballot(bad);
+    if (any != 0 && (int)(threadIdx.x & 63) == __builtin_ctzll(any)) atomicOr(err, bits);
+}
+
 }  // namespace pkv

@@ -50,6 +50,7 @@ struct AttnParams {
                                    // [B][num_queries][H][D]. A segment (seq, kv head) has
                                    // num_queries * group columns (query token, head).
     int dtype;                     // q / K / V element type (16/32-bit path)
+    int* err;                      // error word (pkv_set_error_word), or null
     // FP8 pools: K/V are E4M3 codes times a per-kv-head scale; q has q_dtype
     const float* k_scales;
     const float* v_scales;
@@ -80,6 +81,7 @@ struct AppendParams {
     int log2_bs;
     int num_blocks;
     int num_queries;               // new tokens per sequence: k_new is [B][nq][Hkv][D]
+    int* err;                      // error word (pkv_set_error_word), or null
 };
 
 // Quantising append into FP8 E4M3 pools.
@@ -99,6 +101,8 @@ struct AppendFp8Params {
     int head_dim;
     int log2_bs;
     int num_blocks;
+    int num_queries;               // new tokens per sequence: k_new is [B][nq][Hkv][D]
+    int* err;                      // error word (pkv_set_error_word), or null
 };
 
 // Block copies from one pool pair into another (the same pair for
@@ -113,7 +117,11 @@ struct CopyParams {
     long long block_bytes;         // num_kv_heads * block_size * row bytes
     int src_num_blocks;
     int dst_num_blocks;
+    int* err;                      // error word (pkv_set_error_word), or null
 };
+
+// The error word registered for the current device (null if none).
+int* error_word();
 
 hipError_t launch_paged_attention(const AttnParams& a, hipStream_t stream);
 hipError_t launch_append(const AppendParams& a, hipStream_t stream);

@@ -8,6 +8,9 @@ no expected value is computed from device results.
 
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -18,6 +21,30 @@ from oracle import (fp8_dequantize_pool, paged_decode_attention, pool_after_appe
 # max-abs tolerance on attention outputs (fp32 accumulation, fp32 output)
 TOL = {torch.float32: 1e-5, torch.float16: 2e-3, torch.bfloat16: 2e-3}
 _INT = {4: torch.int32, 2: torch.int16, 1: torch.uint8}
+
+
+# Precision guards: per kernel path, the max-abs error observed on the
+# full-size parity cases (fixed seeds) and a bound of ten times that. The
+# tolerances above are the acceptance bar; a guard catches a precision
+# regression far below it (a dropped residual term, a narrower accumulator).
+_GUARDS_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                            "precision_guards.json")
+GUARDS = json.load(open(_GUARDS_PATH))["paths"] if os.path.exists(_GUARDS_PATH) else {}
+
+
+def check_error(path: str, err: float, tolerance: float, what: str = "") -> None:
+    """Assert the acceptance tolerance, then the path's precision guard.
+    With PKV_RECORD_ERRORS=<file> set, each observation is also appended to
+    that file as a JSON line (how the guards' observed values are taken)."""
+    assert err <= tolerance, f"{what}: max abs error {err:.3e} above {tolerance:g}"
+    rec = os.environ.get("PKV_RECORD_ERRORS")
+    if rec:
+        with open(rec, "a") as f:
+            f.write(json.dumps({"path": path, "what": what, "err": err}) + "\n")
+    g = GUARDS.get(path)
+    if g is not None:
+        assert err <= g["bound"], (f"{what}: max abs error {err:.3e} is over the {path} "
+                                   f"guard {g['bound']:.3e} (observed {g['observed']:.3e})")
 
 
 def tol(w) -> float:

@@ -350,3 +350,21 @@ def test_stage_keyword_maps_to_the_flags():
     assert _lib._policy(False, "walk") == 0x10 and _lib._policy(True, "merge") == 0x21
     with pytest.raises(ValueError):
         _lib._policy(False, "reduce")
+
+
+@pytest.mark.parametrize("stage", ["walk", "merge"])
+def test_split_stages_refuse_an_internal_workspace(lib, stage):
+    """A walk call leaves partial results in its workspace for the merge call:
+    the binding must not allocate one of its own for either half (it would be
+    dropped, and its memory reused, between the two calls). The refusal comes
+    before any tensor reaches the library, so CPU tensors do here."""
+    import torch
+    q = torch.zeros(2, 4, 128, dtype=torch.float16)
+    pool = torch.zeros(8, 4, 16, 128, dtype=torch.float16)
+    tables = torch.zeros(2, 8, dtype=torch.int32)
+    lens = torch.full((2,), 100, dtype=torch.int32)
+    with pytest.raises(ValueError, match="caller-owned workspace"):
+        _lib.paged_attention_decode(torch.empty_like(q, dtype=torch.float32), q, pool, pool,
+                                    tables, lens, 128, 0.1, partition_size=64, stage=stage)
+    # the whole call, or a single pass (nothing to merge), needs no caller workspace
+    assert _lib._workspace(0, None, "cpu", None, stage) is None

@@ -16,7 +16,8 @@ import torch
 import paged_kv_cache_440_amd as pkv
 from oracle import paged_decode_attention
 from paged_kv_cache_440_amd import workloads as wl
-from tests.gpu_support import (Device, bits, expected_attention, expected_pools, max_err,
+from tests.gpu_support import (Device, bits, check_error, expected_attention, expected_pools,
+                               max_err,
                                poison_unwritten_slots, widen)
 
 pytestmark = pytest.mark.gpu
@@ -123,4 +124,4 @@ def test_full_size_matches_oracle(name, partition, kv_reuse):
     assert np.array_equal(bits(d.k_pool), kb) and np.array_equal(bits(d.v_pool), vb)
     del d
     err = max_err(out, expected_attention(w, kb, vb))
-    assert err <= 2e-3, f"max abs error {err:.3e}"
+    check_error("grouped_f16", err, 2e-3, f"{name} partition {partition} reuse {kv_reuse}")

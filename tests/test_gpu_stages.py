@@ -108,3 +108,30 @@ def test_grouped(partition):
                                            partition_size=partition, workspace=ws, stage=stage)
 
     assert_same_bits(*both_and_split(call, w, partition))
+
+
+def test_internal_workspace_on_a_side_stream():
+    """workspace=None on a stream other than the current one: the binding's
+    own workspace is tied to that stream, and the result is the bits of the
+    call on the current stream with a caller workspace."""
+    w = wl.opt13b_fp16(num_seqs=8, len_range=(600, 1500))
+    d = Device(w)
+    d.copy_and_append()
+    ref = torch.empty(tuple(w.q.shape), dtype=torch.float32, device="cuda")
+    pkv.paged_attention_decode(ref, d.q, d.k_pool, d.v_pool, d.tables, d.lens, w.max_seq_len,
+                               w.scale, partition_size=64, workspace=workspace(w, 64, 0))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        out = torch.full(tuple(w.q.shape), float("nan"), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        pkv.paged_attention_decode(out, d.q, d.k_pool, d.v_pool, d.tables, d.lens, w.max_seq_len,
+                                   w.scale, partition_size=64, stream=side)
+        # allocations on the current stream meanwhile must not take the
+        # workspace's memory while the side stream still uses it
+        torch.empty(1 << 22, dtype=torch.uint8, device="cuda").fill_(0x55)
+        outs.append(out)
+    side.synchronize()
+    for out in outs:
+        assert_same_bits(ref, out)
