@@ -79,7 +79,8 @@ typedef enum {
     PKV_ERR_UNSUPPORTED = -2, /* head_dim / block_size / head grouping / dtype not built */
     PKV_ERR_WORKSPACE = -3,   /* split-K workspace missing, misaligned or too small */
     PKV_ERR_HIP = -4,         /* the HIP runtime reported an error when launching */
-    PKV_ERR_NO_BLOCKS = -5    /* block manager: the pool has no free block */
+    PKV_ERR_NO_BLOCKS = -5,   /* block manager: the pool has no free block */
+    PKV_ERR_SCRATCH = -6      /* the call needs more scratch than the static buffer holds */
 } pkv_status;
 
 /*
@@ -228,6 +229,34 @@ PKV_API int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype,
                                int head_dim, int block_size, int num_blocks,
                                float scale, int partition_size,
                                void* workspace, size_t workspace_bytes,
+                               pkv_dtype dtype, int kv_policy, void* stream);
+
+/*
+ * pkv_paged_attention_decode without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. The split-K records go to a
+ * static device array of the library instead, PKV_NOALLOC_SCRATCH_BYTES
+ * bytes, one copy per device, held from the library's first use on that
+ * device until the process ends. Arguments, results (the same bits) and
+ * errors are those of pkv_paged_attention_decode, plus PKV_ERR_SCRATCH,
+ * before anything is enqueued, when pkv_paged_attention_workspace_size(...)
+ * for these arguments exceeds PKV_NOALLOC_SCRATCH_BYTES (the balanced
+ * schedule fits for up to 8 query heads per kv head at head_dim 128). The
+ * call allocates nothing; its first call on a device looks up that
+ * device's copy of the array. Every call on a device shares its copy, which
+ * keeps the last call's contents: calls that can overlap on one device
+ * (different streams, or different host threads) race and give wrong
+ * results; so does any such call between a PKV_STAGE_WALK call and its
+ * PKV_STAGE_MERGE call.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+PKV_API int pkv_paged_attention_decode_noalloc(void* out, pkv_dtype out_dtype, const void* q,
+                               const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* seq_lens, int max_seq_len,
+                               int num_seqs, int num_heads, int num_kv_heads,
+                               int head_dim, int block_size, int num_blocks,
+                               float scale, int partition_size,
                                pkv_dtype dtype, int kv_policy, void* stream);
 
 /*

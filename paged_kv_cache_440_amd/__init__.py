@@ -17,6 +17,8 @@ _API = (
     "copy_blocks",
     "swap_blocks",
     "paged_attention_decode",
+    "paged_attention_decode_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "paged_attention_workspace_size",
     "status_string",
     "probe_read",

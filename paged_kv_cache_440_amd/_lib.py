@@ -19,7 +19,9 @@ DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 FP8_E4M3 = 3            # PKV_FP8_E4M3: pools of uint8 E4M3 codes with per-head scales
 POOL_CODES = {**DTYPE_CODES, torch.uint8: FP8_E4M3}
 STATUS = {0: "PKV_OK", -1: "PKV_ERR_INVALID", -2: "PKV_ERR_UNSUPPORTED",
-          -3: "PKV_ERR_WORKSPACE", -4: "PKV_ERR_HIP", -5: "PKV_ERR_NO_BLOCKS"}
+          -3: "PKV_ERR_WORKSPACE", -4: "PKV_ERR_HIP", -5: "PKV_ERR_NO_BLOCKS",
+          -6: "PKV_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 40 << 20      # PKV_NOALLOC_SCRATCH_BYTES
 
 
 class PkvError(RuntimeError):
@@ -50,6 +52,9 @@ def library() -> ctypes.CDLL:
     lib.pkv_paged_attention_decode.argtypes = [P, I, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I,
                                                P, Z, I, I, P]
     lib.pkv_paged_attention_decode.restype = I
+    lib.pkv_paged_attention_decode_noalloc.argtypes = [P, I, P, P, P, P, I, P, I, I, I, I, I, I,
+                                                       I, F, I, I, I, P]
+    lib.pkv_paged_attention_decode_noalloc.restype = I
     lib.pkv_kv_cache_append_fp8.argtypes = [P, P, I, P, P, P, P, P, I, P, I, I, I, I, I, P]
     lib.pkv_kv_cache_append_fp8.restype = I
     lib.pkv_paged_attention_decode_fp8.argtypes = [P, I, P, I, P, P, P, P, P, I, P, I, I, I, I, I,
@@ -305,6 +310,32 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, max_s
         _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32),
         block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len),
         b, h, hkv, d, bs, nb, float(scale), int(partition_size), ws_ptr, ws_bytes, code,
+        _policy(kv_reuse, stage), _stream(stream)))
+    return out
+
+
+def paged_attention_decode_noalloc(out, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len,
+                                   scale, partition_size=PARTITION_BALANCED, stream=None,
+                                   kv_reuse: bool = False, stage: str = "both") -> torch.Tensor:
+    """pkv_paged_attention_decode_noalloc: paged_attention_decode with its
+    split-K records in the library's static per-device scratch (nothing is
+    allocated, here or in the library). Calls that can overlap on one device
+    race on that scratch."""
+    nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
+    if code == FP8_E4M3:
+        raise TypeError("uint8 (FP8) pools are read by paged_attention_decode_fp8")
+    if q.dim() != 3 or q.shape[2] != d or q.dtype != k_pool.dtype:
+        raise ValueError("q must be [num_seqs][num_heads][head_dim] in the pool's dtype")
+    b, h = q.shape[0], q.shape[1]
+    if out.shape != q.shape or out.dtype not in DTYPE_CODES:
+        raise ValueError("out must be [num_seqs][num_heads][head_dim], float32/float16/bfloat16")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or seq_lens.shape != (b,):
+        raise ValueError("block_tables must be [num_seqs][max_blocks], seq_lens [num_seqs]")
+    _check("pkv_paged_attention_decode_noalloc", library().pkv_paged_attention_decode_noalloc(
+        _dev(out, "out"), DTYPE_CODES[out.dtype], _dev(q, "q"), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len),
+        b, h, hkv, d, bs, nb, float(scale), int(partition_size), code,
         _policy(kv_reuse, stage), _stream(stream)))
     return out
 

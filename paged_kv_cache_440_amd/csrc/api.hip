@@ -196,6 +196,8 @@ const char* pkv_status_string(int status) {
         case PKV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case PKV_ERR_HIP: return "HIP runtime error at launch";
         case PKV_ERR_NO_BLOCKS: return "no free block in the pool";
+        case PKV_ERR_SCRATCH:
+            return "the call needs more split-K scratch than the library's static buffer holds";
         default: return "unknown status";
     }
 }

@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert _lib.status_string(code) and _lib.status_string(code) != "unknown status"
     assert _lib.status_string(42) == "unknown status"
 
@@ -368,3 +368,21 @@ def test_split_stages_refuse_an_internal_workspace(lib, stage):
                                     tables, lens, 128, 0.1, partition_size=64, stage=stage)
     # the whole call, or a single pass (nothing to merge), needs no caller workspace
     assert _lib._workspace(0, None, "cpu", None, stage) is None
+
+
+def test_noalloc_refuses_a_call_beyond_its_static_scratch(lib):
+    """pkv_paged_attention_decode_noalloc checks the call's workspace need
+    against its static scratch before touching the device: PKV_ERR_SCRATCH
+    for more, the ordinary validation of pkv_paged_attention_decode
+    otherwise (here a missing pointer)."""
+    import ctypes
+    SCRATCH = -6
+    assert _lib.paged_attention_workspace_size(256, 40, 40, 128, 4096, 64) > _lib.NOALLOC_SCRATCH_BYTES
+    args = [FAKE, 0, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 4096, 256, 40, 40, 128, 16, 100000,
+            ctypes.c_float(0.1), 64, 1, 0, None]
+    assert lib.pkv_paged_attention_decode_noalloc(*args) == SCRATCH
+    assert _lib.paged_attention_workspace_size(256, 40, 40, 128, 4096, 1024) <= _lib.NOALLOC_SCRATCH_BYTES
+    args[9] = -1                                     # a negative batch is the decode call's error
+    assert lib.pkv_paged_attention_decode_noalloc(*args) == INVALID
+    args[9] = 0                                      # an empty batch enqueues nothing
+    assert lib.pkv_paged_attention_decode_noalloc(*args) == OK
