@@ -82,6 +82,10 @@ DEFAULT_SCHEDULE = {
     "shared_prefix_cow_fp16": 1024,
     "opt13b_fp8": 512,
     "opt13b_spec4_fp16": "balanced",
+    "opt13b_spec4_fp8": "balanced",
+    "opt13b_prefill256_fp16": "balanced",   # a single pass per 16-column tile
+    "shared_prefix_fp8": 1024,           # grouped call over an FP8 cache
+    "shared_prefix_cow_fp8": 1024,
     "tiny_fp32": 512,
 }
 
@@ -101,7 +105,8 @@ def cpu_baseline(w, min_seconds: float = 10.0):
     from concurrent.futures import ThreadPoolExecutor
     from threadpoolctl import threadpool_limits
     from oracle import (fp8_dequantize_pool, paged_decode_attention, paged_multi_query_attention,
-                        pool_after_append, pool_after_append_fp8, pool_after_append_multi)
+                        pool_after_append, pool_after_append_fp8, pool_after_append_multi,
+                        pool_after_append_multi_fp8)
 
     def bits(t):
         ints = {1: torch.uint8, 2: torch.int16, 4: torch.int32}
@@ -121,19 +126,25 @@ def cpu_baseline(w, min_seconds: float = 10.0):
         fn = paged_multi_query_attention if w.num_queries > 1 else paged_decode_attention
         fn(q[idx], kf, vf, w.block_tables[idx], w.seq_lens[idx], w.block_size, w.scale)
 
+    spent = {"append": 0.0, "attention": 0.0}
+
     def one_step(ex):
+        t_a = time.perf_counter()
         if w.fp8:
             ks, vs = w.k_scales.numpy(), w.v_scales.numpy()
-            k2, v2 = pool_after_append_fp8(kb, vb, w.k_new.float().numpy(),
-                                           w.v_new.float().numpy(), ks, vs, w.block_tables,
-                                           w.seq_lens, w.block_size)
+            app = pool_after_append_multi_fp8 if w.num_queries > 1 else pool_after_append_fp8
+            k2, v2 = app(kb, vb, w.k_new.float().numpy(), w.v_new.float().numpy(), ks, vs,
+                         w.block_tables, w.seq_lens, w.block_size)
             kf, vf = fp8_dequantize_pool(k2, ks), fp8_dequantize_pool(v2, vs)
         else:
             app = pool_after_append_multi if w.num_queries > 1 else pool_after_append
             k2, v2 = app(kb, vb, bits(w.k_new), bits(w.v_new), w.block_tables, w.seq_lens,
                          w.block_size)
             kf, vf = widen(k2), widen(v2)
+        t_b = time.perf_counter()
         list(ex.map(lambda idx: attention(idx, kf, vf), parts))
+        spent["append"] += t_b - t_a
+        spent["attention"] += time.perf_counter() - t_b
 
     # whole steps until at least min_seconds of oracle work (one step at least)
     with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
@@ -145,11 +156,19 @@ def cpu_baseline(w, min_seconds: float = 10.0):
             dt = time.perf_counter() - t0
             if dt >= min_seconds:
                 break
-    return {"value": steps * w.num_seqs * w.num_queries / dt, "unit": "tokens/s",
+    tokens = steps * w.num_seqs * w.num_queries
+    attn_rate = tokens / spent["attention"]
+    return {"value": tokens / dt, "unit": "tokens/s",
             "cores": workers, "kind": "oracle",
+            "attention_only_tokens_per_s": attn_rate,
+            "append_s_per_step": spent["append"] / steps,
+            "attention_s_per_step": spent["attention"] / steps,
             "sample": f"{steps} whole decode steps of the batch ({w.num_seqs} sequences, all "
                       f"heads: append + attention), float64 numpy; attention over {workers} "
-                      f"threads, the append on one; {dt:.1f} s wall"}
+                      f"threads, the append on one; {dt:.1f} s wall, of which the append "
+                      f"(the oracle's functional copy of both pools plus the scatter) "
+                      f"{spent['append']:.1f} s and attention {spent['attention']:.1f} s: "
+                      f"attention alone runs at {attn_rate:.1f} tokens/s"}
 
 
 def block_manager_bench(steps: int, warmup: int) -> None:
@@ -359,6 +378,9 @@ def main():
     ap.add_argument("--no-grouped", action="store_true",
                     help="time parallel-sampling workloads with the plain decode call instead "
                          "of the grouped one (shared prompt blocks read once per group)")
+    ap.add_argument("--walker", choices=("auto", "vector"), default="auto",
+                    help="vector: grouped query heads on the vector units instead of the matrix "
+                         "cores (PKV_WALKER_VECTOR), for comparison")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-manager", action="store_true",
                     help="only time the host block manager's decode-step bookkeeping "
@@ -425,7 +447,18 @@ def main():
     auto_reuse = w.shared_blocks and not grouped
     reuse = auto_reuse if args.kv_policy == "auto" else args.kv_policy == "reuse"
 
-    if w.num_queries > 1:
+    if w.num_queries > 1 and w.fp8:
+        ks, vs = w.k_scales.to(dev), w.v_scales.to(dev)
+
+        def attention(stage="both"):
+            pkv.paged_attention_multi_fp8(out, q, kp, vp, ks, vs, tables, lens, max_len, w.scale,
+                                          partition_size=args.partition, workspace=ws,
+                                          stream=stream, kv_reuse=reuse, stage=stage)
+
+        def append():
+            pkv.kv_cache_append_multi_fp8(k_new, v_new, kp, vp, ks, vs, tables, lens,
+                                          stream=stream)
+    elif w.num_queries > 1:
         def attention(stage="both"):
             pkv.paged_attention_multi(out, q, kp, vp, tables, lens, max_len, w.scale,
                                       partition_size=args.partition, workspace=ws, stream=stream,
@@ -433,6 +466,19 @@ def main():
 
         def append():
             pkv.kv_cache_append_multi(k_new, v_new, kp, vp, tables, lens, stream=stream)
+    elif grouped and w.fp8:
+        ks, vs = w.k_scales.to(dev), w.v_scales.to(dev)
+        samples = w.info["samples"]
+        shared = torch.from_numpy(wl.shared_tokens(w, samples)).to(dev)
+
+        def attention(stage="both"):
+            pkv.paged_attention_decode_grouped_fp8(out, q, kp, vp, ks, vs, tables, lens, max_len,
+                                                   w.scale, samples, shared,
+                                                   partition_size=args.partition, workspace=ws,
+                                                   stream=stream, kv_reuse=reuse, stage=stage)
+
+        def append():
+            pkv.kv_cache_append_fp8(k_new, v_new, kp, vp, ks, vs, tables, lens, stream=stream)
     elif w.fp8:
         ks, vs = w.k_scales.to(dev), w.v_scales.to(dev)
 
@@ -459,12 +505,14 @@ def main():
         def attention(stage="both"):
             pkv.paged_attention_decode(out, q, kp, vp, tables, lens, max_len, w.scale,
                                        partition_size=args.partition, workspace=ws, stream=stream,
-                                       kv_reuse=reuse, stage=stage)
+                                       kv_reuse=reuse, stage=stage, walker=args.walker)
 
         def append():
             pkv.kv_cache_append(k_new, v_new, kp, vp, tables, lens, stream=stream)
 
-    entry = ("paged_attention_multi" if w.num_queries > 1 else
+    entry = ("paged_attention_multi_fp8" if w.num_queries > 1 and w.fp8 else
+             "paged_attention_multi" if w.num_queries > 1 else
+             "paged_attention_decode_grouped_fp8" if grouped and w.fp8 else
              "paged_attention_decode_fp8" if w.fp8 else
              "paged_attention_decode_grouped" if grouped else
              "paged_attention_decode")
@@ -527,7 +575,33 @@ def main():
     torch.cuda.synchronize()
     read_ceiling = pool_bytes / (float(np.mean([a.elapsed_time(b) for a, b in rd])) * 1e-3) / 1e9
 
+    # ceiling of the paged access pattern itself: the same rows through the
+    # same tables with the same loads and split, no compute (best of a sweep
+    # of waves per compute unit and loads per round)
     kv_bytes = w.kv_bytes()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    gsink = torch.empty(16 * cus, dtype=torch.int32, device=dev)
+    gather = []
+    for per_cu in (4, 8, 16):
+        for loads in (2, 4, 8):
+            run_g = lambda: pkv.probe_gather(kp, vp, tables, lens, per_cu * cus, loads, gsink,
+                                             stream=stream)
+            for _ in range(2):
+                run_g()
+            ge = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(10)]
+            for a, b in ge:
+                a.record(stream)
+                run_g()
+                b.record(stream)
+            torch.cuda.synchronize()
+            g_us = float(np.mean([a.elapsed_time(b) for a, b in ge])) * 1e3
+            gather.append((kv_bytes / (g_us * 1e-6) / 1e9, per_cu, loads, g_us))
+    gather_gbps, g_per_cu, g_loads, g_us = max(gather)
+    log(f"[bench] paged gather probe: {gather_gbps:.0f} GB/s ({g_us:.1f} us; {g_per_cu} waves "
+        f"per CU, {g_loads} loads of K and of V per round); sweep "
+        + ", ".join(f"{c}/{l}: {x:.0f}" for x, c, l, _ in gather))
+
     unique_bytes = w.unique_kv_bytes()
     # the roofline counts what HBM must deliver, each distinct K/V row once,
     # over the dominant kernel's own time; the whole call is reported beside it
@@ -576,6 +650,7 @@ def main():
             "partition_size": args.partition,
             "kv_policy": "reuse" if reuse else "stream",
             "entry": entry,
+            "walker": args.walker,
             "kv_bytes_per_step": kv_bytes,
             "unique_kv_bytes_per_step": unique_bytes,
         },
@@ -592,6 +667,10 @@ def main():
         "kv_frac_of_peak": achieved / PEAK_HBM_GBPS,
         "read_probe_gbps": read_ceiling,
         "kv_frac_of_read_probe": achieved / read_ceiling,
+        "gather_probe_gbps": gather_gbps,
+        "gather_probe_us": g_us,
+        "gather_probe_config": {"waves_per_cu": g_per_cu, "loads_per_round": g_loads},
+        "walk_frac_of_gather_probe": g_us / (walk_ms * 1e3),
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,

@@ -159,12 +159,25 @@ PKV_API int pkv_copy_blocks(void* k_pool, void* v_pool,
 #define PKV_STAGE_MERGE 0x20
 
 /*
+ * PKV_WALKER_VECTOR, OR-ed into kv_policy of pkv_paged_attention_decode (and
+ * only there): run 4 or 8 query heads per kv head (16-bit K/V, head_dim 128)
+ * on the vector units instead of the matrix cores. For measurement: it shows
+ * what the matrix cores buy on grouped-query layers. Results agree with the
+ * default within the same tolerance, not bit for bit. Streaming policy only
+ * (PKV_ERR_UNSUPPORTED with PKV_KV_REUSE); no effect where the vector walker
+ * is the default already.
+ */
+#define PKV_WALKER_VECTOR 0x40
+
+/*
  * Bytes of workspace pkv_paged_attention_decode needs for the given sizes and
  * partition_size (0 when it needs none: partition_size == 0, or every
  * sequence fits one partition). Returns 0 for invalid sizes as well. For
  * PKV_PARTITION_BALANCED the size depends only on head_dim and the head
  * grouping: 2 * 4096 * (num_heads / num_kv_heads) * (head_dim + 2) * 4 bytes
- * of partial records plus 2 * 4096 * 4 bytes of merge information.
+ * of partial records plus 2 * 4096 * 4 bytes of merge information, and 0
+ * when num_heads / num_kv_heads exceeds 16 (more than 16 columns per kv head
+ * run the balanced schedule as a single pass).
  */
 PKV_API size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
                                           int head_dim, int max_seq_len, int partition_size);
@@ -306,11 +319,17 @@ PKV_API int pkv_paged_attention_decode_grouped(void* out, pkv_dtype out_dtype, c
  * pkv_paged_attention_multi: q and out [num_seqs][nq][num_heads][head_dim];
  * new token j (position p = L-nq+j) attends causally to positions 0 .. p:
  *   out[i][j][h] = sum_{t <= p} softmax_t(scale * q[i][j][h] . K_i[t][g]) V_i[t][g]
- * (a token with p < 0 gets a zero row). F16 / BF16 K/V and q, head_dim 128,
- * nq * (num_heads / num_kv_heads) <= 16 (PKV_ERR_UNSUPPORTED otherwise).
- * partition_size, kv_policy and the workspace work as in pkv_paged_attention_decode;
- * size the workspace with pkv_paged_attention_workspace_size(num_seqs,
- * num_heads * nq, num_kv_heads, head_dim, max_seq_len, partition_size).
+ * (a token with p < 0 gets a zero row). F16 / BF16 K/V and q, head_dim 128
+ * (PKV_ERR_UNSUPPORTED otherwise). The nq * (num_heads / num_kv_heads)
+ * (query token, head) columns of a (sequence, kv head) run on the matrix
+ * cores 16 at a time; each group of 16 reads the cache only up to the causal
+ * limit of its last column, so a long prefill chunk costs its causal work,
+ * not nq times the history. partition_size, kv_policy and the workspace work
+ * as in pkv_paged_attention_decode, except that with more than 16 columns
+ * PKV_PARTITION_BALANCED runs as a single pass over each group of 16 columns
+ * (the groups fill the GPU; no workspace). Size the workspace with
+ * pkv_paged_attention_workspace_size(num_seqs, num_heads * nq, num_kv_heads,
+ * head_dim, max_seq_len, partition_size).
  */
 PKV_API int pkv_kv_cache_append_multi(const void* k_new, const void* v_new,
                               void* k_pool, void* v_pool,
@@ -408,6 +427,62 @@ PKV_API int pkv_paged_attention_decode_fp8(void* out, pkv_dtype out_dtype,
 #define PKV_ERRBIT_APPEND 0x4
 #define PKV_ERRBIT_COPY 0x8
 PKV_API int pkv_set_error_word(int32_t* error_word);
+
+/*
+ * The multi-query and sampling-group calls over FP8 pools (blog.aqudi.me
+ * section 4 names both a lower-precision KV cache and the several-token
+ * passes of chunked prefill and speculative decoding; [summary] section
+ * "블록 공유" the samples sharing a prompt's blocks).
+ *
+ * pkv_kv_cache_append_multi_fp8: pkv_kv_cache_append_multi into uint8 E4M3
+ * pools, each new token quantised as pkv_kv_cache_append_fp8 quantises its
+ * one token; k_new / v_new are [num_seqs][num_queries][num_kv_heads][128] of
+ * new_dtype. num_queries = 1 is pkv_kv_cache_append_fp8.
+ *
+ * pkv_paged_attention_multi_fp8: pkv_paged_attention_multi over E4M3 pools
+ * with per-head scales (values as in pkv_paged_attention_decode_fp8); q is
+ * F16 or BF16 and sets the type the matrix cores compute in (the codes widen
+ * to it exactly). Same shapes, column groups, schedules, workspace and
+ * errors as pkv_paged_attention_multi.
+ *
+ * pkv_paged_attention_decode_grouped_fp8: pkv_paged_attention_decode_grouped
+ * over E4M3 pools, q F16 or BF16: partitions inside a group's shared tokens
+ * are read once per group on the matrix cores; every other partition per
+ * sequence (the FP8 decode walker). Same arguments, limits, workspace and
+ * errors as pkv_paged_attention_decode_grouped.
+ */
+PKV_API int pkv_kv_cache_append_multi_fp8(const void* k_new, const void* v_new,
+                                          pkv_dtype new_dtype, void* k_pool, void* v_pool,
+                                          const float* k_scales, const float* v_scales,
+                                          const int32_t* block_tables, int max_blocks_per_seq,
+                                          const int32_t* seq_lens, int num_seqs,
+                                          int num_queries, int num_kv_heads, int head_dim,
+                                          int block_size, int num_blocks, void* stream);
+
+PKV_API int pkv_paged_attention_multi_fp8(void* out, pkv_dtype out_dtype,
+                                          const void* q, pkv_dtype q_dtype,
+                                          const void* k_pool, const void* v_pool,
+                                          const float* k_scales, const float* v_scales,
+                                          const int32_t* block_tables, int max_blocks_per_seq,
+                                          const int32_t* seq_lens, int max_seq_len,
+                                          int num_seqs, int num_queries, int num_heads,
+                                          int num_kv_heads, int head_dim, int block_size,
+                                          int num_blocks, float scale, int partition_size,
+                                          void* workspace, size_t workspace_bytes,
+                                          int kv_policy, void* stream);
+
+PKV_API int pkv_paged_attention_decode_grouped_fp8(void* out, pkv_dtype out_dtype,
+                                          const void* q, pkv_dtype q_dtype,
+                                          const void* k_pool, const void* v_pool,
+                                          const float* k_scales, const float* v_scales,
+                                          const int32_t* block_tables, int max_blocks_per_seq,
+                                          const int32_t* seq_lens, int max_seq_len,
+                                          int num_seqs, int num_heads, int num_kv_heads,
+                                          int head_dim, int block_size, int num_blocks,
+                                          float scale, int partition_size, int group_size,
+                                          const int32_t* shared_tokens,
+                                          void* workspace, size_t workspace_bytes,
+                                          int kv_policy, void* stream);
 
 /* Static, NUL-terminated description of a pkv_status value. */
 PKV_API const char* pkv_status_string(int status);

@@ -11,6 +11,14 @@
  *                    transfer of known size, used to scale hardware traffic
  *                    counters (bytes fetched / written per dispatch) into
  *                    bytes.
+ *   pkv_probe_gather reads exactly the K/V rows a decode launch reads --
+ *                    every valid token of every (sequence, kv head), through
+ *                    the block tables, tile by tile -- with the same
+ *                    non-temporal 16-byte loads and the same equal split of
+ *                    32-token units over persistent waves, and computes
+ *                    nothing: the read ceiling of the paged access pattern
+ *                    itself (scattered bs x row-byte tiles, [summary]
+ *                    section "커널 비용과 블록 크기" on block size and access).
  *
  * Conventions are those of pkv.h: device pointers owned by the caller, work
  * enqueued on `stream` (a hipStream_t, NULL = null stream), a pkv_status
@@ -44,6 +52,24 @@ PKV_API size_t pkv_probe_read_sink_words(size_t bytes);
  * (16-byte aligned, not overlapping) with 16-byte loads and stores.
  */
 PKV_API int pkv_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/*
+ * Read every K and V row that decode attention over these tables reads:
+ * tokens 0 .. seq_lens[i]-1 of every kv head of every sequence, row t of
+ * sequence i and head g at slot t % block_size of block
+ * block_tables[i][t / block_size] (entries outside [0, num_blocks) are
+ * clamped), in pools laid out as in pkv.h with rows of row_bytes bytes
+ * (128 or 256: head_dim times the element size). `waves` persistent waves
+ * each take an equal share of the 32-token units of all (sequence, kv head)
+ * pairs; each round a wave issues loads_per_round (2, 4 or 8) wave-wide
+ * 16-byte loads of K and as many of V. One uint32 per wave goes to sink
+ * (`waves` words), the XOR of what it read. Lengths must not exceed
+ * max_blocks_per_seq * block_size.
+ */
+PKV_API int pkv_probe_gather(const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                             int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs,
+                             int num_kv_heads, int row_bytes, int block_size, int num_blocks,
+                             int waves, int loads_per_round, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,5 +21,6 @@ from .fp8 import (  # noqa: F401
     encode as fp8_encode,
     quantize as fp8_quantize,
     pool_after_append_fp8,
+    pool_after_append_multi_fp8,
     dequantize_pool as fp8_dequantize_pool,
 )

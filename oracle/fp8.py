@@ -107,6 +107,30 @@ def pool_after_append_fp8(k_pool, v_pool, k_new, v_new, k_scales, v_scales, bloc
     return k_out, v_out
 
 
+def pool_after_append_multi_fp8(k_pool, v_pool, k_new, v_new, k_scales, v_scales, block_tables,
+                                seq_lens, block_size):
+    """uint8 pools after each sequence stores nq new tokens, quantised per kv
+    head: k_new, v_new [B][nq][H_kv][D]; token j of a sequence of (new)
+    length L goes to position L - nq + j (skipped when negative), i.e. slot
+    (L - nq + j) % block_size of block table[(L - nq + j) // block_size].
+    Returns copies."""
+    k_out = k_pool.copy()
+    v_out = v_pool.copy()
+    nq = k_new.shape[1]
+    num_kv_heads = k_pool.shape[1]
+    for i in range(len(seq_lens)):
+        n = int(seq_lens[i])
+        for j in range(nq):
+            pos = n - nq + j
+            if n <= 0 or pos < 0:
+                continue
+            physical = int(block_tables[i][pos // block_size])
+            for g in range(num_kv_heads):
+                k_out[physical, g, pos % block_size, :] = quantize(k_new[i][j][g], k_scales[g])
+                v_out[physical, g, pos % block_size, :] = quantize(v_new[i][j][g], v_scales[g])
+    return k_out, v_out
+
+
 def dequantize_pool(pool, scales):
     """float64 values of a uint8 pool [num_blocks][Hkv][bs][D] with per-head scales."""
     return decode(pool) * np.asarray(scales, dtype=np.float64)[None, :, None, None]

@@ -10,6 +10,9 @@ _API = (
     "kv_cache_append",
     "kv_cache_append_fp8",
     "kv_cache_append_multi",
+    "kv_cache_append_multi_fp8",
+    "paged_attention_multi_fp8",
+    "paged_attention_decode_grouped_fp8",
     "paged_attention_multi",
     "paged_attention_decode_fp8",
     "paged_attention_decode_grouped",
@@ -23,6 +26,7 @@ _API = (
     "status_string",
     "probe_read",
     "probe_copy",
+    "probe_gather",
     "library",
     "DTYPE_CODES",
     "PARTITION_BALANCED",

@@ -62,6 +62,15 @@ def library() -> ctypes.CDLL:
     lib.pkv_paged_attention_decode_fp8.restype = I
     lib.pkv_kv_cache_append_multi.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, I, P]
     lib.pkv_kv_cache_append_multi.restype = I
+    lib.pkv_kv_cache_append_multi_fp8.argtypes = [P, P, I, P, P, P, P, P, I, P, I, I, I, I, I, I,
+                                                  P]
+    lib.pkv_kv_cache_append_multi_fp8.restype = I
+    lib.pkv_paged_attention_multi_fp8.argtypes = [P, I, P, I, P, P, P, P, P, I, P, I, I, I, I, I,
+                                                  I, I, I, F, I, P, Z, I, P]
+    lib.pkv_paged_attention_multi_fp8.restype = I
+    lib.pkv_paged_attention_decode_grouped_fp8.argtypes = [P, I, P, I, P, P, P, P, P, I, P, I, I,
+                                                           I, I, I, I, I, F, I, I, P, P, Z, I, P]
+    lib.pkv_paged_attention_decode_grouped_fp8.restype = I
     lib.pkv_paged_attention_multi.argtypes = [P, I, P, P, P, P, I, P, I, I, I, I, I, I, I, I, F,
                                               I, P, Z, I, I, P]
     lib.pkv_paged_attention_multi.restype = I
@@ -78,6 +87,8 @@ def library() -> ctypes.CDLL:
     lib.pkv_probe_read.restype = I
     lib.pkv_probe_read_sink_words.argtypes = [Z]
     lib.pkv_probe_read_sink_words.restype = Z
+    lib.pkv_probe_gather.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, P, P]
+    lib.pkv_probe_gather.restype = I
     lib.pkv_probe_copy.argtypes = [P, P, Z, P]
     lib.pkv_probe_copy.restype = I
     _lib = lib
@@ -277,10 +288,13 @@ def paged_attention_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, 
         int(partition_size)))
 
 
+WALKER_VECTOR = 0x40        # PKV_WALKER_VECTOR
+
+
 def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, max_seq_len, scale,
                            partition_size=PARTITION_BALANCED, workspace=None,
                            stream=None, kv_reuse: bool = False,
-                           stage: str = "both") -> torch.Tensor:
+                           stage: str = "both", walker: str = "auto") -> torch.Tensor:
     """pkv_paged_attention_decode into `out` [B][H][D] (float32, float16 or
     bfloat16). partition_size: 0 (one pass per sequence), a multiple of 64
     (fixed partitions) or PARTITION_BALANCED (the default). `workspace` (a
@@ -290,7 +304,11 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, max_s
     stage: "both" (default), "walk" (only the walk over the blocks; partial
     results stay in `workspace`) or "merge" (only the merge, after a "walk"
     call with the same arguments and workspace): PKV_STAGE_WALK /
-    PKV_STAGE_MERGE."""
+    PKV_STAGE_MERGE. walker: "auto" (default) or "vector" (PKV_WALKER_VECTOR:
+    grouped query heads on the vector units instead of the matrix cores, for
+    comparison)."""
+    if walker not in ("auto", "vector"):
+        raise ValueError("walker must be 'auto' or 'vector'")
     nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
     if code == FP8_E4M3:
         raise TypeError("uint8 (FP8) pools are read by paged_attention_decode_fp8")
@@ -310,7 +328,8 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, seq_lens, max_s
         _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32),
         block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len),
         b, h, hkv, d, bs, nb, float(scale), int(partition_size), ws_ptr, ws_bytes, code,
-        _policy(kv_reuse, stage), _stream(stream)))
+        _policy(kv_reuse, stage) | (WALKER_VECTOR if walker == "vector" else 0),
+        _stream(stream)))
     return out
 
 
@@ -357,6 +376,23 @@ def probe_read(src: torch.Tensor, sink: torch.Tensor | None = None, stream=None)
     _check("pkv_probe_read", library().pkv_probe_read(
         _dev(src, "src"), nbytes, _dev(sink, "sink", torch.int32), _stream(stream)))
     return sink
+
+
+def probe_gather(k_pool, v_pool, block_tables, seq_lens, waves, loads_per_round, sink,
+                 stream=None) -> None:
+    """pkv_probe_gather: read every K/V row decode attention over these tables
+    reads (no compute), with `waves` persistent waves issuing loads_per_round
+    wave loads of K and of V per round; sink is an int32 device tensor of at
+    least `waves` words."""
+    nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
+    b = block_tables.shape[0]
+    if sink.numel() < waves:
+        raise ValueError(f"sink must hold {waves} words")
+    _check("pkv_probe_gather", library().pkv_probe_gather(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens", torch.int32), b, hkv, d * k_pool.element_size(), bs, nb,
+        int(waves), int(loads_per_round), _dev(sink, "sink", torch.int32), _stream(stream)))
 
 
 def probe_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
@@ -484,4 +520,99 @@ def paged_attention_multi(out, q, k_pool, v_pool, block_tables, seq_lens, max_se
         block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len),
         b, nq, h, hkv, d, bs, nb, float(scale), int(partition_size), ws_ptr, ws_bytes, code,
         _policy(kv_reuse, stage), _stream(stream)))
+    return out
+
+
+def kv_cache_append_multi_fp8(k_new, v_new, k_pool, v_pool, k_scales, v_scales, block_tables,
+                              seq_lens, stream=None) -> None:
+    """pkv_kv_cache_append_multi_fp8: k_new/v_new [B][nq][Hkv][D] (float32,
+    float16 or bfloat16) quantised into uint8 E4M3 pools; new token j of
+    sequence i goes to position seq_lens[i] - nq + j."""
+    nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
+    if code != FP8_E4M3:
+        raise TypeError("kv_cache_append_multi_fp8 needs uint8 (FP8) pools")
+    b = block_tables.shape[0]
+    if k_new.dim() != 4 or k_new.shape != v_new.shape or k_new.shape[0] != b or \
+            k_new.shape[2:] != (hkv, d) or k_new.dtype != v_new.dtype:
+        raise ValueError(f"k_new/v_new must be [{b}][nq][{hkv}][{d}] of one dtype")
+    if k_new.dtype not in DTYPE_CODES:
+        raise TypeError(f"unsupported k_new dtype {k_new.dtype}")
+    if seq_lens.shape != (b,):
+        raise ValueError("seq_lens must be [num_seqs]")
+    ks, vs = _scales(k_scales, v_scales, hkv)
+    _check("pkv_kv_cache_append_multi_fp8", library().pkv_kv_cache_append_multi_fp8(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), DTYPE_CODES[k_new.dtype],
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), ks, vs,
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens", torch.int32), b, k_new.shape[1], hkv, d, bs, nb,
+        _stream(stream)))
+
+
+def paged_attention_multi_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, seq_lens,
+                              max_seq_len, scale, partition_size=PARTITION_BALANCED,
+                              workspace=None, stream=None, kv_reuse: bool = False,
+                              stage: str = "both") -> torch.Tensor:
+    """pkv_paged_attention_multi_fp8 into `out` [B][nq][H][D]: the
+    multi-query call over uint8 E4M3 pools with per-head float32 scales; q is
+    float16 or bfloat16."""
+    nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
+    if code != FP8_E4M3:
+        raise TypeError("paged_attention_multi_fp8 needs uint8 (FP8) pools")
+    if q.dim() != 4 or q.shape[3] != d or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q must be [num_seqs][nq][num_heads][head_dim], float16 or bfloat16")
+    b, nq, h = q.shape[0], q.shape[1], q.shape[2]
+    if out.shape != q.shape or out.dtype not in DTYPE_CODES:
+        raise ValueError("out must be [num_seqs][nq][num_heads][head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or seq_lens.shape != (b,):
+        raise ValueError("block_tables must be [num_seqs][max_blocks], seq_lens [num_seqs]")
+    ks, vs = _scales(k_scales, v_scales, hkv)
+    need = paged_attention_workspace_size(b, h * nq, hkv, d, max_seq_len, partition_size)
+    workspace = _workspace(need, workspace, q.device, stream, stage)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("pkv_paged_attention_multi_fp8", library().pkv_paged_attention_multi_fp8(
+        _dev(out, "out"), DTYPE_CODES[out.dtype], _dev(q, "q"), DTYPE_CODES[q.dtype],
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), ks, vs,
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), b, nq, h, hkv, d, bs, nb,
+        float(scale), int(partition_size), ws_ptr, ws_bytes, _policy(kv_reuse, stage),
+        _stream(stream)))
+    return out
+
+
+def paged_attention_decode_grouped_fp8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables,
+                                       seq_lens, max_seq_len, scale, group_size, shared_tokens,
+                                       partition_size=512, workspace=None, stream=None,
+                                       kv_reuse: bool = False, stage: str = "both") -> torch.Tensor:
+    """pkv_paged_attention_decode_grouped_fp8 into `out` [B][H][D]: the
+    sampling-group call over uint8 E4M3 pools with per-head float32 scales; q
+    is float16 or bfloat16."""
+    nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
+    if code != FP8_E4M3:
+        raise TypeError("paged_attention_decode_grouped_fp8 needs uint8 (FP8) pools")
+    if q.dim() != 3 or q.shape[2] != d or q.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("q must be [num_seqs][num_heads][head_dim], float16 or bfloat16")
+    b, h = q.shape[0], q.shape[1]
+    if out.shape != q.shape or out.dtype not in DTYPE_CODES:
+        raise ValueError("out must be [num_seqs][num_heads][head_dim]")
+    if group_size <= 0 or b % group_size != 0:
+        raise ValueError("num_seqs must be a multiple of group_size")
+    if shared_tokens.shape != (b // group_size,):
+        raise ValueError("shared_tokens must be [num_seqs // group_size]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != b or seq_lens.shape != (b,):
+        raise ValueError("block_tables must be [num_seqs][max_blocks], seq_lens [num_seqs]")
+    ks, vs = _scales(k_scales, v_scales, hkv)
+    need = paged_attention_workspace_size(b, h, hkv, d, max_seq_len, partition_size)
+    workspace = _workspace(need, workspace, q.device, stream, stage)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("pkv_paged_attention_decode_grouped_fp8",
+           library().pkv_paged_attention_decode_grouped_fp8(
+               _dev(out, "out"), DTYPE_CODES[out.dtype], _dev(q, "q"), DTYPE_CODES[q.dtype],
+               _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), ks, vs,
+               _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+               _dev(seq_lens, "seq_lens", torch.int32), int(max_seq_len), b, h, hkv, d, bs, nb,
+               float(scale), int(partition_size), int(group_size),
+               _dev(shared_tokens, "shared_tokens", torch.int32), ws_ptr, ws_bytes,
+               _policy(kv_reuse, stage), _stream(stream)))
     return out

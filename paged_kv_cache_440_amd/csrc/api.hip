@@ -132,10 +132,14 @@ int prepare_attention(pkv::AttnParams& a, void* out, int out_dtype, const void* 
     if ((long long)num_seqs * max_blocks_per_seq > INT32_MAX) return PKV_ERR_INVALID;
     if ((long long)num_seqs * num_queries * num_heads * head_dim > INT32_MAX) return PKV_ERR_INVALID;
     const int cols = group * num_queries;       // output rows per (sequence, kv head)
-
-    const bool balanced = partition_size == PKV_PARTITION_BALANCED;
-    const long long parts = balanced ? 1 : parts_for(max_seq_len, partition_size);
-    long long items = parts * num_seqs * num_kv_heads;
+    // more than 16 columns (chunked prefill) run as 16-column tiles; there the
+    // balanced schedule is a single pass per tile: the tiles fill the GPU, and
+    // a partial record per query token would cost more than it evens out
+    const int tiles = (cols + 15) / 16;
+    const bool balanced = partition_size == PKV_PARTITION_BALANCED && tiles == 1;
+    const long long parts = partition_size == PKV_PARTITION_BALANCED
+                                ? 1 : parts_for(max_seq_len, partition_size);
+    long long items = parts * num_seqs * num_kv_heads * tiles;
     if (items > INT32_MAX - 64) return PKV_ERR_INVALID;
     const size_t need =
         balanced ? balanced_workspace_bytes(cols, head_dim)
@@ -169,6 +173,7 @@ int prepare_attention(pkv::AttnParams& a, void* out, int out_dtype, const void* 
     a.num_blocks = num_blocks;
     a.scale = scale;
     a.part_tokens = (!balanced && parts > 1) ? partition_size : 0;
+    a.col_tiles = tiles;
     a.max_parts = (int)parts;
     a.max_tokens = max_seq_len;
     a.num_items = (int)items;
@@ -284,6 +289,19 @@ int pkv_kv_cache_append_fp8(const void* k_new, const void* v_new, pkv_dtype new_
                             int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs,
                             int num_kv_heads, int head_dim, int block_size, int num_blocks,
                             void* stream) {
+    return pkv_kv_cache_append_multi_fp8(k_new, v_new, new_dtype, k_pool, v_pool, k_scales,
+                                         v_scales, block_tables, max_blocks_per_seq, seq_lens,
+                                         num_seqs, 1, num_kv_heads, head_dim, block_size,
+                                         num_blocks, stream);
+}
+
+int pkv_kv_cache_append_multi_fp8(const void* k_new, const void* v_new, pkv_dtype new_dtype,
+                                  void* k_pool, void* v_pool, const float* k_scales,
+                                  const float* v_scales, const int32_t* block_tables,
+                                  int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs,
+                                  int num_queries, int num_kv_heads, int head_dim,
+                                  int block_size, int num_blocks, void* stream) {
+    if (num_queries <= 0 || (long long)num_seqs * num_queries > INT32_MAX) return PKV_ERR_INVALID;
     if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
         num_blocks <= 0 || max_blocks_per_seq <= 0 || !valid_dtype(new_dtype))
         return PKV_ERR_INVALID;
@@ -311,7 +329,7 @@ int pkv_kv_cache_append_fp8(const void* k_new, const void* v_new, pkv_dtype new_
     a.head_dim = head_dim;
     a.log2_bs = block_log2(block_size);
     a.num_blocks = num_blocks;
-    a.num_queries = 1;
+    a.num_queries = num_queries;
     a.err = pkv::error_word();
     return pkv::launch_append_fp8(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
@@ -387,8 +405,11 @@ size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, int num_k
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
         head_dim <= 0 || max_seq_len < 0 || partition_size < PKV_PARTITION_BALANCED)
         return 0;
-    if (partition_size == PKV_PARTITION_BALANCED)
-        return num_seqs > 0 ? balanced_workspace_bytes(num_heads / num_kv_heads, head_dim) : 0;
+    if (partition_size == PKV_PARTITION_BALANCED) {
+        // more than 16 columns per kv head: a single pass per 16-column tile
+        const int cols = num_heads / num_kv_heads;
+        return num_seqs > 0 && cols <= 16 ? balanced_workspace_bytes(cols, head_dim) : 0;
+    }
     return workspace_bytes_for((long long)num_seqs * num_heads, head_dim,
                                parts_for(max_seq_len, partition_size));
 }
@@ -403,6 +424,11 @@ int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
                                void* stream) {
     if (!valid_pool_dtype(dtype)) return PKV_ERR_INVALID;
     if (dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;   // see pkv_paged_attention_decode_fp8
+    if (kv_policy & ~(PKV_KV_REUSE | PKV_STAGE_WALK | PKV_STAGE_MERGE | PKV_WALKER_VECTOR))
+        return PKV_ERR_INVALID;
+    const bool force_vector = (kv_policy & PKV_WALKER_VECTOR) != 0;
+    kv_policy &= ~PKV_WALKER_VECTOR;
+    if (force_vector && (kv_policy & PKV_KV_REUSE)) return PKV_ERR_UNSUPPORTED;
     pkv::AttnParams a{};
     const int st = prepare_attention(a, out, out_dtype, q, k_pool, v_pool, block_tables,
                                      max_blocks_per_seq, seq_lens, max_seq_len, num_seqs, num_heads,
@@ -411,6 +437,7 @@ int pkv_paged_attention_decode(void* out, pkv_dtype out_dtype, const void* q,
     if (st != PKV_OK || num_seqs == 0) return st;
     a.dtype = dtype;
     a.q_dtype = dtype;
+    a.force_vector = force_vector ? 1 : 0;
     return pkv::launch_paged_attention(a, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -430,8 +457,7 @@ int pkv_paged_attention_multi(void* out, pkv_dtype out_dtype, const void* q,
                                      partition_size, workspace, workspace_bytes, kv_policy,
                                      num_queries);
     if (st != PKV_OK) return st;
-    if ((dtype != PKV_F16 && dtype != PKV_BF16) || head_dim != 128 || num_queries * a.group > 16)
-        return PKV_ERR_UNSUPPORTED;
+    if ((dtype != PKV_F16 && dtype != PKV_BF16) || head_dim != 128) return PKV_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PKV_OK;
     a.dtype = dtype;
     a.q_dtype = dtype;
@@ -464,6 +490,67 @@ int pkv_paged_attention_decode_grouped(void* out, pkv_dtype out_dtype, const voi
     if (!shared_tokens) return PKV_ERR_INVALID;
     a.dtype = dtype;
     a.q_dtype = dtype;
+    a.group_size = group_size;
+    a.shared_tokens = shared_tokens;
+    return pkv::launch_paged_attention_grouped(a, (hipStream_t)stream) == hipSuccess ? PKV_OK
+                                                                                     : PKV_ERR_HIP;
+}
+
+int pkv_paged_attention_multi_fp8(void* out, pkv_dtype out_dtype, const void* q,
+                                  pkv_dtype q_dtype, const void* k_pool, const void* v_pool,
+                                  const float* k_scales, const float* v_scales,
+                                  const int32_t* block_tables, int max_blocks_per_seq,
+                                  const int32_t* seq_lens, int max_seq_len, int num_seqs,
+                                  int num_queries, int num_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int num_blocks, float scale,
+                                  int partition_size, void* workspace, size_t workspace_bytes,
+                                  int kv_policy, void* stream) {
+    if (!valid_dtype(q_dtype) || num_queries <= 0) return PKV_ERR_INVALID;
+    pkv::AttnParams a{};
+    const int st = prepare_attention(a, out, out_dtype, q, k_pool, v_pool, block_tables,
+                                     max_blocks_per_seq, seq_lens, max_seq_len, num_seqs, num_heads,
+                                     num_kv_heads, head_dim, block_size, num_blocks, scale,
+                                     partition_size, workspace, workspace_bytes, kv_policy,
+                                     num_queries);
+    if (st != PKV_OK) return st;
+    if (q_dtype == PKV_F32 || head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PKV_OK;
+    if (!k_scales || !v_scales) return PKV_ERR_INVALID;
+    a.dtype = PKV_FP8_E4M3;
+    a.q_dtype = q_dtype;
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    return pkv::launch_paged_attention_multi(a, (hipStream_t)stream) == hipSuccess ? PKV_OK
+                                                                                   : PKV_ERR_HIP;
+}
+
+int pkv_paged_attention_decode_grouped_fp8(void* out, pkv_dtype out_dtype, const void* q,
+                                           pkv_dtype q_dtype, const void* k_pool,
+                                           const void* v_pool, const float* k_scales,
+                                           const float* v_scales, const int32_t* block_tables,
+                                           int max_blocks_per_seq, const int32_t* seq_lens,
+                                           int max_seq_len, int num_seqs, int num_heads,
+                                           int num_kv_heads, int head_dim, int block_size,
+                                           int num_blocks, float scale, int partition_size,
+                                           int group_size, const int32_t* shared_tokens,
+                                           void* workspace, size_t workspace_bytes, int kv_policy,
+                                           void* stream) {
+    if (!valid_dtype(q_dtype) || group_size <= 0 || partition_size <= 0) return PKV_ERR_INVALID;
+    pkv::AttnParams a{};
+    const int st = prepare_attention(a, out, out_dtype, q, k_pool, v_pool, block_tables,
+                                     max_blocks_per_seq, seq_lens, max_seq_len, num_seqs, num_heads,
+                                     num_kv_heads, head_dim, block_size, num_blocks, scale,
+                                     partition_size, workspace, workspace_bytes, kv_policy);
+    if (st != PKV_OK) return st;
+    if (q_dtype == PKV_F32 || head_dim != 128 || (long long)group_size * a.group > 16)
+        return PKV_ERR_UNSUPPORTED;
+    if (num_seqs % group_size != 0) return PKV_ERR_INVALID;
+    if (num_seqs == 0) return PKV_OK;
+    if (!shared_tokens || !k_scales || !v_scales) return PKV_ERR_INVALID;
+    a.dtype = PKV_FP8_E4M3;
+    a.q_dtype = q_dtype;
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
     a.group_size = group_size;
     a.shared_tokens = shared_tokens;
     return pkv::launch_paged_attention_grouped(a, (hipStream_t)stream) == hipSuccess ? PKV_OK

@@ -110,8 +110,9 @@ __device__ __forceinline__ void load8_f32(const char* p, int new_dtype, float (&
     }
 }
 
-// One thread per 8 elements of one (sequence, kv head) row of K or of V:
-// 8 inputs -> 8 codes (one 8-byte store).
+// One thread per 8 elements of one (sequence, new token, kv head) row of K
+// or of V: 8 inputs -> 8 codes (one 8-byte store). New token j of a sequence
+// of (new) length L goes to position L - nq + j; positions below 0 are skipped.
 template <int NEW_BYTES>
 __global__ __launch_bounds__(kThreads)
 void append_fp8_kernel(const AppendFp8Params a, long long total) {
@@ -122,11 +123,13 @@ void append_fp8_kernel(const AppendFp8Params a, long long total) {
     long long r = t / groups;
     const int g = (int)(r % a.num_kv_heads);
     r /= a.num_kv_heads;
+    const int j = (int)(r % a.num_queries);
+    r /= a.num_queries;
     const int seq = (int)(r % a.num_seqs);
     const int which = (int)(r / a.num_seqs);      // 0: K, 1: V
     const int L = a.seq_lens[seq];
-    if (L <= 0) return;
-    const int pos = L - 1;
+    const int pos = L - a.num_queries + j;
+    if (L <= 0 || pos < 0) return;
     const int blk = pos >> a.log2_bs;
     if (blk >= a.max_blocks) {
         report_if(a.err, grp == 0, PKV_ERRBIT_APPEND);
@@ -140,7 +143,8 @@ void append_fp8_kernel(const AppendFp8Params a, long long total) {
     const int slot = pos & ((1 << a.log2_bs) - 1);
     const float scale = (which ? a.v_scales : a.k_scales)[g];
     const char* src = reinterpret_cast<const char*>(which ? a.v_new : a.k_new) +
-                      (((size_t)seq * a.num_kv_heads + g) * a.head_dim + (size_t)grp * 8) * NEW_BYTES;
+                      ((((size_t)seq * a.num_queries + j) * a.num_kv_heads + g) * a.head_dim +
+                       (size_t)grp * 8) * NEW_BYTES;
     float x[8];
     load8_f32<NEW_BYTES>(src, a.new_dtype, x);
     uint32_t lo = 0, hi = 0;
@@ -199,7 +203,7 @@ hipError_t launch_append(const AppendParams& a, hipStream_t stream) {
 }
 
 hipError_t launch_append_fp8(const AppendFp8Params& a, hipStream_t stream) {
-    const long long total = 2LL * a.num_seqs * a.num_kv_heads * (a.head_dim / 8);
+    const long long total = 2LL * a.num_seqs * a.num_queries * a.num_kv_heads * (a.head_dim / 8);
     if (total == 0) return hipSuccess;
     const long long blocks = (total + kThreads - 1) / kThreads;
     if (a.new_dtype == PKV_F32)

@@ -53,13 +53,19 @@ __device__ __forceinline__ bool in_shared_part(const AttnParams& a, int seq, int
 }
 
 // ---------------------------------------------------------------------------
-// Single pass and fixed partitions: one wave per (segment, partition).
-// Partial rows: ws_acc[((seq * H + h) * max_parts + part)], the same for ws_ml.
+// Single pass and fixed partitions: one wave per (segment, 16-column tile,
+// partition); a segment has one tile unless it has more than 16 columns
+// (several new tokens per sequence on the matrix cores). Partial rows:
+// ws_acc[((seq * Hkv + g) * cols + c) * max_parts + part] for column c, the
+// same for ws_ml.
 template <class Walker>
-__device__ __forceinline__ void decode_partition(const AttnParams& a, int item) {
+__device__ __forceinline__ void decode_partition(const AttnParams& a, int item_in) {
     constexpr int D = Walker::D, G = Walker::G;
     const int lane = threadIdx.x & 63;
-    if (item >= a.num_items) return;
+    if (item_in >= a.num_items) return;
+    // the tiles of one partition are neighbours: they read the same blocks
+    const int tile = item_in % a.col_tiles;
+    const int item = item_in / a.col_tiles;
     int g, seq, part;
     if constexpr (Walker::kStream) {
         // the kv heads of one sequence side by side: their tiles are neighbours
@@ -81,25 +87,34 @@ __device__ __forceinline__ void decode_partition(const AttnParams& a, int item) 
               PKV_ERRBIT_LENGTH);
     const int L = clamp_len(a, raw_len);
     if (L == 0) {                                   // padding row: zero output
-        if (part == 0) write_zero_rows<D>(a, seq, g, lane);
+        if (part == 0 && tile == 0) write_zero_rows<D>(a, seq, g, lane);
         return;
     }
-    const int part_len = a.part_tokens > 0 ? a.part_tokens : L;
-    const int nparts = (L + part_len - 1) / part_len;
+    // the tokens this tile's columns see (L unless several tiles)
+    const int reach = a.col_tiles > 1 ? tile_reach(a, L, tile) : L;
+    if (reach <= 0) {                               // every column before the start
+        const int c0 = 16 * tile, cols = a.num_queries * G;
+        if (part == 0) write_zero_cols<D>(a, seq, g, c0, c0 + 16 < cols ? c0 + 16 : cols, lane);
+        return;
+    }
+    const int part_len = a.part_tokens > 0 ? a.part_tokens : reach;
+    const int nparts = (reach + part_len - 1) / part_len;
     if (part >= nparts) return;
     if (a.shared_tokens != nullptr && a.part_tokens > 0 && in_shared_part(a, seq, part, L)) return;
     const int t_begin = part * part_len;
-    const int t_stop = (t_begin + part_len < L) ? t_begin + part_len : L;
+    const int t_stop = (t_begin + part_len < reach) ? t_begin + part_len : reach;
 
     Walker st;
     st.init(lane);
-    st.begin(a, seq, g, L);
+    st.begin(a, seq, g, L, tile);
     st.walk(t_begin, t_stop, a.scale * kLog2e);
     if (nparts == 1) {
         st.write_final(a, seq, g);
     } else {
         const int cols = a.num_queries * G;
-        const size_t row0 = ((size_t)seq * a.num_kv_heads * cols + (size_t)g * cols) * a.max_parts + part;
+        const size_t row0 =
+            ((size_t)seq * a.num_kv_heads * cols + (size_t)g * cols + 16 * (size_t)tile) *
+                a.max_parts + part;
         st.write_partial(a, row0, (size_t)a.max_parts);
     }
 }
@@ -230,7 +245,9 @@ void lse_reduce_kernel(const AttnParams a) {
     const int g = (item / cols) % a.num_kv_heads;
     const int n = item % cols;
     const int L = clamp_len(a, a.seq_lens[seq]);
-    const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
+    // partitions of the tokens column n's tile reaches, as the walk cut them
+    const int reach = a.col_tiles > 1 ? tile_reach(a, L, n / 16) : L;
+    const int nparts = reach > 0 ? (reach + a.part_tokens - 1) / a.part_tokens : 0;
     if (nparts <= 1) return;
     const size_t prow0 = (size_t)item * a.max_parts;
     fold_records<D>(a, nparts, [&](int p) { return prow0 + p; }, out_row(a, seq, g, n));
@@ -468,23 +485,36 @@ using DecodeWalker = std::conditional_t<S::bytes == 2 && D == 128 && (G == 4 || 
 
 template <typename S, int D, int G, bool STREAM>
 hipError_t launch_typed(const AttnParams& a, hipStream_t stream) {
+    using Vec = VecWalker<S, D, G, STREAM>;
+    if constexpr (STREAM && !std::is_same_v<DecodeWalker<S, D, G, STREAM>, Vec>) {
+        // PKV_WALKER_VECTOR: grouped heads on the vector units, for comparison
+        if (a.force_vector) return launch_walker<Vec>(a, stream);
+    }
     return launch_walker<DecodeWalker<S, D, G, STREAM>>(a, stream);
 }
+
+// The decode walker for FP8 pools under fixed partitions: the vector walker
+// for one query head per kv head (q in Q), the matrix cores for more.
+template <typename Q, int G, bool STREAM>
+using Fp8DecodeWalker = std::conditional_t<G == 1, Fp8VecWalker<Q, 1, STREAM, 4>,
+                                           MfmaWalker<Q, G, STREAM, true>>;
 
 // Sampling groups: one launch of the shared partitions on the matrix cores
 // (one wave per group, kv head and partition) and every sequence's own
 // partitions, then the reduce over both. (Measured on MI355X: one launch
 // beats two back-to-back launches by 11% on the 32 x 8 sampling layer.)
-template <typename S, int G, bool STREAM>
+// FP8: E4M3 pools, S is q's type.
+template <typename S, int G, bool STREAM, bool FP8>
 hipError_t launch_grouped_typed(const AttnParams& a, hipStream_t stream) {
-    if (a.max_parts <= 1) return launch_partitioned<DecodeWalker<S, 128, G, STREAM>>(a, stream);
+    using SeqWalker = std::conditional_t<FP8, Fp8DecodeWalker<S, G, STREAM>,
+                                         DecodeWalker<S, 128, G, STREAM>>;
+    if (a.max_parts <= 1) return launch_partitioned<SeqWalker>(a, stream);
     const long long group_items =
         (long long)(a.num_seqs / a.group_size) * a.num_kv_heads * a.max_parts;
     const long long total = group_items + a.num_items;
     if (total > INT32_MAX) return hipErrorInvalidValue;
     if (stage_walks(a.stage)) {
-        hipLaunchKernelGGL((paged_decode_grouped_kernel<MfmaWalker<S, G, STREAM>,
-                                                        DecodeWalker<S, 128, G, STREAM>>),
+        hipLaunchKernelGGL((paged_decode_grouped_kernel<MfmaWalker<S, G, STREAM, FP8>, SeqWalker>),
                            dim3((unsigned)((total + kWaves - 1) / kWaves)), dim3(64 * kWaves), 0,
                            stream, a, (int)group_items);
         const hipError_t err = hipGetLastError();
@@ -496,21 +526,21 @@ hipError_t launch_grouped_typed(const AttnParams& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename S, bool STREAM>
+template <typename S, bool STREAM, bool FP8>
 hipError_t launch_grouped_group(const AttnParams& a, hipStream_t stream) {
     switch (a.group) {
-        case 1: return launch_grouped_typed<S, 1, STREAM>(a, stream);
-        case 2: return launch_grouped_typed<S, 2, STREAM>(a, stream);
-        case 4: return launch_grouped_typed<S, 4, STREAM>(a, stream);
-        case 8: return launch_grouped_typed<S, 8, STREAM>(a, stream);
+        case 1: return launch_grouped_typed<S, 1, STREAM, FP8>(a, stream);
+        case 2: return launch_grouped_typed<S, 2, STREAM, FP8>(a, stream);
+        case 4: return launch_grouped_typed<S, 4, STREAM, FP8>(a, stream);
+        case 8: return launch_grouped_typed<S, 8, STREAM, FP8>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename S>
+template <typename S, bool FP8>
 hipError_t launch_grouped_policy(const AttnParams& a, hipStream_t stream) {
-    return a.kv_stream ? launch_grouped_group<S, true>(a, stream)
-                       : launch_grouped_group<S, false>(a, stream);
+    return a.kv_stream ? launch_grouped_group<S, true, FP8>(a, stream)
+                       : launch_grouped_group<S, false, FP8>(a, stream);
 }
 
 template <typename S, int D, bool STREAM>
@@ -570,42 +600,56 @@ hipError_t launch_fp8_policy(const AttnParams& a, hipStream_t stream) {
     return a.kv_stream ? launch_fp8_group<Q, true>(a, stream) : launch_fp8_group<Q, false>(a, stream);
 }
 
-template <typename S, bool STREAM>
+template <typename S, bool STREAM, bool FP8>
 hipError_t launch_multi_group(const AttnParams& a, hipStream_t stream) {
     switch (a.group) {
-        case 1: return launch_walker<MfmaWalker<S, 1, STREAM>>(a, stream);
-        case 2: return launch_walker<MfmaWalker<S, 2, STREAM>>(a, stream);
-        case 4: return launch_walker<MfmaWalker<S, 4, STREAM>>(a, stream);
-        case 8: return launch_walker<MfmaWalker<S, 8, STREAM>>(a, stream);
+        case 1: return launch_walker<MfmaWalker<S, 1, STREAM, FP8>>(a, stream);
+        case 2: return launch_walker<MfmaWalker<S, 2, STREAM, FP8>>(a, stream);
+        case 4: return launch_walker<MfmaWalker<S, 4, STREAM, FP8>>(a, stream);
+        case 8: return launch_walker<MfmaWalker<S, 8, STREAM, FP8>>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename S>
+template <typename S, bool FP8>
 hipError_t launch_multi_policy(const AttnParams& a, hipStream_t stream) {
-    return a.kv_stream ? launch_multi_group<S, true>(a, stream)
-                       : launch_multi_group<S, false>(a, stream);
+    return a.kv_stream ? launch_multi_group<S, true, FP8>(a, stream)
+                       : launch_multi_group<S, false, FP8>(a, stream);
 }
 
 }  // namespace
 
 // Several new tokens per sequence: always the matrix-core walker, whose 16
 // columns hold (new token, query head) pairs with their own causal limits.
+// FP8 pools: E4M3 codes widened to q's type on the way into the matrix cores.
 hipError_t launch_paged_attention_multi(const AttnParams& a, hipStream_t stream) {
-    if (a.head_dim != 128 || a.num_queries * a.group > 16) return hipErrorInvalidValue;
-    switch (a.dtype) {
-        case PKV_F16: return launch_multi_policy<F16>(a, stream);
-        case PKV_BF16: return launch_multi_policy<BF16>(a, stream);
+    if (a.head_dim != 128 || (a.col_tiles > 1 && a.balanced)) return hipErrorInvalidValue;
+    const int t = a.dtype == PKV_FP8_E4M3 ? a.q_dtype : a.dtype;
+    const bool fp8 = a.dtype == PKV_FP8_E4M3;
+    switch (t) {
+        case PKV_F16:
+            return fp8 ? launch_multi_policy<F16, true>(a, stream)
+                       : launch_multi_policy<F16, false>(a, stream);
+        case PKV_BF16:
+            return fp8 ? launch_multi_policy<BF16, true>(a, stream)
+                       : launch_multi_policy<BF16, false>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-// Parallel-sampling groups: 16-bit K/V, head_dim 128, fixed partitions.
+// Parallel-sampling groups: 16-bit K/V or FP8 pools with 16-bit q, head_dim
+// 128, fixed partitions.
 hipError_t launch_paged_attention_grouped(const AttnParams& a, hipStream_t stream) {
     if (a.head_dim != 128 || a.balanced || a.group_size * a.group > 16) return hipErrorInvalidValue;
-    switch (a.dtype) {
-        case PKV_F16: return launch_grouped_policy<F16>(a, stream);
-        case PKV_BF16: return launch_grouped_policy<BF16>(a, stream);
+    const int t = a.dtype == PKV_FP8_E4M3 ? a.q_dtype : a.dtype;
+    const bool fp8 = a.dtype == PKV_FP8_E4M3;
+    switch (t) {
+        case PKV_F16:
+            return fp8 ? launch_grouped_policy<F16, true>(a, stream)
+                       : launch_grouped_policy<F16, false>(a, stream);
+        case PKV_BF16:
+            return fp8 ? launch_grouped_policy<BF16, true>(a, stream)
+                       : launch_grouped_policy<BF16, false>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -60,12 +60,30 @@ __device__ __forceinline__ size_t out_row(const AttnParams& a, int seq, int g, i
            (size_t)g * G + n % G;
 }
 
-// Zero the output rows of every column of segment (seq, g) (padding sequences).
+// Zero the output rows of columns [c0, c1) of segment (seq, g) (padding
+// sequences, and queries before the start of their sequence).
+template <int D>
+__device__ __forceinline__ void write_zero_cols(const AttnParams& a, int seq, int g, int c0,
+                                                int c1, int lane) {
+    for (int idx = lane; idx < (c1 - c0) * D; idx += 64)
+        store_out(a.out, a.out_dtype, out_row(a, seq, g, c0 + idx / D) * D + idx % D, 0.f);
+}
+
+// ... of every column of segment (seq, g).
 template <int D>
 __device__ __forceinline__ void write_zero_rows(const AttnParams& a, int seq, int g, int lane) {
+    write_zero_cols<D>(a, seq, g, 0, a.num_queries * a.group, lane);
+}
+
+// Token positions the columns of 16-column tile `tile` of a segment of
+// length L may see: 0 .. reach - 1, where reach - 1 is the causal limit of
+// the tile's last column (new token j sits at L - nq + j and sees up to
+// itself). L for a segment of at most 16 columns; 0 or less when every
+// column of the tile is a query before the start of its sequence.
+__device__ __forceinline__ int tile_reach(const AttnParams& a, int L, int tile) {
     const int cols = a.num_queries * a.group;
-    for (int idx = lane; idx < cols * D; idx += 64)
-        store_out(a.out, a.out_dtype, out_row(a, seq, g, idx / D) * D + idx % D, 0.f);
+    const int last = 16 * tile + 15 < cols ? 16 * tile + 15 : cols - 1;
+    return L - a.num_queries + last / a.group + 1;
 }
 
 }  // namespace

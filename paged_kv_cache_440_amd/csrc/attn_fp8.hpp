@@ -25,23 +25,6 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
     f[3] = hi[1];
 }
 
-// Codes H*2, H*2 + 1 (bytes) of w as two packed 16-bit values of type S, in
-// one gfx950 conversion (scale 1; every E4M3 value is exact in fp16 and bf16).
-template <typename S, bool H>
-__device__ __forceinline__ uint32_t fp8_pair(uint32_t w);
-template <> __device__ __forceinline__ uint32_t fp8_pair<F16, false>(uint32_t w) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, false));
-}
-template <> __device__ __forceinline__ uint32_t fp8_pair<F16, true>(uint32_t w) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, true));
-}
-template <> __device__ __forceinline__ uint32_t fp8_pair<BF16, false>(uint32_t w) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false));
-}
-template <> __device__ __forceinline__ uint32_t fp8_pair<BF16, true>(uint32_t w) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true));
-}
-
 // q elements [first, first + n) of one row as float32
 template <typename Q>
 __device__ __forceinline__ float q_elem(const char* row, int i);
@@ -95,7 +78,7 @@ struct Fp8VecWalker {
         piece = lane_id % LPT;
     }
 
-    __device__ __forceinline__ void begin(const AttnParams& a, int seq, int g, int L) {
+    __device__ __forceinline__ void begin(const AttnParams& a, int seq, int g, int L, int = 0) {
         log2_bs = a.log2_bs;
         bs_mask = (1 << a.log2_bs) - 1;
         nblk_valid = (L + bs_mask) >> a.log2_bs;
@@ -303,256 +286,11 @@ struct Fp8VecWalker {
 };
 
 // ---------------------------------------------------------------------------
-// Matrix-core walker (2, 4 or 8 query heads per kv head, q in fp16 or bf16).
-// Same contractions and layouts as MfmaWalker (attn_mfma.hpp), on the matrix
-// cores of q's own type: the codes are widened to that type (exact: every
-// E4M3 value is an fp16 and a bf16 value) on the way into the operands, two
-// per v_cvt_scalef32_pk_{f16,bf16}_fp8, and q rows load straight from memory.
-//   K, step s of group q: dims 64h + 16q + 8s' .. +7 (s = 2h + s', h = 0, 1
-//     picks bytes 16q or 64 + 16q of the row): one 16-byte load of codes
-//     gives two steps, and the same dims of q are 16 consecutive bytes.
-//   V: lane (n, q) loads the 8 codes of dims 8n .. 8n+7 of each of its
-//     tokens (an 8-byte load); tile c takes code c of the eight tokens.
-// Rows at or past the range end (masked in softmax_pv) re-read the range's
-// last row, which is in cache, as in the 16-bit walker.
-template <typename Q, int G_, bool STREAM>
-struct Fp8MfmaWalker {
-    static constexpr bool kStream = STREAM;     // K/V load policy
-    static constexpr int kBalancedWavesPerCU = 8;
-    static constexpr int D = 128, G = G_;
-    static constexpr int ROW = 128;
-    static constexpr int CHUNK = 32;
-    static constexpr int kMinWavesPerSimd = 2;
-    static_assert(Q::bytes == 2 && G_ <= 16, "16-bit q, at most 16 query heads");
-
-    f32x4 acc[8];
-    float m, l, vscale, kfac;
-    u32x4 qb[4];        // B operand of Q^T (q's type) for the four k-steps
-
-    int wb, tv;
-    const char* kbase;
-    const char* vbase;
-    const int* trow;
-    size_t head_stride_bytes, kvhead_off;
-    int log2_bs, bs_mask, nblk_valid, max_phys;
-    int* err;           // error word, or null
-    int lane, n, q;
-    int t_end;
-
-    __device__ __forceinline__ void init(int lane_id) {
-        lane = lane_id;
-        n = lane_id & 15;
-        q = lane_id >> 4;
-    }
-
-    __device__ __forceinline__ void begin(const AttnParams& a, int seq, int g, int L) {
-        log2_bs = a.log2_bs;
-        bs_mask = (1 << a.log2_bs) - 1;
-        nblk_valid = (L + bs_mask) >> a.log2_bs;
-        max_phys = a.num_blocks;
-        err = a.err;
-        trow = a.block_tables + (size_t)seq * a.max_blocks;
-        head_stride_bytes = (size_t)a.num_kv_heads * ((size_t)ROW << a.log2_bs);
-        kvhead_off = (size_t)g * ((size_t)ROW << a.log2_bs);
-        kbase = reinterpret_cast<const char*>(a.k_pool);
-        vbase = reinterpret_cast<const char*>(a.v_pool);
-        vscale = a.v_scales[g];
-        kfac = a.k_scales[g];
-        const char* qrow = reinterpret_cast<const char*>(a.q) +
-                           ((size_t)seq * a.num_kv_heads * G + (size_t)g * G + n) * D * Q::bytes;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            // step s = 2h + s2: dims 64h + 16q + 8 s2 .. +7, 16 bytes of q
-            const int d0 = 64 * (s >> 1) + 16 * q + 8 * (s & 1);
-            qb[s] = n < G ? load16(qrow + 2 * d0) : u32x4{0u, 0u, 0u, 0u};
-        }
-        m = -__builtin_inff();
-        l = 0.f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    __device__ __forceinline__ void load_window(int first_block) {
-        wb = first_block;
-        tv = (wb + lane < nblk_valid) ? trow[wb + lane] : 0;
-        // an entry of a valid block outside the pool is read clamped; say so
-        report_wave(err, wb + lane < nblk_valid && (uint32_t)tv >= (uint32_t)max_phys,
-                    PKV_ERRBIT_TABLE);
-    }
-
-    __device__ __forceinline__ uint32_t phys(int blk) {
-        const uint32_t p = (uint32_t)__builtin_amdgcn_ds_bpermute(blk << 2, tv);
-        return p < (uint32_t)max_phys ? p : (uint32_t)(max_phys - 1);
-    }
-
-    // K: kt[t][h] = row (c0 + 16t + n), bytes 64h + 16q .. +15
-    __device__ __forceinline__ void load_k(int c0, u32x4 (&kt)[2][2]) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            int tok = c0 + 16 * t + n;
-            tok = tok < t_end ? tok : t_end - 1;
-            const char* p = kbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes +
-                            kvhead_off + (uint32_t)((tok & bs_mask) * ROW + 16 * q);
-            kt[t][0] = load16_kv<STREAM>(p);
-            kt[t][1] = load16_kv<STREAM>(p + 64);
-        }
-    }
-
-    // V: vt[4h + j] = row (c0 + 16h + 4q + j), bytes 8n .. 8n+7. Four
-    // aligned consecutive tokens never straddle a block (bs >= 8); clamped
-    // rows stay in the block of the first one once it is clamped too.
-    __device__ __forceinline__ void load_v(int c0, u32x2 (&vt)[8]) {
-        const int last = t_end - 1;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int tb = c0 + 16 * h + 4 * q;
-            const int t0 = tb < last ? tb : last;
-            const char* p = vbase + (size_t)phys((t0 >> log2_bs) - wb) * head_stride_bytes +
-                            kvhead_off + (uint32_t)(8 * n);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int tj = tb + j < last ? tb + j : last;
-                vt[4 * h + j] = load8_kv<STREAM>(p + (uint32_t)((tj & bs_mask) * ROW));
-            }
-        }
-    }
-
-    // 8 codes (two dwords) -> the A operand (q's type) of one k-step
-    __device__ __forceinline__ static u32x4 codes_to_16(uint32_t w0, uint32_t w1) {
-        return u32x4{fp8_pair<Q, false>(w0), fp8_pair<Q, true>(w0), fp8_pair<Q, false>(w1),
-                     fp8_pair<Q, true>(w1)};
-    }
-
-    __device__ __forceinline__ void scores(const u32x4 (&kt)[2][2], float scale_log2,
-                                           float (&sc)[8]) {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int s = 2 * h + s2;
-                s0 = mfma_16x16x32(Q{}, codes_to_16(kt[0][h][2 * s2], kt[0][h][2 * s2 + 1]),
-                                   qb[s], s0);
-                s1 = mfma_16x16x32(Q{}, codes_to_16(kt[1][h][2 * s2], kt[1][h][2 * s2 + 1]),
-                                   qb[s], s1);
-            }
-        }
-        const float f = scale_log2 * kfac;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sc[i] = s0[i] * f;
-            sc[4 + i] = s1[i] * f;
-        }
-    }
-
-    template <bool TAIL>
-    __device__ __forceinline__ void softmax_pv(int c0, float (&sc)[8], u32x2 (&vt)[8]) {
-        if constexpr (TAIL) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const bool valid = c0 + 16 * (j >> 2) + 4 * q + (j & 3) < t_end;
-                sc[j] = valid ? sc[j] : -__builtin_inff();
-                vt[j][0] = valid ? vt[j][0] : 0u;
-                vt[j][1] = valid ? vt[j][1] : 0u;
-            }
-        }
-        float mx = sc[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) mx = __builtin_fmaxf(mx, sc[j]);
-        mx = strided_max<16>(mx);
-        const float m_new = __builtin_fmaxf(m, mx);
-        const float alpha = fast_exp2(m - m_new);
-        float p[8], ps = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            p[j] = fast_exp2(sc[j] - m_new);
-            ps += p[j];
-        }
-        l = l * alpha + ps;
-        m = m_new;
-        u32x4 bhi, blo;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const uint32_t h0 = to16(Q{}, p[2 * w]), h1 = to16(Q{}, p[2 * w + 1]);
-            const uint32_t r0 = to16(Q{}, p[2 * w] - from16(Q{}, h0));
-            const uint32_t r1 = to16(Q{}, p[2 * w + 1] - from16(Q{}, h1));
-            bhi[w] = h0 | (h1 << 16);
-            blo[w] = r0 | (r1 << 16);
-        }
-        // widen the eight V pieces: hv[j][k] = codes 2k, 2k+1 of token j in q's type
-        uint32_t hv[8][4];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            hv[j][0] = fp8_pair<Q, false>(vt[j][0]);
-            hv[j][1] = fp8_pair<Q, true>(vt[j][0]);
-            hv[j][2] = fp8_pair<Q, false>(vt[j][1]);
-            hv[j][3] = fp8_pair<Q, true>(vt[j][1]);
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            // V^T tile c: value c of the eight tokens, token order as k-slots
-            u32x4 av;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t x = hv[2 * w][c >> 1], y = hv[2 * w + 1][c >> 1];
-                av[w] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-            }
-            f32x4 o = acc[c] * alpha;
-            o = mfma_16x16x32(Q{}, av, bhi, o);
-            acc[c] = mfma_16x16x32(Q{}, av, blo, o);
-        }
-    }
-
-    __device__ __forceinline__ void walk(int t_begin, int t_stop, float scale_log2) {
-        u32x4 kt[2][2];
-        u32x2 vt[8];
-        float sc[8];
-        for (int w0 = t_begin; w0 < t_stop;) {
-            const int first_block = w0 >> log2_bs;
-            const int win_end = (first_block + 64) << log2_bs;
-            const int w_end = win_end < t_stop ? win_end : t_stop;
-            load_window(first_block);
-            t_end = w_end;
-            int c = w0;
-            load_k(c, kt);
-            load_v(c, vt);
-            for (;;) {
-                const int nx = c + CHUNK;
-                scores(kt, scale_log2, sc);
-                if (nx >= w_end) { softmax_pv<true>(c, sc, vt); break; }
-                load_k(nx, kt);
-                softmax_pv<false>(c, sc, vt);
-                load_v(nx, vt);
-                c = nx;
-            }
-            w0 = w_end;
-        }
-    }
-
-    __device__ __forceinline__ void write_final(const AttnParams& a, int seq, int g) {
-        const float inv = vscale / strided_sum<16>(l);
-        const size_t row = (size_t)seq * a.num_kv_heads * G + (size_t)g * G + (n < G ? n : 0);
-        void* out = a.out;
-        const int dt = a.out_dtype;
-        store_column_tile(acc, inv, row, n < G,
-                          [&](size_t r, int piece, f32x4 v) { store_out4(out, dt, r, piece, v); });
-    }
-
-    __device__ __forceinline__ void write_partial(const AttnParams& a, size_t row0,
-                                                  size_t row_stride) {
-        const float lsum = strided_sum<16>(l);
-        const size_t row = row0 + (size_t)(n < G ? n : 0) * row_stride;
-        float* ws = a.ws_acc;
-        store_column_tile(acc, vscale, row, n < G, [&](size_t r, int piece, f32x4 v) {
-            *reinterpret_cast<f32x4*>(ws + r * D + 4 * piece) = v;
-        });
-        if (n >= G) return;
-        if (q == 0) {
-            a.ws_ml[2 * row] = m;
-            a.ws_ml[2 * row + 1] = lsum;
-        }
-    }
-};
+// Matrix-core walker for FP8 pools (2, 4 or 8 query heads per kv head, several
+// new tokens, or the samples of a group; q in fp16 or bf16): the matrix-core
+// walker of attn_mfma.hpp on E4M3 codes, computing in q's type.
+template <typename Q, int G, bool STREAM>
+using Fp8MfmaWalker = MfmaWalker<Q, G, STREAM, true>;
 
 }  // namespace
 }  // namespace pkv

@@ -41,7 +41,21 @@
 // and their V pieces are zeroed by select before the products; a token past
 // a column's causal limit (multi-query) gets score -inf in that column only,
 // and its V piece stays, since other columns see it.
+//
+// FP8 pools (FP8 = true; blog.aqudi.me "벤치마크가 다가 아니야! vLLM으로 보는
+// LLM 추론 최적화", section 4: a lower-precision KV cache): K/V rows are 128
+// bytes of E4M3 codes times a per-kv-head scale; S is then q's 16-bit type,
+// and the codes are widened to it (exact: every E4M3 value is an fp16 and a
+// bf16 value) on their way into the operands, two per
+// v_cvt_scalef32_pk_{f16,bf16}_fp8. K: one 16-byte load of codes at byte
+// 16q (64 + 16q) gives dims 16q .. 16q+15 (64 + ...), the k-slots of two
+// steps, so step s = 2h + s' takes dims 64h + 16q + 8s' .. +7 (q is loaded
+// in the same order). V: lane (n, q) loads the 8 codes of dims 8n .. 8n+7
+// of each of its tokens (an 8-byte load). The K scale is folded into the
+// score scale and the V scale into the output.
 #pragma once
+
+#include <type_traits>
 
 #include "attn_common.hpp"
 
@@ -70,6 +84,23 @@ __device__ __forceinline__ uint32_t to16(F16, float x) {
 __device__ __forceinline__ float from16(BF16, uint32_t h) { return u2f(h << 16); }
 __device__ __forceinline__ float from16(F16, uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// E4M3 codes H*2, H*2 + 1 (bytes) of w as two packed 16-bit values of type S,
+// in one gfx950 conversion (scale 1; every E4M3 value is exact in fp16 and bf16).
+template <typename S, bool H>
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t w);
+template <> __device__ __forceinline__ uint32_t fp8_pair<F16, false>(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, false));
+}
+template <> __device__ __forceinline__ uint32_t fp8_pair<F16, true>(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, true));
+}
+template <> __device__ __forceinline__ uint32_t fp8_pair<BF16, false>(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false));
+}
+template <> __device__ __forceinline__ uint32_t fp8_pair<BF16, true>(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true));
 }
 
 // The results of up to 16 columns leave a matrix-core walker as a 16 x 128
@@ -130,23 +161,29 @@ __device__ __forceinline__ void store_out4(void* out, int out_dtype, size_t row,
         u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
 }
 
-template <typename S, int G_, bool STREAM>
+template <typename S, int G_, bool STREAM, bool FP8 = false>
 struct MfmaWalker {
     static constexpr bool kStream = STREAM;     // K/V load policy
-    // persistent waves per compute unit in the balanced schedule: one per
-    // SIMD for grouped heads (measured on MI355X: 4 waves beat 8 by 3-5% at 4
-    // and 8 query heads per kv head), two per SIMD for multi-query columns of
-    // one head (8 beat 4 by 9%)
-    static constexpr int kBalancedWavesPerCU = G_ >= 4 ? 4 : 8;
+    // persistent waves per compute unit in the balanced schedule: for 16-bit
+    // K/V one per SIMD for grouped heads (measured on MI355X: 4 waves beat 8
+    // by 3-5% at 4 and 8 query heads per kv head) and two per SIMD for
+    // multi-query columns of one head (8 beat 4 by 9%); two per SIMD for FP8
+    // pools (8 beat 4 and 12 on the long FP8 GQA layer)
+    static constexpr int kBalancedWavesPerCU = FP8 ? 8 : (G_ >= 4 ? 4 : 8);
     static constexpr int D = 128, G = G_;
-    static constexpr int ROW = 256;             // bytes of one token row of one kv head
-    static constexpr int CHUNK = 32;            // tokens per chunk
+    static constexpr int ROW = FP8 ? 128 : 256;   // bytes of one K/V token row of one kv head
+    static constexpr int QROW = 256;              // bytes of one q row (16-bit)
+    static constexpr int KS = FP8 ? 2 : 4;        // 16-byte K loads per token row and lane
+    static constexpr int CHUNK = 32;              // tokens per chunk
     static constexpr int kMinWavesPerSimd = 2;
-    static_assert(S::bytes == 2 && G_ <= 16, "16-bit K/V, at most 16 query heads");
+    // one lane's V piece of one token: 8 dims, 16-bit or codes
+    using VPiece = std::conditional_t<FP8, u32x2, u32x4>;
+    static_assert(S::bytes == 2 && G_ <= 16, "16-bit operands, at most 16 query heads");
 
     f32x4 acc[8];       // O^T tiles: acc[c][i] = head n, dim 32q + 8i + c (unnormalised)
     float m, l;         // head n: running max (log2 units), this lane's partial sum
     u32x4 qb[4];        // B operand of Q^T for the four k-steps
+    float kfac, vscale; // FP8: the kv head's K and V scales
 
     int wb, tv;         // table window: lane j holds the physical id of block wb + j
     const char* kbase;
@@ -158,7 +195,7 @@ struct MfmaWalker {
     int* err;           // error word, or null
     int lane, n, q;
     int t_end;
-    int ncols;          // real columns: num_queries * G (the rest are zero padding)
+    int ncols;          // real columns of this tile: the rest are zero padding
     int lim;            // last token position column n may see (causal rule)
     int mask_from;      // first position some column may not see
     size_t orow;        // output row of column n
@@ -169,7 +206,8 @@ struct MfmaWalker {
         q = lane_id >> 4;
     }
 
-    __device__ __forceinline__ void begin(const AttnParams& a, int seq, int g, int L) {
+    // Point the walker at 16-column tile `tile` of segment (seq, g) of length L.
+    __device__ __forceinline__ void begin(const AttnParams& a, int seq, int g, int L, int tile = 0) {
         log2_bs = a.log2_bs;
         bs_mask = (1 << a.log2_bs) - 1;
         nblk_valid = (L + bs_mask) >> a.log2_bs;
@@ -180,17 +218,15 @@ struct MfmaWalker {
         kvhead_off = (size_t)g * ((size_t)ROW << a.log2_bs);
         kbase = reinterpret_cast<const char*>(a.k_pool);
         vbase = reinterpret_cast<const char*>(a.v_pool);
-        // column n = (query token n / G, head g*G + n % G); a new token at
-        // position L - nq + j sees positions <= its own
+        // column c = 16 tile + n = (query token c / G, head g*G + c % G); a new
+        // token at position L - nq + j sees positions <= its own
         const int nq = a.num_queries;
-        ncols = nq * G;
-        lim = n < ncols ? L - nq + n / G : L - 1;
-        mask_from = L - nq + 1;
-        orow = out_row(a, seq, g, n < ncols ? n : 0);
-        const char* qrow = reinterpret_cast<const char*>(a.q) + orow * ROW + 16 * q;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            qb[s] = n < ncols ? load16(qrow + 64 * s) : u32x4{0u, 0u, 0u, 0u};
+        const int c0 = 16 * tile;
+        ncols = nq * G - c0 < 16 ? nq * G - c0 : 16;
+        lim = n < ncols ? L - nq + (c0 + n) / G : L - 1;
+        mask_from = L - nq + c0 / G + 1;
+        orow = out_row(a, seq, g, c0 + (n < ncols ? n : 0));
+        load_q(a, g, orow, n < ncols);
         m = -__builtin_inff();
         l = 0.f;
 #pragma unroll
@@ -218,13 +254,28 @@ struct MfmaWalker {
         lim = L - 1;
         mask_from = L;
         orow = qrow_idx;
-        const char* qrow = reinterpret_cast<const char*>(a.q) + qrow_idx * ROW + 16 * q;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) qb[s] = active ? load16(qrow + 64 * s) : u32x4{0u, 0u, 0u, 0u};
+        load_q(a, g, qrow_idx, active);
         m = -__builtin_inff();
         l = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // q row `row` as the B operand of the four k-steps (zero if !active):
+    // step s covers dims 32s + 8q .. +7 (16-bit K/V) or 64(s/2) + 16q +
+    // 8(s%2) .. +7 (FP8 codes), 16 consecutive bytes of q either way; and
+    // the kv head's scales for FP8 pools
+    __device__ __forceinline__ void load_q(const AttnParams& a, int g, size_t row, bool active) {
+        const char* qrow = reinterpret_cast<const char*>(a.q) + row * QROW;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int d0 = FP8 ? 64 * (s >> 1) + 16 * q + 8 * (s & 1) : 32 * s + 8 * q;
+            qb[s] = active ? load16(qrow + 2 * d0) : u32x4{0u, 0u, 0u, 0u};
+        }
+        if constexpr (FP8) {
+            kfac = a.k_scales[g];
+            vscale = a.v_scales[g];
+        }
     }
 
     __device__ __forceinline__ void load_window(int first_block) {
@@ -244,7 +295,7 @@ struct MfmaWalker {
     // K: kt[t][s] = row (c0 + 16t + n), bytes 64s + 16q .. +15. Rows at or
     // past the range end (masked by softmax_pv) re-read the range's last row,
     // which is in cache, instead of fetching unrelated blocks from HBM.
-    __device__ __forceinline__ void load_k(int c0, u32x4 (&kt)[2][4]) {
+    __device__ __forceinline__ void load_k(int c0, u32x4 (&kt)[2][KS]) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             int tok = c0 + 16 * t + n;
@@ -252,49 +303,66 @@ struct MfmaWalker {
             const char* p = kbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes +
                             kvhead_off + (uint32_t)((tok & bs_mask) * ROW + 16 * q);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) kt[t][s] = load16_kv<STREAM>(p + 64 * s);
+            for (int s = 0; s < KS; ++s) kt[t][s] = load16_kv<STREAM>(p + 64 * s);
         }
     }
 
-    // V: vt[4h + j] = row (c0 + 16h + 4q + j), bytes 16n .. 16n+15. Four
-    // aligned consecutive tokens never straddle a block (bs >= 8). Rows at or
-    // past the range end (zeroed by softmax_pv) re-read the range's last row,
-    // which lies in the same block as the first of the four rows once that
-    // one is clamped too.
-    __device__ __forceinline__ void load_v(int c0, u32x4 (&vt)[8]) {
+    // V: vt[4h + j] = row (c0 + 16h + 4q + j), dims 8n .. 8n+7 (16 bytes, or
+    // 8 bytes of codes). Four aligned consecutive tokens never straddle a
+    // block (bs >= 8). Rows at or past the range end (zeroed by softmax_pv)
+    // re-read the range's last row, which lies in the same block as the first
+    // of the four rows once that one is clamped too.
+    __device__ __forceinline__ void load_v(int c0, VPiece (&vt)[8]) {
         const int last = t_end - 1;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int tb = c0 + 16 * h + 4 * q;
             const int t0 = tb < last ? tb : last;
             const char* p = vbase + (size_t)phys((t0 >> log2_bs) - wb) * head_stride_bytes +
-                            kvhead_off + (uint32_t)(16 * n);
+                            kvhead_off + (uint32_t)(sizeof(VPiece) * n);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int tj = tb + j < last ? tb + j : last;
-                vt[4 * h + j] = load16_kv<STREAM>(p + (uint32_t)((tj & bs_mask) * ROW));
+                const char* pj = p + (uint32_t)((tj & bs_mask) * ROW);
+                if constexpr (FP8)
+                    vt[4 * h + j] = load8_kv<STREAM>(pj);
+                else
+                    vt[4 * h + j] = load16_kv<STREAM>(pj);
             }
         }
     }
 
+    // A operand of k-step s for token tile t: the K row piece itself, or
+    // (FP8) codes 8(s%2) .. +7 of load s/2 widened to S
+    __device__ __forceinline__ static u32x4 k_operand(const u32x4 (&kt)[KS], int s) {
+        if constexpr (FP8) {
+            const uint32_t w0 = kt[s >> 1][2 * (s & 1)], w1 = kt[s >> 1][2 * (s & 1) + 1];
+            return u32x4{fp8_pair<S, false>(w0), fp8_pair<S, true>(w0), fp8_pair<S, false>(w1),
+                         fp8_pair<S, true>(w1)};
+        } else {
+            return kt[s];
+        }
+    }
+
     // Scores of the chunk: k-slot j of group q is token 16 (j / 4) + 4q + j % 4.
-    __device__ __forceinline__ void scores(const u32x4 (&kt)[2][4], float scale_log2,
+    __device__ __forceinline__ void scores(const u32x4 (&kt)[2][KS], float scale_log2,
                                            float (&sc)[8]) {
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            s0 = mfma_16x16x32(S{}, kt[0][s], qb[s], s0);
-            s1 = mfma_16x16x32(S{}, kt[1][s], qb[s], s1);
+            s0 = mfma_16x16x32(S{}, k_operand(kt[0], s), qb[s], s0);
+            s1 = mfma_16x16x32(S{}, k_operand(kt[1], s), qb[s], s1);
         }
+        const float f = FP8 ? scale_log2 * kfac : scale_log2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sc[i] = s0[i] * scale_log2;
-            sc[4 + i] = s1[i] * scale_log2;
+            sc[i] = s0[i] * f;
+            sc[4 + i] = s1[i] * f;
         }
     }
 
     template <bool TAIL>
-    __device__ __forceinline__ void softmax_pv(int c0, float (&sc)[8], u32x4 (&vt)[8]) {
+    __device__ __forceinline__ void softmax_pv(int c0, float (&sc)[8], VPiece (&vt)[8]) {
         // Scores are masked by the range end and by column n's causal limit;
         // V pieces only by the range end: lane n's V piece holds dims
         // 8n .. 8n+7 of a token for every column, and a token past one
@@ -307,7 +375,8 @@ struct MfmaWalker {
             if constexpr (TAIL) {
                 const bool in_range = tok < t_end;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) vt[j][w] = in_range ? vt[j][w] : 0u;
+                for (int w = 0; w < (int)(sizeof(VPiece) / 4); ++w)
+                    vt[j][w] = in_range ? vt[j][w] : 0u;
             }
         }
         if constexpr (TAIL) {
@@ -341,13 +410,27 @@ struct MfmaWalker {
             bhi[w] = h0 | (h1 << 16);
             blo[w] = r0 | (r1 << 16);
         }
+        // the eight V pieces as pairs of S values: hv[j][k] = dims 2k, 2k+1 of token j
+        uint32_t hv[8][4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if constexpr (FP8) {
+                hv[j][0] = fp8_pair<S, false>(vt[j][0]);
+                hv[j][1] = fp8_pair<S, true>(vt[j][0]);
+                hv[j][2] = fp8_pair<S, false>(vt[j][1]);
+                hv[j][3] = fp8_pair<S, true>(vt[j][1]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) hv[j][k] = vt[j][k];
+            }
+        }
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             // V^T tile c: element c of the eight V pieces, token order as k-slots
             u32x4 av;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const uint32_t x = vt[2 * w][c >> 1], y = vt[2 * w + 1][c >> 1];
+                const uint32_t x = hv[2 * w][c >> 1], y = hv[2 * w + 1][c >> 1];
                 av[w] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
             }
             f32x4 o = acc[c] * alpha;
@@ -361,7 +444,8 @@ struct MfmaWalker {
     // products have consumed this V, so about one chunk stays in flight per
     // wave with half the registers of a double buffer (two waves per SIMD).
     __device__ __forceinline__ void walk(int t_begin, int t_stop, float scale_log2) {
-        u32x4 kt[2][4], vt[8];
+        u32x4 kt[2][KS];
+        VPiece vt[8];
         float sc[8];
         for (int w0 = t_begin; w0 < t_stop;) {
             const int first_block = w0 >> log2_bs;
@@ -394,7 +478,8 @@ struct MfmaWalker {
 
     __device__ __forceinline__ void write_final(const AttnParams& a, int seq, int g) {
         const float lsum = total_sum();
-        const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;   // 0: a query before the start
+        // 0: a query before the start; FP8 values carry the kv head's V scale
+        const float inv = lsum > 0.f ? (FP8 ? vscale / lsum : 1.0f / lsum) : 0.f;
         void* out = a.out;
         const int dt = a.out_dtype;
         store_column_tile(acc, inv, orow, n < ncols,
@@ -410,7 +495,7 @@ struct MfmaWalker {
     __device__ __forceinline__ void write_partial_at(const AttnParams& a, size_t row, bool active) {
         const float lsum = total_sum();
         float* ws = a.ws_acc;
-        store_column_tile(acc, 1.f, row, active, [&](size_t r, int piece, f32x4 v) {
+        store_column_tile(acc, FP8 ? vscale : 1.f, row, active, [&](size_t r, int piece, f32x4 v) {
             *reinterpret_cast<f32x4*>(ws + r * D + 4 * piece) = v;
         });
         if (!active) return;

@@ -160,7 +160,7 @@ struct VecWalker {
     // -- one range of one segment --------------------------------------------
 
     // Point the state at segment (seq, g) of length L and reset it.
-    __device__ __forceinline__ void begin(const AttnParams& a, int seq, int g, int L) {
+    __device__ __forceinline__ void begin(const AttnParams& a, int seq, int g, int L, int = 0) {
         log2_bs = a.log2_bs;
         bs_mask = (1 << a.log2_bs) - 1;
         nblk_valid = (L + bs_mask) >> a.log2_bs;

@@ -49,8 +49,12 @@ struct AttnParams {
     int num_queries;               // new tokens per sequence (1: decode); q and out are
                                    // [B][num_queries][H][D]. A segment (seq, kv head) has
                                    // num_queries * group columns (query token, head).
+    int col_tiles;                 // 16-column tiles per segment: ceil(columns / 16); more
+                                   // than one only for the matrix-core walker, under the
+                                   // single pass or fixed partitions
     int dtype;                     // q / K / V element type (16/32-bit path)
     int* err;                      // error word (pkv_set_error_word), or null
+    int force_vector;              // PKV_WALKER_VECTOR: grouped heads on the vector units
     // FP8 pools: K/V are E4M3 codes times a per-kv-head scale; q has q_dtype
     const float* k_scales;
     const float* v_scales;

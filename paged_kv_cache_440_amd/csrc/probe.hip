@@ -1,7 +1,8 @@
 // Memory-system reference kernels (declared in include/pkv_probe.h): a
-// read-only stream that gives the practical HBM read ceiling, and a plain
-// copy of known size for scaling traffic counters. Both read with the
-// non-temporal 16-byte loads the attention kernels use for K/V.
+// read-only stream that gives the practical HBM read ceiling, a plain copy of
+// known size for scaling traffic counters, and a gather of exactly the K/V
+// rows a decode launch reads (the ceiling of the paged access pattern). All
+// read with the non-temporal 16-byte loads the attention kernels use for K/V.
 
 #include "pkv_probe.h"
 #include "pkv_device.hpp"
@@ -69,6 +70,145 @@ void probe_copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src, l
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// -- paged gather: the K/V rows a decode launch reads, and nothing else -------
+struct GatherParams {
+    const char* k_pool;
+    const char* v_pool;
+    const int32_t* tables;
+    const int32_t* lens;
+    uint32_t* sink;
+    int max_blocks, num_seqs, num_kv_heads, row_bytes, log2_bs, num_blocks, waves;
+};
+
+constexpr int kGatherUnit = 32;           // tokens per unit of the equal split
+constexpr int kGatherWavesPerGroup = 4;
+
+__device__ __forceinline__ long long gather_scan(long long x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const long long y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ int gather_units(const GatherParams& a, int i) {
+    const int L = a.lens[i];
+    return L > 0 ? (L + kGatherUnit - 1) / kGatherUnit : 0;
+}
+
+// Wave w of `waves` takes the w-th of `waves` equal runs of the 32-token
+// units of all (sequence, kv head) segments laid end to end, and reads every
+// K and V row of its run through the block table: lane l loads 16-byte piece
+// l % LPT of token l / LPT of a TPL-token group (one wave load = TPL whole
+// rows, consecutive bytes of one block), NL groups of K and NL of V per
+// round, with non-temporal loads. Rows at or past a range's end are not
+// loaded (exec-masked). The XOR of everything read goes to sink[w].
+template <int LPT, int NL>
+__global__ __launch_bounds__(64 * kGatherWavesPerGroup)
+void probe_gather_kernel(const GatherParams a) {
+    constexpr int TPL = 64 / LPT, CH = TPL * NL;
+    const int lane = threadIdx.x & 63;
+    const int w = blockIdx.x * kGatherWavesPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w >= a.waves) return;
+    long long total = 0;
+    for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
+        const int i = b0 + lane;
+        total += __shfl(gather_scan(i < a.num_seqs ? gather_units(a, i) : 0), 63, 64);
+    }
+    total *= a.num_kv_heads;
+    const long long q = (total + a.waves - 1) / a.waves;
+    const long long u0 = (long long)w * q, u1 = u0 + q < total ? u0 + q : total;
+    uint32_t x = 0;
+    long long base = 0;
+    int seq = a.num_seqs;
+    if (u0 < u1) {
+        for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
+            const int i = b0 + lane;
+            const long long span = i < a.num_seqs ? (long long)a.num_kv_heads * gather_units(a, i) : 0;
+            const long long incl = gather_scan(span);
+            const unsigned long long past = __ballot(base + incl > u0);
+            if (past) {
+                const int j = __builtin_ctzll(past);
+                seq = b0 + j;
+                base += __shfl(incl - span, j, 64);
+                break;
+            }
+            base += __shfl(incl, 63, 64);
+        }
+    }
+    const int bs_mask = (1 << a.log2_bs) - 1;
+    const size_t tile = (size_t)a.row_bytes << a.log2_bs;
+    const size_t blk_stride = (size_t)a.num_kv_heads * tile;
+    const int tok = lane / LPT, piece = lane % LPT;
+    long long u = u0;
+    while (u < u1 && seq < a.num_seqs) {
+        const int L = a.lens[seq];
+        const int nu = L > 0 ? (L + kGatherUnit - 1) / kGatherUnit : 0;
+        if (nu == 0) { ++seq; continue; }
+        const int g = (int)((u - base) / nu);
+        const long long seg0 = base + (long long)g * nu, seg1 = seg0 + nu;
+        const int k0 = (int)(u - seg0);
+        const int k1 = (int)((u1 < seg1 ? u1 : seg1) - seg0);
+        const int t_stop = k1 * kGatherUnit < L ? k1 * kGatherUnit : L;
+        const int* trow = a.tables + (size_t)seq * a.max_blocks;
+        int nblk = (L + bs_mask) >> a.log2_bs;
+        nblk = nblk < a.max_blocks ? nblk : a.max_blocks;   // never read past the table row
+        for (int w0 = k0 * kGatherUnit; w0 < t_stop;) {
+            const int fb = w0 >> a.log2_bs;
+            const int win_end = (fb + 64) << a.log2_bs;
+            const int w_end = win_end < t_stop ? win_end : t_stop;
+            int tv = fb + lane < nblk ? trow[fb + lane] : 0;
+            tv = (uint32_t)tv < (uint32_t)a.num_blocks ? tv : a.num_blocks - 1;
+            const int last_group = ((w_end - 1) / TPL) * TPL;
+            for (int c = w0; c < w_end; c += CH) {
+                u32x4 kr[NL], vr[NL];
+#pragma unroll
+                for (int j = 0; j < NL; ++j) {
+                    int tg = c + j * TPL;
+                    const bool live = tg + tok < w_end;
+                    tg = tg < last_group ? tg : last_group;      // keep the lookup in the window
+                    const uint32_t p = (uint32_t)__builtin_amdgcn_readlane(tv, (tg >> a.log2_bs) - fb);
+                    const size_t off = (size_t)p * blk_stride + (size_t)g * tile +
+                                       (size_t)(((tg & bs_mask) + tok) * a.row_bytes + piece * 16);
+                    kr[j] = u32x4{0u, 0u, 0u, 0u};
+                    vr[j] = u32x4{0u, 0u, 0u, 0u};
+                    if (live) {
+                        kr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.k_pool + off));
+                        vr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.v_pool + off));
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < NL; ++j) x ^= kr[j][0] ^ kr[j][3] ^ vr[j][1] ^ vr[j][2];
+            }
+            w0 = w_end;
+        }
+        u = seg0 + k1;
+        if (g == a.num_kv_heads - 1 && u == seg1) {
+            base = u;
+            ++seq;
+        }
+    }
+    // fold the wave's lanes and store one word per wave (a vector store)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o, 64);
+    if (lane == 0) a.sink[w] = x;
+}
+
+template <int LPT>
+hipError_t launch_gather(const GatherParams& a, int loads, hipStream_t stream) {
+    const dim3 grid((a.waves + kGatherWavesPerGroup - 1) / kGatherWavesPerGroup);
+    const dim3 block(64 * kGatherWavesPerGroup);
+    switch (loads) {
+        case 2: hipLaunchKernelGGL((probe_gather_kernel<LPT, 2>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((probe_gather_kernel<LPT, 4>), grid, block, 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((probe_gather_kernel<LPT, 8>), grid, block, 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -99,6 +239,39 @@ int pkv_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
                        reinterpret_cast<pkv::u32x4*>(dst),
                        reinterpret_cast<const pkv::u32x4*>(src), pieces);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_probe_gather(const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                     int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs,
+                     int num_kv_heads, int row_bytes, int block_size, int num_blocks, int waves,
+                     int loads_per_round, uint32_t* sink, void* stream) {
+    int log2_bs = -1;
+    for (int s = 3; s <= 8; ++s)
+        if (block_size == (1 << s)) log2_bs = s;
+    if (!k_pool || !v_pool || !block_tables || !seq_lens || !sink || num_seqs <= 0 ||
+        num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || waves <= 0 ||
+        !pkv::aligned16(k_pool) || !pkv::aligned16(v_pool))
+        return PKV_ERR_INVALID;
+    if ((row_bytes != 128 && row_bytes != 256) || log2_bs < 0 ||
+        !(loads_per_round == 2 || loads_per_round == 4 || loads_per_round == 8))
+        return PKV_ERR_UNSUPPORTED;
+    if ((long long)num_seqs * max_blocks_per_seq > INT32_MAX) return PKV_ERR_INVALID;
+    pkv::GatherParams a{};
+    a.k_pool = reinterpret_cast<const char*>(k_pool);
+    a.v_pool = reinterpret_cast<const char*>(v_pool);
+    a.tables = block_tables;
+    a.lens = seq_lens;
+    a.sink = sink;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = num_kv_heads;
+    a.row_bytes = row_bytes;
+    a.log2_bs = log2_bs;
+    a.num_blocks = num_blocks;
+    a.waves = waves;
+    const hipError_t err = row_bytes == 128 ? pkv::launch_gather<8>(a, loads_per_round, (hipStream_t)stream)
+                                            : pkv::launch_gather<16>(a, loads_per_round, (hipStream_t)stream);
+    return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
 }  // extern "C"

@@ -335,6 +335,45 @@ def opt13b_spec4_fp16(seed=SEED_BASE + 8, num_seqs=64, len_range=(32, 2048), nq=
     return w
 
 
+def opt13b_prefill256_fp16(seed=SEED_BASE + 11, num_seqs=8, cached_range=(1024, 2048),
+                           chunk=256, block_size=16) -> Workload:
+    """Chunked prefill on the OPT-13B layer (blog.aqudi.me section 4: a long
+    prompt fed in pieces between decode steps): 8 sequences each feed a
+    256-token chunk of prompt after 1024..2048 cached tokens; the chunk's
+    tokens attend causally to the cache and to each other."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(1)[0])
+    lens = rng.integers(cached_range[0], cached_range[1], size=num_seqs, endpoint=True) + chunk
+    w = build_independent("opt13b_prefill256_fp16", lens, dtype=torch.float16, num_heads=40,
+                          num_kv_heads=40, head_dim=128, block_size=block_size, dist="normal",
+                          seed=seed + 100_000)
+    r = np.random.default_rng(np.random.SeedSequence(seed).spawn(2)[1])
+    b = w.num_seqs
+    w.k_new = _small_draw(r, (b, chunk, 40, 128), torch.float16, "normal")
+    w.v_new = _small_draw(r, (b, chunk, 40, 128), torch.float16, "normal")
+    w.q = _small_draw(r, (b, chunk, 40, 128), torch.float16, "normal")
+    w.num_queries = chunk
+    return w
+
+
+def opt13b_spec4_fp8(seed=SEED_BASE + 9, num_seqs=64, len_range=(32, 2048), nq=4,
+                     block_size=16) -> Workload:
+    """Speculative verification of 4 proposed tokens on the OPT-13B layer over
+    an FP8 E4M3 KV cache (per-head scales as opt13b_fp8); q and the new tokens
+    in fp16. Same lengths as opt13b_spec4_fp16."""
+    rng = np.random.default_rng(np.random.SeedSequence(SEED_BASE + 2).spawn(1)[0])
+    lens = rng.integers(len_range[0], len_range[1], size=num_seqs, endpoint=True) + nq - 1
+    w = build_independent("opt13b_spec4_fp8", lens, dtype=torch.float16, num_heads=40,
+                          num_kv_heads=40, head_dim=128, block_size=block_size, dist="normal",
+                          seed=seed + 100_000, fp8_spread=8.0)
+    r = np.random.default_rng(np.random.SeedSequence(seed).spawn(2)[1])
+    b = w.num_seqs
+    w.k_new = _small_draw(r, (b, nq, 40, 128), torch.float16, "normal")
+    w.v_new = _small_draw(r, (b, nq, 40, 128), torch.float16, "normal")
+    w.q = _small_draw(r, (b, nq, 40, 128), torch.float16, "normal")
+    w.num_queries = nq
+    return w
+
+
 def llama13b_bf16(seed=SEED_BASE + 3, num_seqs=256, median=350.0, sigma=0.9,
                   max_len=4096, block_size=16) -> Workload:
     """LLaMA-13B attention layer: 40 heads of 128, bf16, batch 256, chat-like
@@ -362,7 +401,7 @@ def long_gqa_bf16(seed=SEED_BASE + 5, block_size=16, num_seqs=16,
 
 def shared_prefix_fp16(seed=SEED_BASE + 4, prefix_len=1024, num_prompts=32,
                        samples=8, max_divergent=256, block_size=16,
-                       num_heads=40, head_dim=128) -> Workload:
+                       num_heads=40, head_dim=128, fp8_spread=None) -> Workload:
     """Parallel sampling: each prompt's prefix blocks are named by the tables
     of all its samples; each sample adds 0..max_divergent tokens of its own
     plus the token appended this step.
@@ -373,6 +412,9 @@ def shared_prefix_fp16(seed=SEED_BASE + 4, prefix_len=1024, num_prompts=32,
     samples' own tokens that fall inside that block are returned as pending
     appends (to be stored after the copies, one step at a time). History
     tokens past that block are drawn directly into private blocks.
+
+    With fp8_spread the pools hold FP8 E4M3 codes under
+    fp8_head_scales(num_heads, fp8_spread) (q and new tokens stay fp16).
     """
     dtype = torch.float16
     ss_len, ss_tables, ss_k, ss_v, ss_small = np.random.SeedSequence(seed).spawn(5)
@@ -414,8 +456,9 @@ def shared_prefix_fp16(seed=SEED_BASE + 4, prefix_len=1024, num_prompts=32,
             tables[i, prefix_blocks:nb] = own
     assert cursor == needed
     used = perm[:needed]
-    k_pool = _pool(num_blocks, num_heads, block_size, head_dim, dtype, ss_k, "normal", used)
-    v_pool = _pool(num_blocks, num_heads, block_size, head_dim, dtype, ss_v, "normal", used)
+    sc = fp8_head_scales(num_heads, fp8_spread) if fp8_spread is not None else None
+    k_pool = _pool(num_blocks, num_heads, block_size, head_dim, dtype, ss_k, "normal", used, sc)
+    v_pool = _pool(num_blocks, num_heads, block_size, head_dim, dtype, ss_v, "normal", used, sc)
 
     rng = np.random.default_rng(ss_small)
     b = num_prompts * samples
@@ -432,7 +475,8 @@ def shared_prefix_fp16(seed=SEED_BASE + 4, prefix_len=1024, num_prompts=32,
     k_new = _small_draw(rng, (b, num_heads, head_dim), dtype, "normal")
     v_new = _small_draw(rng, (b, num_heads, head_dim), dtype, "normal")
     q = _small_draw(rng, (b, num_heads, head_dim), dtype, "normal")
-    name = "shared_prefix_cow_fp16" if partial else "shared_prefix_fp16"
+    name = ("shared_prefix_cow" if partial else "shared_prefix") + ("_fp8" if sc is not None
+                                                                   else "_fp16")
     return Workload(name=name, dtype=dtype, num_heads=num_heads, num_kv_heads=num_heads,
                     head_dim=head_dim, block_size=block_size, scale=1.0 / math.sqrt(head_dim),
                     num_blocks=num_blocks, seq_lens=seq_lens, block_tables=tables,
@@ -441,13 +485,28 @@ def shared_prefix_fp16(seed=SEED_BASE + 4, prefix_len=1024, num_prompts=32,
                     pending_k=pending_k, pending_v=pending_v, pending_lens=pending_lens,
                     info={"prefix_len": prefix_len, "num_prompts": num_prompts,
                           "samples": samples, "unique_blocks": needed},
-                    shared_blocks=True)
+                    shared_blocks=True,
+                    k_scales=None if sc is None else torch.from_numpy(sc.copy()),
+                    v_scales=None if sc is None else torch.from_numpy(sc.copy()))
 
 
 def shared_prefix_cow_fp16(seed=SEED_BASE + 4, **kw) -> Workload:
     """The shared-prefix workload with a 1032-token prefix: 64 full shared
     blocks plus a shared partial block that 7 of 8 samples copy."""
     kw.setdefault("prefix_len", 1032)
+    return shared_prefix_fp16(seed=seed, **kw)
+
+
+def shared_prefix_fp8(seed=SEED_BASE + 10, **kw) -> Workload:
+    """The 32 x 8 parallel-sampling layer over an FP8 E4M3 KV cache."""
+    kw.setdefault("fp8_spread", 8.0)
+    return shared_prefix_fp16(seed=seed, **kw)
+
+
+def shared_prefix_cow_fp8(seed=SEED_BASE + 10, **kw) -> Workload:
+    """The copy-on-write variant (1032-token prefix) over an FP8 KV cache."""
+    kw.setdefault("prefix_len", 1032)
+    kw.setdefault("fp8_spread", 8.0)
     return shared_prefix_fp16(seed=seed, **kw)
 
 
@@ -461,6 +520,10 @@ WORKLOADS = {
     "opt13b_fp8": opt13b_fp8,
     "opt13b_spec4_fp16": opt13b_spec4_fp16,
     "long_gqa_fp8": long_gqa_fp8,
+    "opt13b_spec4_fp8": opt13b_spec4_fp8,
+    "opt13b_prefill256_fp16": opt13b_prefill256_fp16,
+    "shared_prefix_fp8": shared_prefix_fp8,
+    "shared_prefix_cow_fp8": shared_prefix_cow_fp8,
 }
 
 

@@ -106,7 +106,9 @@ def attn(lib, **kw):
     (dict(B=0, policy=0x21), OK),           # PKV_STAGE_MERGE with PKV_KV_REUSE
     (dict(policy=0x30), INVALID),           # both stages
     (dict(policy=0x12), INVALID),           # a stage with an unknown policy
-    (dict(policy=0x40), INVALID),           # an unknown flag
+    (dict(policy=0x80), INVALID),           # an unknown flag
+    (dict(B=0, policy=0x40), OK),           # PKV_WALKER_VECTOR
+    (dict(policy=0x41), UNSUPPORTED),       # ... with cached loads
 ])
 def test_attention_validation(lib, kw, status):
     assert attn(lib, **kw) == status
@@ -261,7 +263,8 @@ def attn_multi(lib, **kw):
     (dict(dtype=0), UNSUPPORTED),              # fp32 K/V
     (dict(dtype=3), UNSUPPORTED),              # FP8 pools
     (dict(D=64), UNSUPPORTED),
-    (dict(nq=5, H=16, Hkv=4), UNSUPPORTED),    # 5 tokens x 4 heads > 16 columns
+    (dict(nq=5, H=16, Hkv=4, B=0), OK),        # 5 tokens x 4 heads: 16-column groups (no launch)
+    (dict(nq=300, H=16, Hkv=2, dtype=0), UNSUPPORTED),   # any column count, but not fp32 K/V
     (dict(part=64, ws=0), WORKSPACE),
     (dict(policy=3), INVALID),
     (dict(B=0), OK),
@@ -386,3 +389,72 @@ def test_noalloc_refuses_a_call_beyond_its_static_scratch(lib):
     assert lib.pkv_paged_attention_decode_noalloc(*args) == INVALID
     args[9] = 0                                      # an empty batch enqueues nothing
     assert lib.pkv_paged_attention_decode_noalloc(*args) == OK
+
+
+def test_fp8_multi_and_grouped_validation(lib):
+    """The FP8 multi-query, multi-token append and grouped entry points refuse
+    bad arguments before anything is enqueued (no call here reaches a GPU)."""
+    import ctypes
+    f = ctypes.c_float(0.1)
+
+    def multi(**kw):
+        a = dict(out=FAKE, out_dtype=0, q=FAKE, q_dtype=1, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE,
+                 tables=FAKE, max_blocks=8, lens=FAKE, max_seq_len=100, B=2, nq=4, H=4, Hkv=4,
+                 D=128, bs=16, nb=32, part=0, ws=0, ws_bytes=0, policy=0)
+        a.update(kw)
+        return lib.pkv_paged_attention_multi_fp8(
+            a["out"], a["out_dtype"], a["q"], a["q_dtype"], a["k"], a["v"], a["ks"], a["vs"],
+            a["tables"], a["max_blocks"], a["lens"], a["max_seq_len"], a["B"], a["nq"], a["H"],
+            a["Hkv"], a["D"], a["bs"], a["nb"], f, a["part"], a["ws"], a["ws_bytes"], a["policy"],
+            None)
+
+    assert multi(q_dtype=0) == UNSUPPORTED            # fp32 q
+    assert multi(D=64) == UNSUPPORTED
+    assert multi(nq=0) == INVALID
+    assert multi(ks=0) == INVALID
+    assert multi(part=64) == WORKSPACE
+    assert multi(B=0) == OK
+
+    def grouped(**kw):
+        a = dict(q_dtype=2, B=8, group_size=4, shared=FAKE, part=64, ws=FAKE, ks=FAKE)
+        a.update(kw)
+        return lib.pkv_paged_attention_decode_grouped_fp8(
+            FAKE, 0, FAKE, a["q_dtype"], FAKE, FAKE, a["ks"], FAKE, FAKE, 8, FAKE, 100, a["B"], 8,
+            2, 128, 16, 32, f, a["part"], a["group_size"], a["shared"], a["ws"], 1 << 24, 0, None)
+
+    assert grouped(q_dtype=0) == UNSUPPORTED
+    assert grouped(group_size=3) == INVALID            # 8 sequences not a multiple of 3
+    assert grouped(part=0) == INVALID                  # fixed partitions only
+    assert grouped(shared=0) == INVALID                # no shared-token counts
+    assert grouped(ws=0) == WORKSPACE
+    assert grouped(B=0) == OK
+
+    def append(**kw):
+        a = dict(nq=3, D=128, B=2, ks=FAKE)
+        a.update(kw)
+        return lib.pkv_kv_cache_append_multi_fp8(FAKE, FAKE, 1, FAKE, FAKE, a["ks"], FAKE, FAKE, 8,
+                                                 FAKE, a["B"], a["nq"], 4, a["D"], 16, 32, None)
+
+    assert append(nq=0) == INVALID
+    assert append(D=64) == UNSUPPORTED
+    assert append(ks=0) == INVALID
+    assert append(B=0) == OK
+
+
+def test_gather_probe_validation(lib):
+    args = dict(k=FAKE, v=FAKE, tables=FAKE, max_blocks=8, lens=FAKE, B=2, Hkv=4, row=256, bs=16,
+                nb=32, waves=64, loads=4, sink=FAKE)
+
+    def g(**kw):
+        a = dict(args)
+        a.update(kw)
+        return lib.pkv_probe_gather(a["k"], a["v"], a["tables"], a["max_blocks"], a["lens"], a["B"],
+                                    a["Hkv"], a["row"], a["bs"], a["nb"], a["waves"], a["loads"],
+                                    a["sink"], None)
+
+    assert g(row=64) == UNSUPPORTED
+    assert g(loads=3) == UNSUPPORTED
+    assert g(bs=12) == UNSUPPORTED
+    assert g(sink=0) == INVALID
+    assert g(waves=0) == INVALID
+    assert g(k=FAKE + 4) == INVALID

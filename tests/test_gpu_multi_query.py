@@ -120,3 +120,85 @@ def test_kv_policies_give_identical_bits(partition):
     _, _, a = run(w, k_new, v_new, q, partition, kv_reuse=False)
     _, _, b = run(w, k_new, v_new, q, partition, kv_reuse=True)
     assert torch.equal(a.cpu().view(torch.int32), b.cpu().view(torch.int32))
+
+
+# ---------------------------------------------------- chunked prefill (> 16 columns)
+
+PREFILL_LENS = [0, 5, 31, 32, 33, 100, 255, 256, 257, 300, 700, 1300]
+
+
+def prefill_setup(nq, group, dtype, block_size, seed=47):
+    global LENS
+    saved, LENS = LENS, PREFILL_LENS
+    try:
+        return setup(nq, group, dtype, block_size, seed=seed)
+    finally:
+        LENS = saved
+
+
+@pytest.mark.parametrize("nq,group,dtype,block_size", [
+    (32, 1, torch.float16, 16), (128, 1, torch.bfloat16, 8), (256, 1, torch.float16, 64),
+    (32, 8, torch.bfloat16, 16), (128, 8, torch.float16, 32), (256, 8, torch.bfloat16, 16),
+])
+def test_chunked_prefill_matches_oracle(nq, group, dtype, block_size):
+    """Chunks of 32 to 256 new tokens, 1 or 8 query heads per kv head: the
+    (token, head) columns run 16 at a time, each group reading the cache up to
+    its last column's causal limit. Lengths cross block and partition edges
+    and include chunks longer than their sequence (zero rows before the
+    start); every schedule against one oracle evaluation."""
+    w, k_new, v_new, q = prefill_setup(nq, group, dtype, block_size)
+    kb, vb = pool_after_append_multi(bits(w.k_pool), bits(w.v_pool), bits(k_new), bits(v_new),
+                                     w.block_tables, w.seq_lens, w.block_size)
+    ref = paged_multi_query_attention(widen(q), widen(from_bits(kb, dtype)),
+                                      widen(from_bits(vb, dtype)), w.block_tables, w.seq_lens,
+                                      w.block_size, w.scale)
+    for partition in (0, 64, 512, BAL):
+        kp, vp, out = run(w, k_new, v_new, q, partition)
+        assert np.array_equal(bits(kp), kb) and np.array_equal(bits(vp), vb)
+        o = out.cpu().double().numpy()
+        assert np.isfinite(o).all()
+        path = "prefill_f16" if dtype == torch.float16 else "prefill_bf16"
+        check_error(path, float(np.abs(o - ref).max()), 2e-3,
+                    f"nq {nq} G {group} bs {block_size} partition {partition}")
+        for i, n in enumerate(PREFILL_LENS):
+            for j in range(nq):
+                if n - nq + j < 0:
+                    assert (o[i, j] == 0).all(), (partition, i, j)
+
+
+def test_chunked_prefill_balanced_is_the_single_pass():
+    """With more than 16 columns the balanced schedule runs as a single pass
+    per 16-column group: the same bits, and no workspace."""
+    w, k_new, v_new, q = prefill_setup(64, 2, torch.float16, 16)
+    assert pkv.paged_attention_workspace_size(w.num_seqs, 4 * 64, 2, 128, w.max_seq_len, BAL) == 0
+    _, _, a = run(w, k_new, v_new, q, 0)
+    _, _, b = run(w, k_new, v_new, q, BAL)
+    assert torch.equal(a.cpu(), b.cpu())
+
+
+def test_full_size_chunked_prefill_matches_oracle():
+    """The OPT-13B prefill workload (8 x 256-token chunks over 1-2k cached
+    tokens) in the timed configuration, on sampled rows the oracle computes
+    one by one: pools bit-exact, the sampled outputs within 2e-3."""
+    w = wl.opt13b_prefill256_fp16()
+    kp, vp, out = run(w, w.k_new, w.v_new, w.q, BAL)
+    kb, vb = pool_after_append_multi(bits(w.k_pool), bits(w.v_pool), bits(w.k_new),
+                                     bits(w.v_new), w.block_tables, w.seq_lens, w.block_size)
+    assert np.array_equal(bits(kp), kb) and np.array_equal(bits(vp), vb)
+    del kp, vp
+    # every sequence, the first, last and a spread of middle chunk tokens
+    toks = [0, 1, 15, 16, 17, 100, 127, 128, 200, 254, 255]
+    k64, v64 = widen(from_bits(kb, torch.float16)), widen(from_bits(vb, torch.float16))
+    o = out.cpu().double().numpy()
+    worst = 0.0
+    for i in range(w.num_seqs):
+        sub_q = widen(w.q[i:i + 1, toks])
+        L = int(w.seq_lens[i])
+        # the sampled tokens of sequence i, each a one-query problem at its position
+        for jj, j in enumerate(toks):
+            lens = np.array([L - 256 + j + 1], dtype=np.int32)
+            ref = paged_multi_query_attention(sub_q[:, jj:jj + 1], k64, v64,
+                                              w.block_tables[i:i + 1], lens, w.block_size,
+                                              w.scale)
+            worst = max(worst, float(np.abs(o[i, j] - ref[0, 0]).max()))
+    check_error("prefill_f16", worst, 2e-3, "opt13b_prefill256_fp16 balanced (sampled)")

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import paged_kv_cache_440_amd as pkv
 from paged_kv_cache_440_amd import workloads as wl
 from paged_kv_cache_440_amd import PARTITION_BALANCED as BAL
 from tests.gpu_support import (TOL, Device, bits, check_error, expected_attention, expected_pools,
@@ -423,3 +424,49 @@ def test_kv_policies_give_identical_bits(dtype, head_dim, group, partition):
     assert torch.equal(bits_t(streamed), bits_t(cached))
     ref = expected_attention(w, *expected_pools(w))
     assert max_err(streamed, ref) <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("partition", [0, 512, BAL])
+@pytest.mark.parametrize("heads", [32, 64])
+def test_vector_walker_forced_on_grouped_heads(heads, partition):
+    """PKV_WALKER_VECTOR runs 4 or 8 query heads per kv head on the vector
+    units (the comparison the matrix-core walker is measured against): the
+    same oracle tolerance."""
+    w = wl.long_gqa_bf16(num_seqs=3, len_range=(700, 2500))
+    q = torch.from_numpy(np.random.default_rng(heads).standard_normal(
+        (w.num_seqs, heads, 128), dtype=np.float32)).to(torch.bfloat16)
+    w.q = q
+    w.num_heads = heads
+    d = Device(w)
+    d.copy_and_append()
+    out = torch.empty(tuple(q.shape), dtype=torch.float32, device="cuda")
+    pkv.paged_attention_decode(out, d.q, d.k_pool, d.v_pool, d.tables, d.lens, w.max_seq_len,
+                               w.scale, partition_size=partition, walker="vector")
+    err = max_err(out, expected_attention(w, *expected_pools(w)))
+    check_error("vector_bf16", err, TOL[w.dtype], f"forced vector walker G={heads // 8}")
+
+
+@pytest.mark.parametrize("name", ["opt13b_fp16", "long_gqa_fp8"])
+def test_gather_probe_reads_every_row_once(name):
+    """pkv_probe_gather XORs words 0 and 3 of each K piece and words 1 and 2
+    of each V piece it loads; XOR is order-free, so over all waves this must
+    equal the same fold over every row decode reads, each exactly once."""
+    w = wl.make(name, num_seqs=6, len_range=(1, 700))
+    d = Device(w)
+    k32 = w.k_pool.contiguous().view(torch.int32).numpy()
+    v32 = w.v_pool.contiguous().view(torch.int32).numpy()
+    row_words = k32.shape[-1]
+    want = 0
+    for i, n in enumerate(w.seq_lens):
+        for t in range(int(n)):
+            blk, slot = int(w.block_tables[i, t // w.block_size]), t % w.block_size
+            kr = k32[blk, :, slot].reshape(w.num_kv_heads, row_words // 4, 4)
+            vr = v32[blk, :, slot].reshape(w.num_kv_heads, row_words // 4, 4)
+            x = (np.bitwise_xor.reduce(kr[..., 0], axis=None) ^ np.bitwise_xor.reduce(kr[..., 3], axis=None)
+                 ^ np.bitwise_xor.reduce(vr[..., 1], axis=None) ^ np.bitwise_xor.reduce(vr[..., 2], axis=None))
+            want ^= int(x) & 0xFFFFFFFF
+    for waves, loads in ((256, 4), (1024, 8), (37, 2)):
+        sink = torch.zeros(waves, dtype=torch.int32, device="cuda")
+        pkv.probe_gather(d.k_pool, d.v_pool, d.tables, d.lens, waves, loads, sink)
+        got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
+        assert got == want, (name, waves, loads)

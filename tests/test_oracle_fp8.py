@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from oracle import (fp8_decode, fp8_dequantize_pool, fp8_encode, fp8_quantize,
-                    pool_after_append_fp8)
+                    pool_after_append_fp8, pool_after_append_multi_fp8)
 from oracle.fp8 import _encode_one
 
 ALL = np.arange(256, dtype=np.uint8)
@@ -130,3 +130,35 @@ def test_dequantize_pool_scales_each_head_by_its_own_factor():
     # the NaN code stays NaN, whatever the head's scale
     nan_pool = np.full((1, 4, 1, 2), 0x7F, dtype=np.uint8)
     assert np.isnan(fp8_dequantize_pool(nan_pool, scales)).all()
+
+
+def test_multi_token_append_equals_one_token_appends_in_order():
+    # nq new tokens per sequence at positions L-nq .. L-1 (blog.aqudi.me
+    # section 4: several tokens per pass); stored one at a time by the
+    # single-token append with lengths L-nq+1 .. L, the pools must be the same
+    rng = np.random.default_rng(41)
+    bs, hkv, d, nq = 8, 3, 16, 5
+    lens = np.array([0, 3, 5, 9, 17, 40], dtype=np.int32)      # includes L < nq and L = 0
+    nblk = [-(-int(n) // bs) for n in lens]
+    perm = rng.permutation(sum(nblk) + 4)
+    tables = np.full((len(lens), max(nblk)), -1, dtype=np.int32)
+    c = 0
+    for i, nb in enumerate(nblk):
+        tables[i, :nb] = perm[c:c + nb]
+        c += nb
+    k_pool = rng.integers(0, 256, size=(len(perm), hkv, bs, d)).astype(np.uint8)
+    v_pool = rng.integers(0, 256, size=(len(perm), hkv, bs, d)).astype(np.uint8)
+    k_new = (rng.standard_normal((len(lens), nq, hkv, d)) * 3).astype(np.float32)
+    v_new = (rng.standard_normal((len(lens), nq, hkv, d)) * 3).astype(np.float32)
+    ks = np.array([0.5, 0.03125, 2.0], dtype=np.float32)
+    vs = np.array([0.25, 1.0, 0.0078125], dtype=np.float32)
+    k2, v2 = pool_after_append_multi_fp8(k_pool, v_pool, k_new, v_new, ks, vs, tables, lens, bs)
+    kr, vr = k_pool, v_pool
+    for j in range(nq):
+        step_lens = np.where(lens - nq + j >= 0, lens - nq + j + 1, 0)
+        kr, vr = pool_after_append_fp8(kr, vr, k_new[:, j], v_new[:, j], ks, vs, tables,
+                                       step_lens, bs)
+    assert np.array_equal(k2, kr) and np.array_equal(v2, vr)
+    # sequence 3 (L = 9): token 4 (the last) sits at position 8: block 1, slot 0
+    assert np.array_equal(k2[tables[3, 1], :, 0], np.stack([fp8_quantize(k_new[3, 4, g], ks[g])
+                                                           for g in range(hkv)]))

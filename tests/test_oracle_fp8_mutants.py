@@ -59,6 +59,25 @@ def _dequant_scale_axis(axis=1, head0=False):
     return dequantize_pool
 
 
+def _multi_append_variant(reverse=False, shift=0):
+    def pool_after_append_multi_fp8(k_pool, v_pool, k_new, v_new, ks, vs, tables, lens, bs):
+        k_out, v_out = k_pool.copy(), v_pool.copy()
+        nq = k_new.shape[1]
+        for i in range(len(lens)):
+            n = int(lens[i])
+            for j in range(nq):
+                pos = n - nq + j + shift
+                src = nq - 1 - j if reverse else j
+                if n <= 0 or pos < 0 or pos >= n:
+                    continue
+                b = int(tables[i][pos // bs])
+                for g in range(k_pool.shape[1]):
+                    k_out[b, g, pos % bs] = f8.quantize(k_new[i][src][g], ks[g])
+                    v_out[b, g, pos % bs] = f8.quantize(v_new[i][src][g], vs[g])
+        return k_out, v_out
+    return pool_after_append_multi_fp8
+
+
 MUTANTS = {
     "exponent_bias_8": {"fp8_decode": _decode_with(_value_with(bias=8))},
     "subnormal_scale_2^-7": {"fp8_decode": _decode_with(_value_with(sub_exp=-7))},
@@ -68,6 +87,8 @@ MUTANTS = {
     "dequant_head0_scale_everywhere": {"fp8_dequantize_pool": _dequant_scale_axis(head0=True)},
     "dequant_scale_on_block_axis": {"fp8_dequantize_pool": _dequant_scale_axis(axis=0)},
     "dequant_scale_on_slot_axis": {"fp8_dequantize_pool": _dequant_scale_axis(axis=2)},
+    "multi_append_tokens_reversed": {"pool_after_append_multi_fp8": _multi_append_variant(reverse=True)},
+    "multi_append_one_early": {"pool_after_append_multi_fp8": _multi_append_variant(shift=-1)},
 }
 
 
