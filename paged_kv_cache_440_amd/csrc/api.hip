@@ -174,6 +174,7 @@ int prepare_attention(pkv::AttnParams& a, void* out, int out_dtype, const void* 
     a.scale = scale;
     a.part_tokens = (!balanced && parts > 1) ? partition_size : 0;
     a.col_tiles = tiles;
+    a.tiles_per_item = 1;
     a.max_parts = (int)parts;
     a.max_tokens = max_seq_len;
     a.num_items = (int)items;

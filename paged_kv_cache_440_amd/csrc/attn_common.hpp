@@ -86,5 +86,12 @@ __device__ __forceinline__ int tile_reach(const AttnParams& a, int L, int tile) 
     return L - a.num_queries + last / a.group + 1;
 }
 
+// The same for the group of tiles_per_item tiles one work item walks together:
+// the reach of its last tile.
+__device__ __forceinline__ int group_reach(const AttnParams& a, int L, int group) {
+    const int last = a.tiles_per_item * (group + 1) - 1;
+    return tile_reach(a, L, last < a.col_tiles ? last : a.col_tiles - 1);
+}
+
 }  // namespace
 }  // namespace pkv

@@ -161,7 +161,26 @@ __device__ __forceinline__ void store_out4(void* out, int out_dtype, size_t row,
         u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
 }
 
-template <typename S, int G_, bool STREAM, bool FP8 = false>
+// LDS-pointer form the direct-to-LDS load takes (its destination is M0-based).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Wait until at most N of this wave's vector-memory operations are in
+// flight (gfx9 s_waitcnt encoding; N < 16). The memory clobber keeps the
+// compiler from moving LDS reads of data those loads write above the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 16, "vmcnt");
+    __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// The workgroup's three K/V chunk buffers for shared walks (16 KB each).
+__device__ __forceinline__ char* shared_chunk(int b) {
+    __shared__ __attribute__((aligned(16))) char bufs[3][16384];
+    return bufs[b];
+}
+
+template <typename S, int G_, bool STREAM, bool FP8 = false, int NT = 1,
+          int WPS = (NT > 1 ? 1 : 2)>
 struct MfmaWalker {
     static constexpr bool kStream = STREAM;     // K/V load policy
     // persistent waves per compute unit in the balanced schedule: for 16-bit
@@ -175,14 +194,23 @@ struct MfmaWalker {
     static constexpr int QROW = 256;              // bytes of one q row (16-bit)
     static constexpr int KS = FP8 ? 2 : 4;        // 16-byte K loads per token row and lane
     static constexpr int CHUNK = 32;              // tokens per chunk
-    static constexpr int kMinWavesPerSimd = 2;
+    // NT 16-column tiles per wave share each K/V chunk (chunked prefill);
+    // WPS waves per SIMD bound the registers (one for several tiles whose
+    // K/V chunks are held in registers; the shared walk, which holds them
+    // in LDS, fits two tiles at two)
+    static constexpr int kTiles = NT;
+    static constexpr int kMinWavesPerSimd = WPS;
     // one lane's V piece of one token: 8 dims, 16-bit or codes
     using VPiece = std::conditional_t<FP8, u32x2, u32x4>;
     static_assert(S::bytes == 2 && G_ <= 16, "16-bit operands, at most 16 query heads");
 
-    f32x4 acc[8];       // O^T tiles: acc[c][i] = head n, dim 32q + 8i + c (unnormalised)
-    float m, l;         // head n: running max (log2 units), this lane's partial sum
-    u32x4 qb[4];        // B operand of Q^T for the four k-steps
+    // per tile t of the wave (lane (n, q) holds column n of each)
+    f32x4 acc[NT][8];   // O^T tiles: acc[t][c][i] = column n, dim 32q + 8i + c (unnormalised)
+    float m[NT], l[NT]; // column n: running max (log2 units), this lane's partial sum
+    u32x4 qb[NT][4];    // B operand of Q^T for the four k-steps
+    int ncols[NT];      // real columns of tile t: the rest are zero padding
+    int lim[NT];        // last token position column n of tile t may see (causal rule)
+    size_t orow[NT];    // output row of column n of tile t
     float kfac, vscale; // FP8: the kv head's K and V scales
 
     int wb, tv;         // table window: lane j holds the physical id of block wb + j
@@ -195,10 +223,7 @@ struct MfmaWalker {
     int* err;           // error word, or null
     int lane, n, q;
     int t_end;
-    int ncols;          // real columns of this tile: the rest are zero padding
-    int lim;            // last token position column n may see (causal rule)
     int mask_from;      // first position some column may not see
-    size_t orow;        // output row of column n
 
     __device__ __forceinline__ void init(int lane_id) {
         lane = lane_id;
@@ -206,40 +231,7 @@ struct MfmaWalker {
         q = lane_id >> 4;
     }
 
-    // Point the walker at 16-column tile `tile` of segment (seq, g) of length L.
-    __device__ __forceinline__ void begin(const AttnParams& a, int seq, int g, int L, int tile = 0) {
-        log2_bs = a.log2_bs;
-        bs_mask = (1 << a.log2_bs) - 1;
-        nblk_valid = (L + bs_mask) >> a.log2_bs;
-        max_phys = a.num_blocks;
-        err = a.err;
-        trow = a.block_tables + (size_t)seq * a.max_blocks;
-        head_stride_bytes = (size_t)a.num_kv_heads * ((size_t)ROW << a.log2_bs);
-        kvhead_off = (size_t)g * ((size_t)ROW << a.log2_bs);
-        kbase = reinterpret_cast<const char*>(a.k_pool);
-        vbase = reinterpret_cast<const char*>(a.v_pool);
-        // column c = 16 tile + n = (query token c / G, head g*G + c % G); a new
-        // token at position L - nq + j sees positions <= its own
-        const int nq = a.num_queries;
-        const int c0 = 16 * tile;
-        ncols = nq * G - c0 < 16 ? nq * G - c0 : 16;
-        lim = n < ncols ? L - nq + (c0 + n) / G : L - 1;
-        mask_from = L - nq + c0 / G + 1;
-        orow = out_row(a, seq, g, c0 + (n < ncols ? n : 0));
-        load_q(a, g, orow, n < ncols);
-        m = -__builtin_inff();
-        l = 0.f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    // Columns taken from several sequences that share the blocks of tokens
-    // [0, L) (the samples of one prompt): the tables of table_seq are walked,
-    // this lane's column n reads q row qrow_idx if active and a zero row
-    // otherwise, and every token of the walked range is visible to every
-    // column.
-    __device__ __forceinline__ void begin_columns(const AttnParams& a, int table_seq, int g, int L,
-                                                  size_t qrow_idx, bool active) {
+    __device__ __forceinline__ void begin_table(const AttnParams& a, int table_seq, int g, int L) {
         log2_bs = a.log2_bs;
         bs_mask = (1 << a.log2_bs) - 1;
         nblk_valid = (L + bs_mask) >> a.log2_bs;
@@ -250,31 +242,69 @@ struct MfmaWalker {
         kvhead_off = (size_t)g * ((size_t)ROW << a.log2_bs);
         kbase = reinterpret_cast<const char*>(a.k_pool);
         vbase = reinterpret_cast<const char*>(a.v_pool);
-        ncols = 16;
-        lim = L - 1;
-        mask_from = L;
-        orow = qrow_idx;
-        load_q(a, g, qrow_idx, active);
-        m = -__builtin_inff();
-        l = 0.f;
+        if constexpr (FP8) {
+            kfac = a.k_scales[g];
+            vscale = a.v_scales[g];
+        }
+    }
+
+    __device__ __forceinline__ void reset() {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NT; ++t) {
+            m[t] = -__builtin_inff();
+            l[t] = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    // Point the walker at the NT 16-column tiles NT*group .. of segment
+    // (seq, g) of length L: column c = 16 tile + n = (query token c / G, head
+    // g*G + c % G); a new token at position L - nq + j sees positions <= its own.
+    __device__ __forceinline__ void begin(const AttnParams& a, int seq, int g, int L, int group = 0) {
+        begin_table(a, seq, g, L);
+        const int nq = a.num_queries, cols = nq * G;
+        mask_from = L - nq + (16 * NT * group) / G + 1;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int c0 = 16 * (NT * group + t);
+            ncols[t] = cols - c0 < 16 ? cols - c0 : 16;       // <= 0 past the last column
+            const bool active = n < ncols[t];
+            const int c = active ? c0 + n : (c0 < cols ? c0 : cols - 1);
+            lim[t] = active ? L - nq + c / G : L - 1;
+            orow[t] = out_row(a, seq, g, c);
+            load_q(a, orow[t], active, qb[t]);
+        }
+        reset();
+    }
+
+    // Columns taken from several sequences that share the blocks of tokens
+    // [0, L) (the samples of one prompt): the tables of table_seq are walked,
+    // this lane's column n reads q row qrow_idx if active and a zero row
+    // otherwise, and every token of the walked range is visible to every
+    // column.
+    __device__ __forceinline__ void begin_columns(const AttnParams& a, int table_seq, int g, int L,
+                                                  size_t qrow_idx, bool active) {
+        static_assert(NT == 1, "one tile of sampled columns");
+        begin_table(a, table_seq, g, L);
+        ncols[0] = 16;
+        lim[0] = L - 1;
+        mask_from = L;
+        orow[0] = qrow_idx;
+        load_q(a, qrow_idx, active, qb[0]);
+        reset();
     }
 
     // q row `row` as the B operand of the four k-steps (zero if !active):
     // step s covers dims 32s + 8q .. +7 (16-bit K/V) or 64(s/2) + 16q +
-    // 8(s%2) .. +7 (FP8 codes), 16 consecutive bytes of q either way; and
-    // the kv head's scales for FP8 pools
-    __device__ __forceinline__ void load_q(const AttnParams& a, int g, size_t row, bool active) {
+    // 8(s%2) .. +7 (FP8 codes), 16 consecutive bytes of q either way
+    __device__ __forceinline__ void load_q(const AttnParams& a, size_t row, bool active,
+                                           u32x4 (&b)[4]) {
         const char* qrow = reinterpret_cast<const char*>(a.q) + row * QROW;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int d0 = FP8 ? 64 * (s >> 1) + 16 * q + 8 * (s & 1) : 32 * s + 8 * q;
-            qb[s] = active ? load16(qrow + 2 * d0) : u32x4{0u, 0u, 0u, 0u};
-        }
-        if constexpr (FP8) {
-            kfac = a.k_scales[g];
-            vscale = a.v_scales[g];
+            b[s] = active ? load16(qrow + 2 * d0) : u32x4{0u, 0u, 0u, 0u};
         }
     }
 
@@ -344,71 +374,84 @@ struct MfmaWalker {
         }
     }
 
-    // Scores of the chunk: k-slot j of group q is token 16 (j / 4) + 4q + j % 4.
+    // Scores of the chunk for every tile: k-slot j of group q is token
+    // 16 (j / 4) + 4q + j % 4. The K operands are built once for all tiles.
     __device__ __forceinline__ void scores(const u32x4 (&kt)[2][KS], float scale_log2,
-                                           float (&sc)[8]) {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+                                           float (&sc)[NT][8]) {
+        f32x4 s0[NT], s1[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) s0[t] = s1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            s0 = mfma_16x16x32(S{}, k_operand(kt[0], s), qb[s], s0);
-            s1 = mfma_16x16x32(S{}, k_operand(kt[1], s), qb[s], s1);
+            const u32x4 a0 = k_operand(kt[0], s), a1 = k_operand(kt[1], s);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                s0[t] = mfma_16x16x32(S{}, a0, qb[t][s], s0[t]);
+                s1[t] = mfma_16x16x32(S{}, a1, qb[t][s], s1[t]);
+            }
         }
         const float f = FP8 ? scale_log2 * kfac : scale_log2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sc[i] = s0[i] * f;
-            sc[4 + i] = s1[i] * f;
-        }
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sc[t][i] = s0[t][i] * f;
+                sc[t][4 + i] = s1[t][i] * f;
+            }
     }
 
     template <bool TAIL>
-    __device__ __forceinline__ void softmax_pv(int c0, float (&sc)[8], VPiece (&vt)[8]) {
+    __device__ __forceinline__ void softmax_pv(int c0, float (&sc)[NT][8], VPiece (&vt)[8]) {
         // Scores are masked by the range end and by column n's causal limit;
         // V pieces only by the range end: lane n's V piece holds dims
         // 8n .. 8n+7 of a token for every column, and a token past one
         // column's limit is still real data (its weight there is 0).
-        bool valid[8];
+        if constexpr (TAIL) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int tok = c0 + 16 * (j >> 2) + 4 * q + (j & 3);
-            valid[j] = !TAIL || (tok < t_end && tok <= lim);
-            if constexpr (TAIL) {
-                const bool in_range = tok < t_end;
+            for (int j = 0; j < 8; ++j) {
+                const bool in_range = c0 + 16 * (j >> 2) + 4 * q + (j & 3) < t_end;
 #pragma unroll
                 for (int w = 0; w < (int)(sizeof(VPiece) / 4); ++w)
                     vt[j][w] = in_range ? vt[j][w] : 0u;
             }
         }
-        if constexpr (TAIL) {
+        // P^T of every tile as a 16-bit high part and the 16-bit residual
+        u32x4 bhi[NT], blo[NT];
+        float alpha[NT];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sc[j] = valid[j] ? sc[j] : -__builtin_inff();
-        }
-        float mx = sc[0];
+        for (int t = 0; t < NT; ++t) {
+            bool valid[8];
 #pragma unroll
-        for (int j = 1; j < 8; ++j) mx = __builtin_fmaxf(mx, sc[j]);
-        mx = strided_max<16>(mx);
-        // Outside masked chunks every token is valid and mx is finite. In a
-        // masked chunk a column may have seen no valid token yet: then m_new is
-        // -inf, every p is 0 and alpha (1) only multiplies zeros.
-        const float m_new = __builtin_fmaxf(m, mx);
-        const float alpha = (TAIL && m_new == -__builtin_inff()) ? 1.f : fast_exp2(m - m_new);
-        float p[8], ps = 0.f;
+            for (int j = 0; j < 8; ++j) {
+                const int tok = c0 + 16 * (j >> 2) + 4 * q + (j & 3);
+                valid[j] = !TAIL || (tok < t_end && tok <= lim[t]);
+                if constexpr (TAIL) sc[t][j] = valid[j] ? sc[t][j] : -__builtin_inff();
+            }
+            float mx = sc[t][0];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            p[j] = (TAIL && !valid[j]) ? 0.f : fast_exp2(sc[j] - m_new);
-            ps += p[j];
-        }
-        l = l * alpha + ps;
-        m = m_new;
-        // P^T as a 16-bit high part and the 16-bit residual
-        u32x4 bhi, blo;
+            for (int j = 1; j < 8; ++j) mx = __builtin_fmaxf(mx, sc[t][j]);
+            mx = strided_max<16>(mx);
+            // Outside masked chunks every token is valid and mx is finite. In a
+            // masked chunk a column may have seen no valid token yet: then m_new
+            // is -inf, every p is 0 and alpha (1) only multiplies zeros.
+            const float m_new = __builtin_fmaxf(m[t], mx);
+            alpha[t] = (TAIL && m_new == -__builtin_inff()) ? 1.f : fast_exp2(m[t] - m_new);
+            float p[8], ps = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const uint32_t h0 = to16(S{}, p[2 * w]), h1 = to16(S{}, p[2 * w + 1]);
-            const uint32_t r0 = to16(S{}, p[2 * w] - from16(S{}, h0));
-            const uint32_t r1 = to16(S{}, p[2 * w + 1] - from16(S{}, h1));
-            bhi[w] = h0 | (h1 << 16);
-            blo[w] = r0 | (r1 << 16);
+            for (int j = 0; j < 8; ++j) {
+                p[j] = (TAIL && !valid[j]) ? 0.f : fast_exp2(sc[t][j] - m_new);
+                ps += p[j];
+            }
+            l[t] = l[t] * alpha[t] + ps;
+            m[t] = m_new;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t h0 = to16(S{}, p[2 * w]), h1 = to16(S{}, p[2 * w + 1]);
+                const uint32_t r0 = to16(S{}, p[2 * w] - from16(S{}, h0));
+                const uint32_t r1 = to16(S{}, p[2 * w + 1] - from16(S{}, h1));
+                bhi[t][w] = h0 | (h1 << 16);
+                blo[t][w] = r0 | (r1 << 16);
+            }
         }
         // the eight V pieces as pairs of S values: hv[j][k] = dims 2k, 2k+1 of token j
         uint32_t hv[8][4];
@@ -424,6 +467,18 @@ struct MfmaWalker {
                 for (int k = 0; k < 4; ++k) hv[j][k] = vt[j][k];
             }
         }
+        // Rescale a tile's accumulators only when some column's max grew: alpha
+        // is exactly 1 otherwise (exp2 of 0), and past the first chunks the
+        // running max rarely moves, so most chunks skip these 32 products
+        // (the result bits are the same either way). Decode walks only: with
+        // several tiles the branch costs registers, and on MI355X the chunked
+        // prefill ran 9% slower with it.
+        if constexpr (NT == 1) {
+            if (__ballot(alpha[0] != 1.f) != 0) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[0][c] = acc[0][c] * alpha[0];
+            }
+        }
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             // V^T tile c: element c of the eight V pieces, token order as k-slots
@@ -433,9 +488,12 @@ struct MfmaWalker {
                 const uint32_t x = hv[2 * w][c >> 1], y = hv[2 * w + 1][c >> 1];
                 av[w] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
             }
-            f32x4 o = acc[c] * alpha;
-            o = mfma_16x16x32(S{}, av, bhi, o);
-            acc[c] = mfma_16x16x32(S{}, av, blo, o);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const f32x4 o =
+                    mfma_16x16x32(S{}, av, bhi[t], NT == 1 ? acc[t][c] : acc[t][c] * alpha[t]);
+                acc[t][c] = mfma_16x16x32(S{}, av, blo[t], o);
+            }
         }
     }
 
@@ -446,7 +504,7 @@ struct MfmaWalker {
     __device__ __forceinline__ void walk(int t_begin, int t_stop, float scale_log2) {
         u32x4 kt[2][KS];
         VPiece vt[8];
-        float sc[8];
+        float sc[NT][8];
         for (int w0 = t_begin; w0 < t_stop;) {
             const int first_block = w0 >> log2_bs;
             const int win_end = (first_block + 64) << log2_bs;
@@ -474,33 +532,125 @@ struct MfmaWalker {
         }
     }
 
-    __device__ __forceinline__ float total_sum() { return strided_sum<16>(l); }
+    // -- shared walks: the four waves of a workgroup walk the same range ----
+    // Each 32-token chunk is 16 wave-wide loads (8 of K: token tile t, k-step
+    // s; 8 of V: half h, row j), laid out in LDS in the lanes' operand order:
+    // load i puts lane l's 16 bytes at i * 1024 + 16 l. Wave w issues loads
+    // 4w .. 4w+3 straight into LDS (global_load_lds, no registers held), two
+    // chunks ahead of the compute; after a wait and a workgroup barrier every
+    // wave reads the whole chunk back conflict-free and runs its own tiles.
+    static constexpr int kSharedLoads = 4;        // per wave and chunk (16-bit K/V)
+
+    __device__ __forceinline__ void issue_shared(int c0, int b, int wave) {
+        static_assert(!FP8, "shared walks read 16-bit K/V");
+        char* base = shared_chunk(b);
+#pragma unroll
+        for (int u = 0; u < kSharedLoads; ++u) {
+            const int i = wave * kSharedLoads + u;       // wave-uniform
+            const char* p;
+            if (i < 8) {                                 // K: tile t = i / 4, step s = i % 4
+                int tok = c0 + 16 * (i >> 2) + n;
+                tok = tok < t_end ? tok : t_end - 1;
+                p = kbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes + kvhead_off +
+                    (uint32_t)((tok & bs_mask) * ROW + 16 * q + 64 * (i & 3));
+            } else {                                     // V: half h = (i - 8) / 4, row j
+                const int last = t_end - 1;
+                int tok = c0 + 16 * ((i - 8) >> 2) + 4 * q + (i & 3);
+                tok = tok < last ? tok : last;
+                p = vbase + (size_t)phys((tok >> log2_bs) - wb) * head_stride_bytes + kvhead_off +
+                    (uint32_t)((tok & bs_mask) * ROW + 16 * n);
+            }
+            __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(base + i * 1024), 16, 0, 0);
+        }
+    }
+
+    __device__ __forceinline__ void read_shared(int b, u32x4 (&kt)[2][KS], VPiece (&vt)[8]) {
+        const char* base = shared_chunk(b) + 16 * lane;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kt[i >> 2][i & 3] = *reinterpret_cast<const u32x4*>(base + i * 1024);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vt[j] = *reinterpret_cast<const u32x4*>(base + (8 + j) * 1024);
+    }
+
+    // Tokens [t_begin, t_stop) for this wave's tiles, the chunks shared with
+    // the other three waves of the workgroup, which walk the same range
+    // (every wave of the workgroup must call this with the same range).
+    __device__ __forceinline__ void walk_shared(int t_begin, int t_stop, float scale_log2,
+                                                int wave) {
+        u32x4 kt[2][KS];
+        VPiece vt[8];
+        float sc[NT][8];
+        for (int w0 = t_begin; w0 < t_stop;) {
+            const int first_block = w0 >> log2_bs;
+            const int win_end = (first_block + 64) << log2_bs;
+            const int w_end = win_end < t_stop ? win_end : t_stop;
+            load_window(first_block);
+            t_end = w_end;
+            const int nch = (w_end - w0 + CHUNK - 1) / CHUNK;
+            issue_shared(w0, 0, wave);
+            if (nch > 1) issue_shared(w0 + CHUNK, 1, wave);
+            for (int k = 0; k < nch; ++k) {
+                const int c = w0 + k * CHUNK;
+                // this wave's loads of chunk k are done (those of chunk k + 1 may fly)
+                if (k + 1 < nch)
+                    wait_vmcnt<kSharedLoads>();
+                else
+                    wait_vmcnt<0>();
+                // ... and every wave's: chunk k is in LDS, and chunk k - 1's
+                // buffer, which chunk k + 2 takes next, has been read by all
+                __syncthreads();
+                if (k + 2 < nch) issue_shared(c + 2 * CHUNK, (k + 2) % 3, wave);
+                read_shared(k % 3, kt, vt);
+                scores(kt, scale_log2, sc);
+                if (k == nch - 1 || c + CHUNK > mask_from)
+                    softmax_pv<true>(c, sc, vt);
+                else
+                    softmax_pv<false>(c, sc, vt);
+            }
+            // the next window's first loads reuse buffers 0 and 1
+            __syncthreads();
+            w0 = w_end;
+        }
+    }
+
+    __device__ __forceinline__ float total_sum(int t) { return strided_sum<16>(l[t]); }
 
     __device__ __forceinline__ void write_final(const AttnParams& a, int seq, int g) {
-        const float lsum = total_sum();
-        // 0: a query before the start; FP8 values carry the kv head's V scale
-        const float inv = lsum > 0.f ? (FP8 ? vscale / lsum : 1.0f / lsum) : 0.f;
         void* out = a.out;
         const int dt = a.out_dtype;
-        store_column_tile(acc, inv, orow, n < ncols,
-                          [&](size_t r, int piece, f32x4 v) { store_out4(out, dt, r, piece, v); });
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float lsum = total_sum(t);
+            // 0: a query before the start; FP8 values carry the kv head's V scale
+            const float inv = lsum > 0.f ? (FP8 ? vscale / lsum : 1.0f / lsum) : 0.f;
+            store_column_tile(acc[t], inv, orow[t], n < ncols[t],
+                              [&](size_t r, int piece, f32x4 v) { store_out4(out, dt, r, piece, v); });
+        }
     }
 
+    // Partial results: column n of tile t to workspace row row0 + (16 t + n) * row_stride.
     __device__ __forceinline__ void write_partial(const AttnParams& a, size_t row0,
                                                   size_t row_stride) {
-        write_partial_at(a, row0 + (size_t)n * row_stride, n < ncols);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            write_tile_partial(a, t, row0 + (size_t)(16 * t + n) * row_stride, n < ncols[t]);
     }
 
-    // Column n's partial result into workspace row `row` (this lane's), if active.
+    // Column n's partial result (tile 0) into workspace row `row` (this lane's), if active.
     __device__ __forceinline__ void write_partial_at(const AttnParams& a, size_t row, bool active) {
-        const float lsum = total_sum();
+        write_tile_partial(a, 0, row, active);
+    }
+
+    __device__ __forceinline__ void write_tile_partial(const AttnParams& a, int t, size_t row,
+                                                       bool active) {
+        const float lsum = total_sum(t);
         float* ws = a.ws_acc;
-        store_column_tile(acc, FP8 ? vscale : 1.f, row, active, [&](size_t r, int piece, f32x4 v) {
+        store_column_tile(acc[t], FP8 ? vscale : 1.f, row, active, [&](size_t r, int piece, f32x4 v) {
             *reinterpret_cast<f32x4*>(ws + r * D + 4 * piece) = v;
         });
         if (!active) return;
         if (q == 0) {
-            a.ws_ml[2 * row] = m;
+            a.ws_ml[2 * row] = m[t];
             a.ws_ml[2 * row + 1] = lsum;
         }
     }

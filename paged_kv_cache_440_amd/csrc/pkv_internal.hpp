@@ -52,6 +52,8 @@ struct AttnParams {
     int col_tiles;                 // 16-column tiles per segment: ceil(columns / 16); more
                                    // than one only for the matrix-core walker, under the
                                    // single pass or fixed partitions
+    int tiles_per_item;            // tiles one work item (a wave, or a workgroup for
+                                   // chunked prefill) walks together, sharing each K/V chunk
     int dtype;                     // q / K / V element type (16/32-bit path)
     int* err;                      // error word (pkv_set_error_word), or null
     int force_vector;              // PKV_WALKER_VECTOR: grouped heads on the vector units
