@@ -601,6 +601,28 @@ def main():
     log(f"[bench] paged gather probe: {gather_gbps:.0f} GB/s ({g_us:.1f} us; {g_per_cu} waves "
         f"per CU, {g_loads} loads of K and of V per round); sweep "
         + ", ".join(f"{c}/{l}: {x:.0f}" for x, c, l, _ in gather))
+    # the same rows read with the matrix-core walker's load shapes (K as
+    # 16-row operand tiles: 64 bytes of each row per load)
+    gather_mfma = []
+    for per_cu in (4, 8, 16):
+        for chunks in (1, 2):
+            run_m = lambda: pkv.probe_gather_mfma(kp, vp, tables, lens, per_cu * cus, chunks, gsink,
+                                                  stream=stream)
+            for _ in range(2):
+                run_m()
+            ge = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(10)]
+            for a, b in ge:
+                a.record(stream)
+                run_m()
+                b.record(stream)
+            torch.cuda.synchronize()
+            m_us = float(np.mean([a.elapsed_time(b) for a, b in ge])) * 1e3
+            gather_mfma.append((kv_bytes / (m_us * 1e-6) / 1e9, per_cu, chunks, m_us))
+    gm_gbps, gm_per_cu, gm_chunks, gm_us = max(gather_mfma)
+    log(f"[bench] paged gather probe, matrix-core load shapes: {gm_gbps:.0f} GB/s ({gm_us:.1f} us; "
+        f"{gm_per_cu} waves per CU, {gm_chunks} chunks per round); sweep "
+        + ", ".join(f"{c}/{l}: {x:.0f}" for x, c, l, _ in gather_mfma))
 
     unique_bytes = w.unique_kv_bytes()
     # the roofline counts what HBM must deliver, each distinct K/V row once,
@@ -671,6 +693,10 @@ def main():
         "gather_probe_us": g_us,
         "gather_probe_config": {"waves_per_cu": g_per_cu, "loads_per_round": g_loads},
         "walk_frac_of_gather_probe": g_us / (walk_ms * 1e3),
+        "gather_mfma_probe_gbps": gm_gbps,
+        "gather_mfma_probe_us": gm_us,
+        "gather_mfma_probe_config": {"waves_per_cu": gm_per_cu, "chunks_per_round": gm_chunks},
+        "walk_frac_of_gather_mfma_probe": gm_us / (walk_ms * 1e3),
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,

@@ -19,6 +19,10 @@
  *                    nothing: the read ceiling of the paged access pattern
  *                    itself (scattered bs x row-byte tiles, [summary]
  *                    section "커널 비용과 블록 크기" on block size and access).
+ *   pkv_probe_gather_mfma  the same rows, split the same way, read with the
+ *                    matrix-core walker's own load shapes (K as 16-row
+ *                    operand tiles, 64 bytes of each row per wave load; V as
+ *                    4-row pieces): the ceiling of that walker's access pattern.
  *
  * Conventions are those of pkv.h: device pointers owned by the caller, work
  * enqueued on `stream` (a hipStream_t, NULL = null stream), a pkv_status
@@ -70,6 +74,27 @@ PKV_API int pkv_probe_gather(const void* k_pool, const void* v_pool, const int32
                              int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs,
                              int num_kv_heads, int row_bytes, int block_size, int num_blocks,
                              int waves, int loads_per_round, uint32_t* sink, void* stream);
+
+/*
+ * Read the same rows as pkv_probe_gather (same tables, lengths, pools and
+ * split of 32-token units over `waves` persistent waves), a 32-token chunk
+ * at a time with the load shapes of the matrix-core walker: for K, two
+ * 16-token tiles, each wave load giving lane (n, q) (n = lane % 16,
+ * q = lane / 16) the 16 bytes at byte 64 s + 16 q of the tile's row n
+ * (row_bytes / 64 loads per tile); for V, eight wave loads giving lane
+ * (n, q) bytes (row_bytes / 16) n .. + row_bytes / 16 - 1 of token
+ * 16 h + 4 q + j of the chunk (h < 2, j < 4). chunks_per_round (1 or 2)
+ * chunks are requested before any is used. As in the walker, lanes whose
+ * row is at or past a range's end re-read the range's last row. sink gets
+ * one uint32 per wave (`waves` words): the XOR of words 0 and 3 of every
+ * 16-byte piece of the K rows and words 1 and 2 of every 16-byte piece of
+ * the V rows in range (each once), the same fold as pkv_probe_gather.
+ */
+PKV_API int pkv_probe_gather_mfma(const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, int max_blocks_per_seq,
+                                  const int32_t* seq_lens, int num_seqs, int num_kv_heads,
+                                  int row_bytes, int block_size, int num_blocks, int waves,
+                                  int chunks_per_round, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,6 +27,7 @@ _API = (
     "probe_read",
     "probe_copy",
     "probe_gather",
+    "probe_gather_mfma",
     "library",
     "DTYPE_CODES",
     "PARTITION_BALANCED",

@@ -89,6 +89,8 @@ def library() -> ctypes.CDLL:
     lib.pkv_probe_read_sink_words.restype = Z
     lib.pkv_probe_gather.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, P, P]
     lib.pkv_probe_gather.restype = I
+    lib.pkv_probe_gather_mfma.argtypes = [P, P, P, I, P, I, I, I, I, I, I, I, P, P]
+    lib.pkv_probe_gather_mfma.restype = I
     lib.pkv_probe_copy.argtypes = [P, P, Z, P]
     lib.pkv_probe_copy.restype = I
     _lib = lib
@@ -393,6 +395,22 @@ def probe_gather(k_pool, v_pool, block_tables, seq_lens, waves, loads_per_round,
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(seq_lens, "seq_lens", torch.int32), b, hkv, d * k_pool.element_size(), bs, nb,
         int(waves), int(loads_per_round), _dev(sink, "sink", torch.int32), _stream(stream)))
+
+
+def probe_gather_mfma(k_pool, v_pool, block_tables, seq_lens, waves, chunks_per_round, sink,
+                      stream=None) -> None:
+    """pkv_probe_gather_mfma: the rows probe_gather reads, with the matrix-core
+    walker's load shapes, chunks_per_round (1 or 2) 32-token chunks requested
+    per round; sink is an int32 device tensor of at least `waves` words."""
+    nb, hkv, bs, d, code = _pool_geometry(k_pool, v_pool)
+    b = block_tables.shape[0]
+    if sink.numel() < waves:
+        raise ValueError(f"sink must hold {waves} words")
+    _check("pkv_probe_gather_mfma", library().pkv_probe_gather_mfma(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens", torch.int32), b, hkv, d * k_pool.element_size(), bs, nb,
+        int(waves), int(chunks_per_round), _dev(sink, "sink", torch.int32), _stream(stream)))
 
 
 def probe_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

@@ -452,6 +452,21 @@ def test_gather_probe_validation(lib):
                                     a["Hkv"], a["row"], a["bs"], a["nb"], a["waves"], a["loads"],
                                     a["sink"], None)
 
+    def gm(**kw):
+        a = dict(args, loads=1)
+        a.update(kw)
+        return lib.pkv_probe_gather_mfma(a["k"], a["v"], a["tables"], a["max_blocks"], a["lens"],
+                                         a["B"], a["Hkv"], a["row"], a["bs"], a["nb"], a["waves"],
+                                         a["loads"], a["sink"], None)
+
+    for f in (g, gm):
+        assert f(row=64) == UNSUPPORTED
+        assert f(bs=12) == UNSUPPORTED
+        assert f(sink=0) == INVALID
+        assert f(waves=0) == INVALID
+        assert f(k=FAKE + 4) == INVALID
+    assert gm(loads=4) == UNSUPPORTED
+    assert gm(loads=0) == UNSUPPORTED
     assert g(row=64) == UNSUPPORTED
     assert g(loads=3) == UNSUPPORTED
     assert g(bs=12) == UNSUPPORTED

@@ -448,9 +448,10 @@ def test_vector_walker_forced_on_grouped_heads(heads, partition):
 
 @pytest.mark.parametrize("name", ["opt13b_fp16", "long_gqa_fp8"])
 def test_gather_probe_reads_every_row_once(name):
-    """pkv_probe_gather XORs words 0 and 3 of each K piece and words 1 and 2
-    of each V piece it loads; XOR is order-free, so over all waves this must
-    equal the same fold over every row decode reads, each exactly once."""
+    """pkv_probe_gather (and pkv_probe_gather_mfma) XOR words 0 and 3 of each
+    K piece and words 1 and 2 of each V piece they load; XOR is order-free, so
+    over all waves this must equal the same fold over every row decode reads,
+    each exactly once."""
     w = wl.make(name, num_seqs=6, len_range=(1, 700))
     d = Device(w)
     k32 = w.k_pool.contiguous().view(torch.int32).numpy()
@@ -470,3 +471,9 @@ def test_gather_probe_reads_every_row_once(name):
         pkv.probe_gather(d.k_pool, d.v_pool, d.tables, d.lens, waves, loads, sink)
         got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
         assert got == want, (name, waves, loads)
+    # the matrix-core walker's load shapes read the same pieces, each once
+    for waves, chunks in ((256, 1), (1024, 2), (37, 2), (5, 1)):
+        sink = torch.zeros(waves, dtype=torch.int32, device="cuda")
+        pkv.probe_gather_mfma(d.k_pool, d.v_pool, d.tables, d.lens, waves, chunks, sink)
+        got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
+        assert got == want, (name, "mfma shapes", waves, chunks)
