@@ -608,6 +608,23 @@ hipError_t launch_fp8_policy(const AttnParams& a, hipStream_t stream) {
 // loaded once, straight into LDS, two chunks ahead) and each runs NT tiles
 // on it, so the cache is read once per group instead of once per tile.
 // Partial rows as in paged_decode_kernel.
+// The sequence of rank r when sequences are ordered by decreasing length
+// (ties by index), for up to 64 sequences; sequence r beyond that. Workgroups
+// take sequences in this order, so the longest walks start first and the
+// ones that wait for a free compute unit are the shortest.
+__device__ __forceinline__ int seq_of_length_rank(const AttnParams& a, int r) {
+    if (a.num_seqs > 64) return r;
+    const int lane = threadIdx.x & 63;
+    const int Lj = lane < a.num_seqs ? clamp_len(a, a.seq_lens[lane]) : -1;
+    int rank = 0;
+    for (int k = 0; k < a.num_seqs; ++k) {
+        const int Lk = __shfl(Lj, k, 64);
+        rank += (Lk > Lj || (Lk == Lj && k < lane)) ? 1 : 0;
+    }
+    const unsigned long long hit = __ballot(lane < a.num_seqs && rank == r);
+    return hit ? __builtin_ctzll(hit) : r;
+}
+
 template <class Walker>
 __global__ __launch_bounds__(64 * kWaves)
 __attribute__((amdgpu_waves_per_eu(Walker::kMinWavesPerSimd)))
@@ -619,7 +636,8 @@ void paged_prefill_kernel(const AttnParams a) {
     const int sg = blockIdx.x % groups;              // the group of tiles of this workgroup
     const int rest = blockIdx.x / groups;
     const int g = rest % a.num_kv_heads;
-    const int seq = (rest / a.num_kv_heads) % a.num_seqs;
+    const int seq = __builtin_amdgcn_readfirstlane(
+        seq_of_length_rank(a, (rest / a.num_kv_heads) % a.num_seqs));
     const int part = rest / (a.num_kv_heads * a.num_seqs);
     const int raw_len = a.seq_lens[seq];
     report_if(a.err, threadIdx.x == 0 && g == 0 && part == 0 && sg == 0 &&
@@ -658,9 +676,11 @@ void paged_prefill_kernel(const AttnParams a) {
 // Tiles each wave runs: with shared chunks (16-bit K/V) four waves of
 // kPrefillTiles tiles walk together, two waves per SIMD (measured on MI355X
 // on the OPT-13B prefill layer: 289 us, against 306 us for one tile per wave
-// and 385-397 us for two or four tiles at one wave per SIMD); FP8 pools use
-// one wave of kPrefillTilesFp8 tiles per work item, one wave per SIMD (two
-// tiles per wave: 316 us against 622 us for one, on 16-bit pools).
+// and 385-397 us for two or four tiles at one wave per SIMD; with the output
+// tiles moved into the chunk buffers, so that two workgroups fit a compute
+// unit's LDS, and the longest sequences dispatched first: 243 us); FP8 pools
+// use one wave of kPrefillTilesFp8 tiles per work item, one wave per SIMD
+// (two tiles per wave: 316 us against 622 us for one, on 16-bit pools).
 #ifndef PKV_PREFILL_TILES
 #define PKV_PREFILL_TILES 2
 #endif
@@ -681,7 +701,7 @@ hipError_t launch_multi_typed(const AttnParams& a, hipStream_t stream) {
             b.num_items = (int)((long long)b.max_parts * b.num_seqs * b.num_kv_heads * groups);
             return launch_partitioned<MfmaWalker<S, G, STREAM, FP8, kPrefillTilesFp8>>(b, stream);
         } else {
-            using W = MfmaWalker<S, G, STREAM, false, kPrefillTiles, kPrefillWavesPerSimd>;
+            using W = MfmaWalker<S, G, STREAM, false, kPrefillTiles, kPrefillWavesPerSimd, true>;
             b.tiles_per_item = kWaves * kPrefillTiles;
             const long long groups = (b.col_tiles + b.tiles_per_item - 1) / b.tiles_per_item;
             const long long wgs = (long long)b.max_parts * b.num_seqs * b.num_kv_heads * groups;

@@ -119,10 +119,9 @@ __device__ __forceinline__ f32x4 (*wave_tile())[32] {
 }
 
 template <class Store>
-__device__ __forceinline__ void store_column_tile(const f32x4 (&acc)[8], float scale, size_t row,
-                                                  bool active, Store store) {
+__device__ __forceinline__ void store_column_tile(f32x4 (*t)[32], const f32x4 (&acc)[8], float scale,
+                                                  size_t row, bool active, Store store) {
     const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
-    f32x4 (*t)[32] = wave_tile();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         t[n][8 * q + 2 * i] = f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]} * scale;
@@ -173,14 +172,24 @@ __device__ __forceinline__ void wait_vmcnt() {
     __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// The workgroup's three K/V chunk buffers for shared walks (16 KB each).
+// The workgroup's K/V chunk buffers for shared walks (16 KB each): chunks
+// are requested kSharedBufs - 1 ahead (four buffers measured no faster than
+// three on MI355X). Once a shared walk is over they hold the waves' output
+// tiles (8 KB per wave), so a workgroup needs 48 KB of LDS and two fit a
+// compute unit with room to spare.
+#ifndef PKV_SHARED_BUFS
+#define PKV_SHARED_BUFS 3
+#endif
+constexpr int kSharedBufs = PKV_SHARED_BUFS;
+static_assert(kSharedBufs >= 3 && kSharedBufs <= 4 && kSharedBufs * 16384 >= kWaves * 8192,
+              "shared chunk buffers");
 __device__ __forceinline__ char* shared_chunk(int b) {
-    __shared__ __attribute__((aligned(16))) char bufs[3][16384];
+    __shared__ __attribute__((aligned(16))) char bufs[kSharedBufs][16384];
     return bufs[b];
 }
 
 template <typename S, int G_, bool STREAM, bool FP8 = false, int NT = 1,
-          int WPS = (NT > 1 ? 1 : 2)>
+          int WPS = (NT > 1 ? 1 : 2), bool SHARED = false>
 struct MfmaWalker {
     static constexpr bool kStream = STREAM;     // K/V load policy
     // persistent waves per compute unit in the balanced schedule: for 16-bit
@@ -587,33 +596,49 @@ struct MfmaWalker {
             load_window(first_block);
             t_end = w_end;
             const int nch = (w_end - w0 + CHUNK - 1) / CHUNK;
-            issue_shared(w0, 0, wave);
-            if (nch > 1) issue_shared(w0 + CHUNK, 1, wave);
+            constexpr int AHEAD = kSharedBufs - 1;     // chunks requested ahead of the one in use
+#pragma unroll
+            for (int k = 0; k < AHEAD; ++k)
+                if (k < nch) issue_shared(w0 + k * CHUNK, k, wave);
             for (int k = 0; k < nch; ++k) {
                 const int c = w0 + k * CHUNK;
-                // this wave's loads of chunk k are done (those of chunk k + 1 may fly)
-                if (k + 1 < nch)
+                // this wave's loads of chunk k are done (those of the chunks
+                // after it may fly)
+                const int later = nch - 1 - k < AHEAD - 1 ? nch - 1 - k : AHEAD - 1;
+                if (later >= 2)
+                    wait_vmcnt<2 * kSharedLoads>();
+                else if (later == 1)
                     wait_vmcnt<kSharedLoads>();
                 else
                     wait_vmcnt<0>();
                 // ... and every wave's: chunk k is in LDS, and chunk k - 1's
-                // buffer, which chunk k + 2 takes next, has been read by all
+                // buffer, which chunk k + AHEAD takes next, has been read by all
                 __syncthreads();
-                if (k + 2 < nch) issue_shared(c + 2 * CHUNK, (k + 2) % 3, wave);
-                read_shared(k % 3, kt, vt);
+                if (k + AHEAD < nch) issue_shared(c + AHEAD * CHUNK, (k + AHEAD) % kSharedBufs, wave);
+                read_shared(k % kSharedBufs, kt, vt);
                 scores(kt, scale_log2, sc);
                 if (k == nch - 1 || c + CHUNK > mask_from)
                     softmax_pv<true>(c, sc, vt);
                 else
                     softmax_pv<false>(c, sc, vt);
             }
-            // the next window's first loads reuse buffers 0 and 1
+            // the next window's first loads reuse the first buffers
             __syncthreads();
             w0 = w_end;
         }
     }
 
     __device__ __forceinline__ float total_sum(int t) { return strided_sum<16>(l[t]); }
+
+    // LDS for the output transposes: the wave's own slice, or, after a
+    // shared walk (SHARED: the workgroup walks with walk_shared), the wave's
+    // 8 KB of the chunk buffers, which the walk has finished with
+    __device__ __forceinline__ static f32x4 (*out_tile())[32] {
+        if constexpr (SHARED)
+            return reinterpret_cast<f32x4(*)[32]>(shared_chunk(0) + 8192 * (threadIdx.x >> 6));
+        else
+            return wave_tile();
+    }
 
     __device__ __forceinline__ void write_final(const AttnParams& a, int seq, int g) {
         void* out = a.out;
@@ -623,7 +648,7 @@ struct MfmaWalker {
             const float lsum = total_sum(t);
             // 0: a query before the start; FP8 values carry the kv head's V scale
             const float inv = lsum > 0.f ? (FP8 ? vscale / lsum : 1.0f / lsum) : 0.f;
-            store_column_tile(acc[t], inv, orow[t], n < ncols[t],
+            store_column_tile(out_tile(), acc[t], inv, orow[t], n < ncols[t],
                               [&](size_t r, int piece, f32x4 v) { store_out4(out, dt, r, piece, v); });
         }
     }
@@ -645,7 +670,8 @@ struct MfmaWalker {
                                                        bool active) {
         const float lsum = total_sum(t);
         float* ws = a.ws_acc;
-        store_column_tile(acc[t], FP8 ? vscale : 1.f, row, active, [&](size_t r, int piece, f32x4 v) {
+        store_column_tile(out_tile(), acc[t], FP8 ? vscale : 1.f, row, active,
+                          [&](size_t r, int piece, f32x4 v) {
             *reinterpret_cast<f32x4*>(ws + r * D + 4 * piece) = v;
         });
         if (!active) return;
