@@ -495,7 +495,10 @@ struct MfmaWalker {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const uint32_t x = hv[2 * w][c >> 1], y = hv[2 * w + 1][c >> 1];
-                av[w] = (c & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+                // low halves of x and y (c even) or high halves (c odd), x's
+                // first, in one byte permute (v_perm_b32: selector bytes 0-3
+                // pick bytes of the second operand, 4-7 of the first)
+                av[w] = __builtin_amdgcn_perm(y, x, (c & 1) ? 0x07060302u : 0x05040100u);
             }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
