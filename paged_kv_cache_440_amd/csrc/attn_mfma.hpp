@@ -74,16 +74,26 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(F16, const u32x4& a, const u32x4&
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// fp32 -> 16-bit (round to nearest even), as the low bits of a dword
-__device__ __forceinline__ uint32_t to16(BF16, float x) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 values -> two 16-bit values (round to nearest even) in one dword,
+// x in the low half: one v_cvt_pk_{bf16,f16}_f32
+__device__ __forceinline__ uint32_t pack16(BF16, float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
 }
-__device__ __forceinline__ uint32_t to16(F16, float x) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+__device__ __forceinline__ uint32_t pack16(F16, float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, f16x2));
 }
-__device__ __forceinline__ float from16(BF16, uint32_t h) { return u2f(h << 16); }
-__device__ __forceinline__ float from16(F16, uint32_t h) {
+// the low / high 16-bit value of a dword, widened to fp32 (exact)
+__device__ __forceinline__ float lo16(BF16, uint32_t h) { return u2f(h << 16); }
+__device__ __forceinline__ float hi16(BF16, uint32_t h) { return u2f(h & 0xffff0000u); }
+__device__ __forceinline__ float lo16(F16, uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ float hi16(F16, uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(h >> 16));
 }
 
 // E4M3 codes H*2, H*2 + 1 (bytes) of w as two packed 16-bit values of type S,
@@ -455,11 +465,9 @@ struct MfmaWalker {
             m[t] = m_new;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const uint32_t h0 = to16(S{}, p[2 * w]), h1 = to16(S{}, p[2 * w + 1]);
-                const uint32_t r0 = to16(S{}, p[2 * w] - from16(S{}, h0));
-                const uint32_t r1 = to16(S{}, p[2 * w + 1] - from16(S{}, h1));
-                bhi[t][w] = h0 | (h1 << 16);
-                blo[t][w] = r0 | (r1 << 16);
+                const uint32_t h = pack16(S{}, p[2 * w], p[2 * w + 1]);
+                bhi[t][w] = h;
+                blo[t][w] = pack16(S{}, p[2 * w] - lo16(S{}, h), p[2 * w + 1] - hi16(S{}, h));
             }
         }
         // the eight V pieces as pairs of S values: hv[j][k] = dims 2k, 2k+1 of token j
