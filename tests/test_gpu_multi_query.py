@@ -166,6 +166,37 @@ def test_chunked_prefill_matches_oracle(nq, group, dtype, block_size):
                     assert (o[i, j] == 0).all(), (partition, i, j)
 
 
+@pytest.mark.parametrize("num_seqs", [64, 70])
+def test_chunked_prefill_many_sequences(num_seqs):
+    """Prefill workgroups take sequences longest first when there are at most
+    64 of them and in index order beyond that: both orders, over lengths with
+    ties, empty rows and chunks longer than their sequence, give the oracle's
+    result (and every column is written once)."""
+    global LENS
+    rng = np.random.default_rng(4712 + num_seqs)
+    lens = [int(x) for x in rng.integers(0, 200, num_seqs)]
+    lens[3] = lens[5] = lens[7]                               # ties in length
+    lens[1] = 0
+    saved, LENS = LENS, lens
+    try:
+        w, k_new, v_new, q = setup(32, 1, torch.float16, 16, seed=53)
+    finally:
+        LENS = saved
+    kb, vb = pool_after_append_multi(bits(w.k_pool), bits(w.v_pool), bits(k_new), bits(v_new),
+                                     w.block_tables, w.seq_lens, w.block_size)
+    ref = paged_multi_query_attention(widen(q), widen(from_bits(kb, torch.float16)),
+                                      widen(from_bits(vb, torch.float16)), w.block_tables,
+                                      w.seq_lens, w.block_size, w.scale)
+    _, _, out = run(w, k_new, v_new, q, BAL)
+    o = out.cpu().double().numpy()
+    assert np.isfinite(o).all()
+    check_error("prefill_f16", float(np.abs(o - ref).max()), 2e-3, f"{num_seqs} sequences")
+    for i, n in enumerate(lens):
+        for j in range(32):
+            if n - 32 + j < 0:
+                assert (o[i, j] == 0).all(), (i, j)
+
+
 def test_chunked_prefill_balanced_is_the_single_pass():
     """With more than 16 columns the balanced schedule runs as a single pass
     per 16-column group: the same bits, and no workspace."""
