@@ -484,16 +484,21 @@ struct MfmaWalker {
                 for (int k = 0; k < 4; ++k) hv[j][k] = vt[j][k];
             }
         }
-        // Rescale a tile's accumulators only when some column's max grew: alpha
-        // is exactly 1 otherwise (exp2 of 0), and past the first chunks the
-        // running max rarely moves, so most chunks skip these 32 products
-        // (the result bits are the same either way). Decode walks only: with
-        // several tiles the branch costs registers, and on MI355X the chunked
-        // prefill ran 9% slower with it.
-        if constexpr (NT == 1) {
-            if (__ballot(alpha[0] != 1.f) != 0) {
+        // Rescale the accumulators only when some column's max grew: alpha is
+        // exactly 1 otherwise (exp2 of 0), and past the first chunks the
+        // running max rarely moves, so most chunks skip these 32 products per
+        // tile (the result bits are the same either way). One test for all
+        // the wave's tiles: a branch per tile cost registers and made the
+        // two-tile prefill walk 9% slower on MI355X; this one is 1% faster.
+        {
+            bool grew = false;
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[0][c] = acc[0][c] * alpha[0];
+            for (int t = 0; t < NT; ++t) grew = grew || alpha[t] != 1.f;
+            if (__ballot(grew) != 0) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) acc[t][c] = acc[t][c] * alpha[t];
             }
         }
 #pragma unroll
@@ -510,8 +515,7 @@ struct MfmaWalker {
             }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const f32x4 o =
-                    mfma_16x16x32(S{}, av, bhi[t], NT == 1 ? acc[t][c] : acc[t][c] * alpha[t]);
+                const f32x4 o = mfma_16x16x32(S{}, av, bhi[t], acc[t][c]);
                 acc[t][c] = mfma_16x16x32(S{}, av, blo[t], o);
             }
         }

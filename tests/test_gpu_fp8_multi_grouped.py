@@ -78,6 +78,8 @@ def multi_expected(w):
 @pytest.mark.parametrize("nq,group,q_dtype,block_size", [
     (1, 2, torch.float16, 16), (4, 1, torch.bfloat16, 8), (16, 1, torch.float16, 32),
     (8, 2, torch.bfloat16, 16), (4, 4, torch.float16, 64), (2, 8, torch.bfloat16, 16),
+    # chunked prefill over an FP8 cache: 64 and 256 columns per (sequence, kv head)
+    (64, 1, torch.float16, 16), (32, 8, torch.bfloat16, 32),
 ])
 def test_multi_query_fp8_matches_oracle(nq, group, q_dtype, block_size, partition):
     w = multi_setup(nq, group, q_dtype, block_size)

@@ -190,6 +190,30 @@ def test_shared_prefix_equals_private_copies(name, partition):
     assert torch.equal(bits_t(_run(w2, partition)), bits_t(ref))
 
 
+@pytest.mark.parametrize("partition", [0, 64, 512])
+@pytest.mark.parametrize("name", ["llama13b_bf16", "opt13b_fp16", "long_gqa_bf16_bs16"])
+def test_fixed_partitions_are_batch_invariant(name, partition):
+    """Under a single pass or fixed partitions a row's bits depend on its own
+    sequence only: the same rows computed in sub-batches (one sequence alone,
+    a random half, the batch reversed) equal the full batch's rows bit for
+    bit. (The balanced schedule splits the batch's whole token count over the
+    waves, so there a row's rounding may change with the rest of the batch.)"""
+    w = _small(name)
+    d = Device(w)
+    d.copy_and_append()
+    full = d.attention(partition_size=partition).cpu()
+    rng = np.random.default_rng(7)
+    half = sorted(rng.choice(w.num_seqs, size=max(1, w.num_seqs // 2), replace=False).tolist())
+    for sub in ([w.num_seqs - 1], half, list(reversed(range(w.num_seqs)))):
+        idx = torch.tensor(sub, dtype=torch.long, device="cuda")
+        q = d.q[idx].contiguous()
+        out = torch.empty(tuple(q.shape), dtype=torch.float32, device="cuda")
+        pkv.paged_attention_decode(out, q, d.k_pool, d.v_pool, d.tables[idx].contiguous(),
+                                   d.lens[idx].contiguous(), w.max_seq_len, w.scale,
+                                   partition_size=partition)
+        assert torch.equal(bits_t(out.cpu()), bits_t(full[sub])), (name, partition, sub)
+
+
 @pytest.mark.parametrize("partition", [0, 64, BAL])
 def test_runs_are_deterministic(partition):
     w = _small("llama13b_bf16")
