@@ -221,7 +221,9 @@ PKV_API size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, i
  *                           pieces of a sequence split between waves are
  *                           merged by a log-sum-exp reduce. The split points
  *                           depend on the lengths of the whole batch, so a
- *                           row's rounding can change when other rows change.
+ *                           row's rounding can change when other rows change
+ *                           (under 0 or fixed partitions it cannot: a row's
+ *                           bits depend on its own sequence only).
  * When a split is possible, `workspace` (16-byte aligned, at least
  * pkv_paged_attention_workspace_size(...) bytes, contents ignored and
  * overwritten) holds the partial results. Work enqueued on `stream` by
