@@ -360,8 +360,12 @@ void paged_decode_balanced_kernel(const AttnParams a) {
     st.init(lane);
     const float scale_log2 = a.scale * kLog2e;
     long long u = u0;
+    // the next segment's length and first table window, read while the
+    // current segment is walked (sequence -1: nothing read ahead)
+    int pf_seq = -1, pf_g = -1, pf_len = 0, pf_tv = 0;
     while (u < u1 && seq < a.num_seqs) {
-        const int L = clamp_len(a, a.seq_lens[seq]);
+        const int raw_len = seq == pf_seq ? pf_len : a.seq_lens[seq];
+        const int L = clamp_len(a, raw_len);
         const int nu = units_of(L);
         if (nu == 0) { ++seq; continue; }        // empty sequences own no units
         const int g = (int)((u - base) / nu);
@@ -371,6 +375,18 @@ void paged_decode_balanced_kernel(const AttnParams a) {
         const int k1 = (int)((u1 < seg1 ? u1 : seg1) - seg0);
         const int t_stop = (k1 * kUnit < L) ? k1 * kUnit : L;
         st.begin(a, seq, g, L);
+        if (seq == pf_seq && g == pf_g) st.preload_window(pf_tv);
+        // the segment after this one, if this wave's run goes on into it
+        const int nseq = g + 1 < a.num_kv_heads ? seq : seq + 1;
+        const int ng = g + 1 < a.num_kv_heads ? g + 1 : 0;
+        if (seg0 + k1 < u1 && nseq < a.num_seqs) {
+            pf_seq = nseq;
+            pf_g = ng;
+            pf_len = nseq == seq ? raw_len : a.seq_lens[nseq];
+            pf_tv = lane < a.max_blocks ? a.block_tables[(size_t)nseq * a.max_blocks + lane] : 0;
+        } else {
+            pf_seq = -1;
+        }
         st.walk(k0 * kUnit, t_stop, scale_log2);
         if (k0 == 0 && k1 == nu) {
             st.write_final(a, seq, g);

@@ -63,6 +63,8 @@ struct Fp8VecWalker {
     float vscale;
 
     int wb, tv;
+    int pre_tv = 0;     // a window read ahead (preload_window)
+    bool pre = false;
     const char* kbase;
     const char* vbase;
     const int* trow;
@@ -111,9 +113,19 @@ struct Fp8VecWalker {
         }
     }
 
+    // Entries of blocks 0 .. 63 of the next segment's table row (lane j: block
+    // j), read ahead by the caller while the previous segment was walked; the
+    // next load_window(0) takes them instead of reading the table.
+    __device__ __forceinline__ void preload_window(int entries) {
+        pre_tv = entries;
+        pre = true;
+    }
+
     __device__ __forceinline__ void load_window(int first_block) {
         wb = first_block;
-        tv = (wb + lane < nblk_valid) ? trow[wb + lane] : 0;
+        const bool valid = wb + lane < nblk_valid;
+        tv = (pre && first_block == 0) ? (valid ? pre_tv : 0) : (valid ? trow[wb + lane] : 0);
+        pre = false;
         // an entry of a valid block outside the pool is read clamped; say so
         report_wave(err, wb + lane < nblk_valid && (uint32_t)tv >= (uint32_t)max_phys,
                     PKV_ERRBIT_TABLE);
