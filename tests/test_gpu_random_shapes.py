@@ -114,3 +114,50 @@ def test_multi_query(case):
                                       bs, w.scale)
     err = float(np.abs(out.cpu().double().numpy() - ref).max())
     assert err <= 2e-3, f"{shape}: max abs error {err:.3e}"
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_chunked_prefill(case):
+    """Random chunked-prefill shapes: more than 16 (token, head) columns per
+    (sequence, kv head), so the columns run in 16-column tiles, grouped eight
+    to a workgroup of four waves that share each K/V chunk."""
+    rng = np.random.default_rng(9700 + case)
+    dtype = [torch.float16, torch.bfloat16][rng.integers(2)]
+    group = int(rng.choice([1, 2, 4, 8]))
+    nq = int(rng.integers(16 // group + 1, 160 // group + 1))
+    hkv = int(rng.integers(1, 3))
+    bs = int(rng.choice([8, 16, 32, 64, 128]))
+    lens = lengths(rng, int(rng.integers(1, 7)), int(rng.choice([40, 300, 900])))
+    part = int(rng.choice([0, 64, 512, BAL]))
+    shape = f"{dtype} G={group} nq={nq} Hkv={hkv} bs={bs} lens={lens} partition={part}"
+    seed = int(rng.integers(1 << 30))
+    w = wl.build_independent("random_prefill", lens, dtype=dtype, num_heads=hkv * group,
+                             num_kv_heads=hkv, head_dim=128, block_size=bs, dist="normal",
+                             seed=seed)
+    for i, n in enumerate(w.seq_lens):          # stale slots from the new tokens on
+        n = int(n)
+        for t in range(max(0, n - nq), -(-n // bs) * bs):
+            w.k_pool[int(w.block_tables[i, t // bs]), :, t % bs] = float("nan")
+            w.v_pool[int(w.block_tables[i, t // bs]), :, t % bs] = float("nan")
+    r = np.random.default_rng(seed)
+    b = len(lens)
+    k_new = torch.from_numpy(r.standard_normal((b, nq, hkv, 128), dtype=np.float32)).to(dtype)
+    v_new = torch.from_numpy(r.standard_normal((b, nq, hkv, 128), dtype=np.float32)).to(dtype)
+    q = torch.from_numpy(r.standard_normal((b, nq, hkv * group, 128), dtype=np.float32)).to(dtype)
+    kp, vp = w.k_pool.cuda(), w.v_pool.cuda()
+    tables = torch.from_numpy(w.block_tables).cuda()
+    lens_d = torch.from_numpy(w.seq_lens).cuda()
+    pkv.kv_cache_append_multi(k_new.cuda(), v_new.cuda(), kp, vp, tables, lens_d)
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    pkv.paged_attention_multi(out, q.cuda(), kp, vp, tables, lens_d, w.max_seq_len, w.scale,
+                              partition_size=part)
+    kb, vb = pool_after_append_multi(bits(w.k_pool), bits(w.v_pool), bits(k_new), bits(v_new),
+                                     w.block_tables, w.seq_lens, bs)
+    assert np.array_equal(bits(kp), kb) and np.array_equal(bits(vp), vb), shape
+    ref = paged_multi_query_attention(widen(q), widen(from_bits(kb, dtype)),
+                                      widen(from_bits(vb, dtype)), w.block_tables, w.seq_lens,
+                                      bs, w.scale)
+    o = out.cpu().double().numpy()
+    assert np.isfinite(o).all(), f"{shape}: a row was not written"
+    err = float(np.abs(o - ref).max())
+    assert err <= 2e-3, f"{shape}: max abs error {err:.3e}"
