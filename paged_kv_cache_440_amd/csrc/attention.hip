@@ -266,7 +266,10 @@ void lse_reduce_kernel(const AttnParams a) {
 // starts writes record 2w + 1, every later wave writes record 2w (a wave's
 // run begins inside at most one segment that started earlier, and ends inside
 // at most one that goes on). Record r holds G rows: ws_acc[r * G + h],
-// ws_ml[r * G + h].
+// ws_ml[r * G + h]. When the waves of a cut segment all belong to one
+// workgroup, the pieces meet in LDS instead: each later wave parks its piece
+// there, and the wave where the segment starts folds them in once the whole
+// workgroup is done, writing no record (walkers with kDepositBytes > 0).
 
 constexpr int kUnit = 32;
 
@@ -299,14 +302,32 @@ __device__ __forceinline__ long long units_before(const AttnParams& a, int end) 
     return total * a.num_kv_heads;
 }
 
+// LDS slots of the workgroup's waves for pieces that another wave of the
+// workgroup finishes (BYTES per wave), and the segment each slot holds (-1:
+// none).
+template <int BYTES>
+__device__ __forceinline__ char* deposit_slots() {
+    __shared__ __attribute__((aligned(16))) char slots[kWaves * BYTES];
+    return slots;
+}
+
+__device__ __forceinline__ int* deposit_tags() {
+    __shared__ int tags[kWaves];
+    return tags;
+}
+
+// Wave w's run of the balanced schedule. A segment cut by run boundaries
+// whose first and last units fall in waves of one workgroup is not written
+// to the workspace: each later wave deposits its piece in its LDS slot
+// (tagged with the segment, seq * Hkv + g), and the wave where the segment
+// starts (its run ends inside it) returns the segment, keeping its own piece
+// in st; the caller merges them once every wave of the workgroup is done.
+// Returns -1 otherwise.
 template <class Walker>
-__global__ __launch_bounds__(64 * kWaves)
-__attribute__((amdgpu_waves_per_eu(Walker::kMinWavesPerSimd)))
-void paged_decode_balanced_kernel(const AttnParams a) {
+__device__ __forceinline__ int balanced_run(const AttnParams& a, int w, Walker& st) {
     constexpr int G = Walker::G;
+    constexpr bool kInGroup = Walker::kDepositBytes > 0;
     const int lane = threadIdx.x & 63;
-    const int w = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (w >= a.num_items) return;
     const int W = a.num_items;
     // padding sequences (length 0) own no units: wave w zeroes the rows of
     // sequences w, w + W, ...
@@ -322,8 +343,15 @@ void paged_decode_balanced_kernel(const AttnParams a) {
     const long long u1 = (u0 + q < total) ? u0 + q : total;
     if (u0 >= u1) {
         if (lane == 0) a.ws_info[2 * w] = -1;    // holds no piece of any segment
-        return;
+        return -1;
     }
+    // The workgroup's waves hold units [g_lo, g_hi). A segment that starts
+    // before u0 merges inside the workgroup if it starts at or after g_lo
+    // and ends by g_hi; one that starts in this run and goes on past u1, if
+    // its units past u1 number at most g_room.
+    const long long g_lo = (long long)(w - w % kWaves) * q, g_hi = g_lo + kWaves * q;
+    const int g_room = __builtin_amdgcn_readfirstlane(
+        kInGroup ? (int)(g_hi - u1 < 0x7fffffff ? g_hi - u1 : 0x7fffffff) : -1);
 
     // the sequence whose segments hold unit u0, and the units before it
     long long base = 0;
@@ -343,22 +371,26 @@ void paged_decode_balanced_kernel(const AttnParams a) {
         base += __shfl(incl, 63, 64);
     }
 
-    // Tell the merge kernel whether this wave ends a split segment: the one
-    // holding unit u0, if it started in an earlier wave and ends in this run.
+    // Tell the merge kernel whether this wave ends a split segment that it
+    // must merge: the one holding unit u0, if it started in an earlier wave
+    // and ends in this run (and is not merged inside the workgroup).
+    bool first_in_group;
     {
         const int nu = units_of(clamp_len(a, a.seq_lens[seq]));
         const int g = (int)((u0 - base) / nu);
         const long long seg0 = base + (long long)g * nu;
-        const bool ends_split = seg0 < u0 && seg0 + nu <= u1;
+        first_in_group = __builtin_amdgcn_readfirstlane(
+            kInGroup && seg0 < u0 && seg0 >= g_lo && seg0 + nu <= g_hi);
+        const bool ends_split = seg0 < u0 && seg0 + nu <= u1 && !first_in_group;
         if (lane == 0) {
             a.ws_info[2 * w] = ends_split ? seq * a.num_kv_heads + g : -1;
             a.ws_info[2 * w + 1] = (int)(seg0 / q);
         }
     }
 
-    Walker st;
     st.init(lane);
     const float scale_log2 = a.scale * kLog2e;
+    int pending = -1;
     long long u = u0;
     // the next segment's length and first table window, read while the
     // current segment is walked (sequence -1: nothing read ahead)
@@ -390,6 +422,18 @@ void paged_decode_balanced_kernel(const AttnParams a) {
         st.walk(k0 * kUnit, t_stop, scale_log2);
         if (k0 == 0 && k1 == nu) {
             st.write_final(a, seq, g);
+        } else if (k0 > 0 ? first_in_group : nu - k1 <= g_room) {
+            if constexpr (kInGroup) {
+                if (k0 > 0) {
+                    // a later piece (this run's first): into this wave's slot
+                    st.deposit(deposit_slots<Walker::kDepositBytes>() +
+                               (w % kWaves) * Walker::kDepositBytes);
+                    if (lane == 0) deposit_tags()[w % kWaves] = seq * a.num_kv_heads + g;
+                } else {
+                    // the first piece, which ends this run: kept in st
+                    pending = __builtin_amdgcn_readfirstlane(seq * a.num_kv_heads + g);
+                }
+            }
         } else {
             const size_t rec = 2 * (size_t)w + (k0 == 0 ? 1 : 0);
             st.write_partial(a, rec * (a.num_queries * G), 1);
@@ -398,6 +442,35 @@ void paged_decode_balanced_kernel(const AttnParams a) {
         if (g == a.num_kv_heads - 1 && u == seg1) {
             base = u;
             ++seq;
+        }
+    }
+    return pending;
+}
+
+template <class Walker>
+__global__ __launch_bounds__(64 * kWaves)
+__attribute__((amdgpu_waves_per_eu(Walker::kBalancedMinWavesPerSimd)))
+void paged_decode_balanced_kernel(const AttnParams a) {
+    const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int w = blockIdx.x * kWaves + wl;
+    constexpr bool kInGroup = Walker::kDepositBytes > 0;
+    if constexpr (kInGroup) {
+        if ((threadIdx.x & 63) == 0) deposit_tags()[wl] = -1;
+    }
+    Walker st;
+    const int pending = w < a.num_items ? balanced_run<Walker>(a, w, st) : -1;
+    if constexpr (kInGroup) {
+        // every wave of the workgroup reaches this barrier (no early exits
+        // above): the deposits and their tags are in place
+        __syncthreads();
+        if (pending >= 0) {
+            // the segment's later pieces sit in the slots of the next waves
+            int n = 0;
+            while (wl + 1 + n < kWaves && deposit_tags()[wl + 1 + n] == pending) ++n;
+            st.write_final_merged(a, pending / a.num_kv_heads, pending % a.num_kv_heads,
+                                  deposit_slots<Walker::kDepositBytes>() +
+                                      (wl + 1) * Walker::kDepositBytes,
+                                  n);
         }
     }
 }

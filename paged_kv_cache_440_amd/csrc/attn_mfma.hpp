@@ -219,6 +219,7 @@ struct MfmaWalker {
     // in LDS, fits two tiles at two)
     static constexpr int kTiles = NT;
     static constexpr int kMinWavesPerSimd = WPS;
+    static constexpr int kBalancedMinWavesPerSimd = WPS;
     // one lane's V piece of one token: 8 dims, 16-bit or codes
     using VPiece = std::conditional_t<FP8, u32x2, u32x4>;
     static_assert(S::bytes == 2 && G_ <= 16, "16-bit operands, at most 16 query heads");
@@ -678,6 +679,41 @@ struct MfmaWalker {
             store_column_tile(out_tile(), acc[t], inv, orow[t], n < ncols[t],
                               [&](size_t r, int piece, f32x4 v) { store_out4(out, dt, r, piece, v); });
         }
+    }
+
+    // A piece of a segment that another wave of the workgroup finishes (the
+    // balanced schedule): the lane state as it stands, acc[0][c] at 16-byte
+    // slot c * 64 + lane, then m and l at word 2048 + lane and 2112 + lane.
+    static constexpr int kDepositBytes = (NT == 1 && !SHARED) ? 64 * 8 * 16 + 2 * 64 * 4 : 0;
+
+    __device__ __forceinline__ void deposit(char* slot) const {
+        f32x4* s = reinterpret_cast<f32x4*>(slot);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) s[c * 64 + lane] = acc[0][c];
+        float* f = reinterpret_cast<float*>(slot + 64 * 8 * 16);
+        f[lane] = m[0];
+        f[64 + lane] = l[0];
+    }
+
+    // Fold the n pieces deposited at slots, slots + kDepositBytes, ... into
+    // this wave's state by the log-sum-exp rule (per column: both maxima
+    // are replicated over the column's lanes), then write the segment.
+    __device__ __forceinline__ void write_final_merged(const AttnParams& a, int seq, int g,
+                                                       const char* slots, int n) {
+        for (int j = 0; j < n; ++j) {
+            const char* slot = slots + (size_t)j * kDepositBytes;
+            const f32x4* s = reinterpret_cast<const f32x4*>(slot);
+            const float* f = reinterpret_cast<const float*>(slot + 64 * 8 * 16);
+            const float dm = f[lane], dl = f[64 + lane];
+            const float mn = m[0] > dm ? m[0] : dm;
+            const float a1 = m[0] == -__builtin_inff() ? 0.f : fast_exp2(m[0] - mn);
+            const float a2 = dm == -__builtin_inff() ? 0.f : fast_exp2(dm - mn);
+            l[0] = l[0] * a1 + dl * a2;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[0][c] = acc[0][c] * a1 + s[c * 64 + lane] * a2;
+            m[0] = mn;
+        }
+        write_final(a, seq, g);
     }
 
     // Partial results: column n of tile t to workspace row row0 + (16 t + n) * row_stride.
