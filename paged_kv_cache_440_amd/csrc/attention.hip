@@ -266,10 +266,14 @@ void lse_reduce_kernel(const AttnParams a) {
 // starts writes record 2w + 1, every later wave writes record 2w (a wave's
 // run begins inside at most one segment that started earlier, and ends inside
 // at most one that goes on). Record r holds G rows: ws_acc[r * G + h],
-// ws_ml[r * G + h]. When the waves of a cut segment all belong to one
-// workgroup, the pieces meet in LDS instead: each later wave parks its piece
-// there, and the wave where the segment starts folds them in once the whole
-// workgroup is done, writing no record (walkers with kDepositBytes > 0).
+// ws_ml[r * G + h]. The pieces of a cut segment first meet in LDS: each
+// wave parks its cut pieces there (the first of its run in slot 0, the last
+// in slot 1), and once the whole workgroup is done, the pieces that fall in
+// one workgroup are folded by one of its waves. If the segment starts and
+// ends in the workgroup, that wave writes the output; otherwise it writes
+// the workgroup's one record: the wave where the segment starts record
+// 2w + 1, the first wave of every later workgroup record 2w. The merge
+// kernel folds those records.
 
 constexpr int kUnit = 32;
 
@@ -302,32 +306,80 @@ __device__ __forceinline__ long long units_before(const AttnParams& a, int end) 
     return total * a.num_kv_heads;
 }
 
-// LDS slots of the workgroup's waves for pieces that another wave of the
-// workgroup finishes (BYTES per wave), and the segment each slot holds (-1:
-// none).
-template <int BYTES>
-__device__ __forceinline__ char* deposit_slots() {
-    __shared__ __attribute__((aligned(16))) char slots[kWaves * BYTES];
-    return slots;
-}
-
-__device__ __forceinline__ int* deposit_tags() {
+// The segment (seq * Hkv + g) whose piece each wave of the workgroup holds
+// in its LDS slot 0 (-1: none).
+__device__ __forceinline__ int* slot_tags() {
     __shared__ int tags[kWaves];
     return tags;
 }
 
-// Wave w's run of the balanced schedule. A segment cut by run boundaries
-// whose first and last units fall in waves of one workgroup is not written
-// to the workspace: each later wave deposits its piece in its LDS slot
-// (tagged with the segment, seq * Hkv + g), and the wave where the segment
-// starts (its run ends inside it) returns the segment, keeping its own piece
-// in st; the caller merges them once every wave of the workgroup is done.
-// Returns -1 otherwise.
+// 16-byte (fp32) or 8-byte (16-bit) store of outputs idx .. idx + 3.
+__device__ __forceinline__ void store_out_quad(void* out, int out_dtype, size_t idx, f32x4 v) {
+    if (out_dtype == PKV_F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + idx) = v;
+        return;
+    }
+    uint32_t h[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        h[k] = out_dtype == PKV_F16 ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[k])
+                                    : (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[k]);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + idx) =
+        u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+}
+
+// Fold nslots pieces of segment (seq, g) parked in LDS (record form, as the
+// walkers' deposit writes them; slot k at acc_of(k), ml_of(k)) by the
+// log-sum-exp rule, and write its cols columns: the outputs if `final`,
+// else workspace record rec (rows rec * cols + c).
+template <class Walker, class AccOf, class MlOf>
+__device__ __forceinline__ void fold_slots(const AttnParams& a, int nslots, AccOf acc_of, MlOf ml_of,
+                                           bool final, int seq, int g, size_t rec) {
+    constexpr int D = Walker::D, SC = Walker::kSlotCols, LPR = D / 4, RPW = 64 / LPR;
+    const int lane = threadIdx.x & 63, grp = lane / LPR, sub = lane % LPR;
+    const int cols = a.num_queries * Walker::G;
+    for (int c0 = 0; c0 < cols; c0 += RPW) {
+        const int c = c0 + grp;
+        if (c >= cols) break;
+        float mrun = -__builtin_inff(), lsum = 0.f;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < nslots; ++k) {
+            const float* ml = ml_of(k);
+            const float mk = ml[c], lk = ml[SC + c];
+            const f32x4 x = *reinterpret_cast<const f32x4*>(acc_of(k) + c * D + 4 * sub);
+            const float mnew = __builtin_fmaxf(mrun, mk);
+            const float keep = (mrun == -__builtin_inff()) ? 0.f : fast_exp2(mrun - mnew);
+            const float take = (mk == -__builtin_inff()) ? 0.f : fast_exp2(mk - mnew);
+            lsum = __builtin_fmaf(take, lk, lsum * keep);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = __builtin_fmaf(take, x[j], o[j] * keep);
+            mrun = mnew;
+        }
+        if (final) {
+            const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;   // 0: a query before the start
+            store_out_quad(a.out, a.out_dtype, out_row(a, seq, g, c) * D + 4 * sub, o * inv);
+        } else {
+            const size_t row = rec * cols + c;
+            *reinterpret_cast<f32x4*>(a.ws_acc + row * D + 4 * sub) = o;
+            if (sub == 0) {
+                a.ws_ml[2 * row] = mrun;
+                a.ws_ml[2 * row + 1] = lsum;
+            }
+        }
+    }
+}
+
+// Wave w's run of the balanced schedule. Its cut pieces go to its LDS slots:
+// the first piece, if it continues a segment begun before the run, to slot
+// 0 (tagged with the segment, seq * Hkv + g), the last, if it begins a
+// segment that goes on past the run, to slot 1. Returns that last piece's
+// segment (-1: none), and in *ends_here whether the segment ends inside the
+// workgroup.
 template <class Walker>
-__device__ __forceinline__ int balanced_run(const AttnParams& a, int w, Walker& st) {
-    constexpr int G = Walker::G;
-    constexpr bool kInGroup = Walker::kDepositBytes > 0;
+__device__ __forceinline__ int balanced_run(const AttnParams& a, int w, Walker& st,
+                                            bool* ends_here) {
     const int lane = threadIdx.x & 63;
+    const int wl = w % kWaves;
     const int W = a.num_items;
     // padding sequences (length 0) own no units: wave w zeroes the rows of
     // sequences w, w + W, ...
@@ -346,12 +398,12 @@ __device__ __forceinline__ int balanced_run(const AttnParams& a, int w, Walker& 
         return -1;
     }
     // The workgroup's waves hold units [g_lo, g_hi). A segment that starts
-    // before u0 merges inside the workgroup if it starts at or after g_lo
-    // and ends by g_hi; one that starts in this run and goes on past u1, if
-    // its units past u1 number at most g_room.
-    const long long g_lo = (long long)(w - w % kWaves) * q, g_hi = g_lo + kWaves * q;
+    // before u0 lies inside the workgroup if it starts at or after g_lo and
+    // ends by g_hi; one that starts in this run and goes on past u1, if its
+    // units past u1 number at most g_room.
+    const long long g_lo = (long long)(w - wl) * q, g_hi = g_lo + kWaves * q;
     const int g_room = __builtin_amdgcn_readfirstlane(
-        kInGroup ? (int)(g_hi - u1 < 0x7fffffff ? g_hi - u1 : 0x7fffffff) : -1);
+        (int)(g_hi - u1 < 0x7fffffff ? g_hi - u1 : 0x7fffffff));
 
     // the sequence whose segments hold unit u0, and the units before it
     long long base = 0;
@@ -373,15 +425,13 @@ __device__ __forceinline__ int balanced_run(const AttnParams& a, int w, Walker& 
 
     // Tell the merge kernel whether this wave ends a split segment that it
     // must merge: the one holding unit u0, if it started in an earlier wave
-    // and ends in this run (and is not merged inside the workgroup).
-    bool first_in_group;
+    // and ends in this run, unless it lies inside the workgroup.
     {
         const int nu = units_of(clamp_len(a, a.seq_lens[seq]));
         const int g = (int)((u0 - base) / nu);
         const long long seg0 = base + (long long)g * nu;
-        first_in_group = __builtin_amdgcn_readfirstlane(
-            kInGroup && seg0 < u0 && seg0 >= g_lo && seg0 + nu <= g_hi);
-        const bool ends_split = seg0 < u0 && seg0 + nu <= u1 && !first_in_group;
+        const bool inside = seg0 >= g_lo && seg0 + nu <= g_hi;
+        const bool ends_split = seg0 < u0 && seg0 + nu <= u1 && !inside;
         if (lane == 0) {
             a.ws_info[2 * w] = ends_split ? seq * a.num_kv_heads + g : -1;
             a.ws_info[2 * w + 1] = (int)(seg0 / q);
@@ -422,21 +472,15 @@ __device__ __forceinline__ int balanced_run(const AttnParams& a, int w, Walker& 
         st.walk(k0 * kUnit, t_stop, scale_log2);
         if (k0 == 0 && k1 == nu) {
             st.write_final(a, seq, g);
-        } else if (k0 > 0 ? first_in_group : nu - k1 <= g_room) {
-            if constexpr (kInGroup) {
-                if (k0 > 0) {
-                    // a later piece (this run's first): into this wave's slot
-                    st.deposit(deposit_slots<Walker::kDepositBytes>() +
-                               (w % kWaves) * Walker::kDepositBytes);
-                    if (lane == 0) deposit_tags()[w % kWaves] = seq * a.num_kv_heads + g;
-                } else {
-                    // the first piece, which ends this run: kept in st
-                    pending = __builtin_amdgcn_readfirstlane(seq * a.num_kv_heads + g);
-                }
-            }
+        } else if (k0 > 0) {
+            // a later piece of a segment begun before this run (its first piece)
+            st.template deposit<0>(wl);
+            if (lane == 0) slot_tags()[wl] = seq * a.num_kv_heads + g;
         } else {
-            const size_t rec = 2 * (size_t)w + (k0 == 0 ? 1 : 0);
-            st.write_partial(a, rec * (a.num_queries * G), 1);
+            // the first piece of a segment that goes on past this run (its last)
+            st.template deposit<1>(wl);
+            pending = __builtin_amdgcn_readfirstlane(seq * a.num_kv_heads + g);
+            *ends_here = nu - k1 <= g_room;
         }
         u = seg0 + k1;
         if (g == a.num_kv_heads - 1 && u == seg1) {
@@ -453,25 +497,39 @@ __attribute__((amdgpu_waves_per_eu(Walker::kBalancedMinWavesPerSimd)))
 void paged_decode_balanced_kernel(const AttnParams a) {
     const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int w = blockIdx.x * kWaves + wl;
-    constexpr bool kInGroup = Walker::kDepositBytes > 0;
-    if constexpr (kInGroup) {
-        if ((threadIdx.x & 63) == 0) deposit_tags()[wl] = -1;
-    }
+    int* tags = slot_tags();
+    if ((threadIdx.x & 63) == 0) tags[wl] = -1;
     Walker st;
-    const int pending = w < a.num_items ? balanced_run<Walker>(a, w, st) : -1;
-    if constexpr (kInGroup) {
-        // every wave of the workgroup reaches this barrier (no early exits
-        // above): the deposits and their tags are in place
-        __syncthreads();
-        if (pending >= 0) {
-            // the segment's later pieces sit in the slots of the next waves
-            int n = 0;
-            while (wl + 1 + n < kWaves && deposit_tags()[wl + 1 + n] == pending) ++n;
-            st.write_final_merged(a, pending / a.num_kv_heads, pending % a.num_kv_heads,
-                                  deposit_slots<Walker::kDepositBytes>() +
-                                      (wl + 1) * Walker::kDepositBytes,
-                                  n);
-        }
+    bool ends_here = false;
+    const int pending = w < a.num_items ? balanced_run<Walker>(a, w, st, &ends_here) : -1;
+    // every wave of the workgroup reaches this barrier (no early exits
+    // above): the parked pieces and their tags are in place
+    __syncthreads();
+    const int hkv = a.num_kv_heads;
+    if (pending >= 0) {
+        // the segment this wave begins: its piece in slot 1, the later ones
+        // in slot 0 of the next waves of the workgroup
+        int n = 1;
+        while (wl + n < kWaves && tags[wl + n] == pending) ++n;
+        auto acc_of = [&](int k) {
+            return k == 0 ? Walker::template slot_acc<1>(wl) : Walker::template slot_acc<0>(wl + k);
+        };
+        auto ml_of = [&](int k) {
+            return k == 0 ? Walker::template slot_ml<1>(wl) : Walker::template slot_ml<0>(wl + k);
+        };
+        fold_slots<Walker>(a, n, acc_of, ml_of, ends_here, pending / hkv, pending % hkv,
+                           2 * (size_t)w + 1);
+    }
+    const int s0 = tags[0];
+    if (wl == 0 && s0 >= 0) {
+        // the segment begun in an earlier workgroup that goes on into this
+        // one: its pieces in slot 0 of the first waves
+        int n = 1;
+        while (n < kWaves && tags[n] == s0) ++n;
+        fold_slots<Walker>(
+            a, n, [&](int k) { return Walker::template slot_acc<0>(k); },
+            [&](int k) { return Walker::template slot_ml<0>(k); }, false, s0 / hkv, s0 % hkv,
+            2 * (size_t)w);
     }
 }
 
@@ -490,8 +548,13 @@ void balanced_reduce_kernel(const AttnParams a) {
     const int seg = a.ws_info[2 * w];
     if (seg < 0) return;
     const int wf = a.ws_info[2 * w + 1];
-    fold_records<D>(a, w - wf + 1,
-                    [&](int r) { return (2 * (size_t)(wf + r) + (r == 0 ? 1 : 0)) * cols + n; },
+    // the starting wave's record, then that of the first wave of each later
+    // workgroup up to this wave's
+    const int wg0 = wf / kWaves;
+    fold_records<D>(a, 1 + w / kWaves - wg0,
+                    [&](int r) {
+                        return (r == 0 ? 2 * (size_t)wf + 1 : 2 * (size_t)(wg0 + r) * kWaves) * cols + n;
+                    },
                     out_row(a, seg / a.num_kv_heads, seg % a.num_kv_heads, n));
 }
 
@@ -517,6 +580,8 @@ template <class Walker>
 hipError_t launch_balanced(const AttnParams& a_in, hipStream_t stream) {
     constexpr int D = Walker::D, G = Walker::G;
     AttnParams a = a_in;
+    // the LDS slots hold kSlotCols columns of a segment
+    if (a.num_queries * G > Walker::kSlotCols) return hipErrorInvalidValue;
     // a.num_items holds the compute-unit count; launch at most as many
     // persistent waves as are resident together, so that all of them start
     // at once and finish together

@@ -123,10 +123,12 @@ template <> __device__ __forceinline__ uint32_t fp8_pair<BF16, true>(uint32_t w)
 // dims 4 piece .. 4 piece + 3 of a row.
 // The calling wave's 8 KB slice of LDS (one allocation per kernel, however
 // many call sites).
-__device__ __forceinline__ f32x4 (*wave_tile())[32] {
+__device__ __forceinline__ f32x4 (*wave_tile_at(int wave))[32] {
     __shared__ f32x4 tile[kWaves][16][32];
-    return tile[threadIdx.x >> 6];
+    return tile[wave];
 }
+
+__device__ __forceinline__ f32x4 (*wave_tile())[32] { return wave_tile_at(threadIdx.x >> 6); }
 
 template <class Store>
 __device__ __forceinline__ void store_column_tile(f32x4 (*t)[32], const f32x4 (&acc)[8], float scale,
@@ -681,39 +683,53 @@ struct MfmaWalker {
         }
     }
 
-    // A piece of a segment that another wave of the workgroup finishes (the
-    // balanced schedule): the lane state as it stands, acc[0][c] at 16-byte
-    // slot c * 64 + lane, then m and l at word 2048 + lane and 2112 + lane.
-    static constexpr int kDepositBytes = (NT == 1 && !SHARED) ? 64 * 8 * 16 + 2 * 64 * 4 : 0;
+    // Pieces of segments that the balanced schedule cuts, parked in LDS
+    // until the workgroup is done, in record form: slot (K, wave) holds
+    // column c's unnormalised accumulator row (value scale) at
+    // slot_acc<K>(wave) + 128 c, its max and sum at slot_ml<K>(wave)[c] and
+    // [16 + c]. Slot 1 is the wave's output tile, which a wave fills only
+    // with its last piece.
+    static constexpr int kSlotCols = 16;
 
-    __device__ __forceinline__ void deposit(char* slot) const {
-        f32x4* s = reinterpret_cast<f32x4*>(slot);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) s[c * 64 + lane] = acc[0][c];
-        float* f = reinterpret_cast<float*>(slot + 64 * 8 * 16);
-        f[lane] = m[0];
-        f[64 + lane] = l[0];
+    __device__ __forceinline__ static float* slot_rows() {
+        __shared__ __attribute__((aligned(16))) float rows[kWaves * 16 * 128];
+        return rows;
     }
 
-    // Fold the n pieces deposited at slots, slots + kDepositBytes, ... into
-    // this wave's state by the log-sum-exp rule (per column: both maxima
-    // are replicated over the column's lanes), then write the segment.
-    __device__ __forceinline__ void write_final_merged(const AttnParams& a, int seq, int g,
-                                                       const char* slots, int n) {
-        for (int j = 0; j < n; ++j) {
-            const char* slot = slots + (size_t)j * kDepositBytes;
-            const f32x4* s = reinterpret_cast<const f32x4*>(slot);
-            const float* f = reinterpret_cast<const float*>(slot + 64 * 8 * 16);
-            const float dm = f[lane], dl = f[64 + lane];
-            const float mn = m[0] > dm ? m[0] : dm;
-            const float a1 = m[0] == -__builtin_inff() ? 0.f : fast_exp2(m[0] - mn);
-            const float a2 = dm == -__builtin_inff() ? 0.f : fast_exp2(dm - mn);
-            l[0] = l[0] * a1 + dl * a2;
+    __device__ __forceinline__ static float* slot_mls() {
+        __shared__ float ml[2 * kWaves * 32];
+        return ml;
+    }
+
+    template <int K>
+    __device__ __forceinline__ static float* slot_acc(int wave) {
+        static_assert(NT == 1 && !SHARED, "one tile per wave, own tiles");
+        if constexpr (K == 0)
+            return slot_rows() + wave * 16 * 128;
+        else
+            return reinterpret_cast<float*>(wave_tile_at(wave));
+    }
+
+    template <int K>
+    __device__ __forceinline__ static float* slot_ml(int wave) {
+        return slot_mls() + (K * kWaves + wave) * 32;
+    }
+
+    template <int K>
+    __device__ __forceinline__ void deposit(int wave) const {
+        f32x4 (*t)[32] = reinterpret_cast<f32x4(*)[32]>(slot_acc<K>(wave));
+        const float scale = FP8 ? vscale : 1.f;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) acc[0][c] = acc[0][c] * a1 + s[c * 64 + lane] * a2;
-            m[0] = mn;
+        for (int i = 0; i < 4; ++i) {
+            t[n][8 * q + 2 * i] = f32x4{acc[0][0][i], acc[0][1][i], acc[0][2][i], acc[0][3][i]} * scale;
+            t[n][8 * q + 2 * i + 1] =
+                f32x4{acc[0][4][i], acc[0][5][i], acc[0][6][i], acc[0][7][i]} * scale;
         }
-        write_final(a, seq, g);
+        const float lsum = strided_sum<16>(l[0]);
+        if (q == 0) {
+            slot_ml<K>(wave)[n] = m[0];
+            slot_ml<K>(wave)[16 + n] = lsum;
+        }
     }
 
     // Partial results: column n of tile t to workspace row row0 + (16 t + n) * row_stride.

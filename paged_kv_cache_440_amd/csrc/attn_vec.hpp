@@ -241,57 +241,60 @@ struct VecWalker {
         for (int e = 0; e < EPL; ++e) acc[h][e] = strided_sum<LPT>(acc[h][e] * w);
     }
 
-    // A piece of a segment that another wave of the workgroup finishes (the
-    // balanced schedule), classes merged: head h's accumulator row at words
-    // h * D .., its max and sum at words G * D + 2 h, + 1.
-    static constexpr int kDepositBytes = (G * (D + 2) * 4 + 15) / 16 * 16;
+    // Pieces of segments that the balanced schedule cuts, parked in LDS
+    // until the workgroup is done, in record form (classes merged):
+    // slot (K, wave) holds head h's unnormalised accumulator row at
+    // slot_acc<K>(wave) + D h, its max and sum at slot_ml<K>(wave)[h] and [G + h].
+    static constexpr int kSlotCols = G;
 
-    __device__ __forceinline__ void deposit(char* slot) {
-        float* f = reinterpret_cast<float*>(slot);
+    __device__ __forceinline__ static float* slot_rows() {
+        __shared__ __attribute__((aligned(16))) float rows[2 * kWaves * G * D];
+        return rows;
+    }
+
+    __device__ __forceinline__ static float* slot_mls() {
+        __shared__ float ml[2 * kWaves * 2 * G];
+        return ml;
+    }
+
+    template <int K>
+    __device__ __forceinline__ static float* slot_acc(int wave) {
+        return slot_rows() + (K * kWaves + wave) * G * D;
+    }
+
+    template <int K>
+    __device__ __forceinline__ static float* slot_ml(int wave) {
+        return slot_mls() + (K * kWaves + wave) * 2 * G;
+    }
+
+    template <int K>
+    __device__ __forceinline__ void deposit(int wave) {
+        float* rows = slot_acc<K>(wave);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float mall, lsum;
             merge_classes(h, mall, lsum);
             if (tok == 0) {
-                f32x4* dst = reinterpret_cast<f32x4*>(f + h * D + piece * EPL);
+                f32x4* dst = reinterpret_cast<f32x4*>(rows + h * D + piece * EPL);
 #pragma unroll
                 for (int r = 0; r < EPL / 4; ++r)
                     dst[r] = f32x4{acc[h][4 * r], acc[h][4 * r + 1], acc[h][4 * r + 2],
                                    acc[h][4 * r + 3]};
             }
             if (lane == 0) {
-                f[G * D + 2 * h] = mall;
-                f[G * D + 2 * h + 1] = lsum;
+                slot_ml<K>(wave)[h] = mall;
+                slot_ml<K>(wave)[G + h] = lsum;
             }
         }
     }
 
     // Write the finished segment (seq, g): out = acc / l for its G heads.
     __device__ __forceinline__ void write_final(const AttnParams& a, int seq, int g) {
-        write_final_merged(a, seq, g, nullptr, 0);
-    }
-
-    // The same after folding in the n pieces deposited at slots, slots +
-    // kDepositBytes, ... by the log-sum-exp rule.
-    __device__ __forceinline__ void write_final_merged(const AttnParams& a, int seq, int g,
-                                                       const char* slots, int n) {
         const size_t row0 = (size_t)seq * a.num_kv_heads * G + (size_t)g * G;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float mall, lsum;
             merge_classes(h, mall, lsum);
-            for (int j = 0; j < n; ++j) {
-                const float* f = reinterpret_cast<const float*>(slots + (size_t)j * kDepositBytes);
-                const float dm = f[G * D + 2 * h], dl = f[G * D + 2 * h + 1];
-                const float mn = mall > dm ? mall : dm;
-                const float a1 = mall == -__builtin_inff() ? 0.f : fast_exp2(mall - mn);
-                const float a2 = dm == -__builtin_inff() ? 0.f : fast_exp2(dm - mn);
-                lsum = lsum * a1 + dl * a2;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    acc[h][e] = acc[h][e] * a1 + f[h * D + piece * EPL + e] * a2;
-                mall = mn;
-            }
             const float inv = 1.0f / lsum;
             if (tok == 0) {
                 if constexpr (EPL == 8) {
