@@ -306,10 +306,12 @@ __device__ __forceinline__ long long units_before(const AttnParams& a, int end) 
     return total * a.num_kv_heads;
 }
 
-// The segment (seq * Hkv + g) whose piece each wave of the workgroup holds
-// in its LDS slot 0 (-1: none).
+// Per wave of the workgroup: the segment (seq * Hkv + g) whose piece it
+// holds in its LDS slot 0 (-1: none), and, if that segment ends in its run
+// after beginning in an earlier workgroup, the first wave holding a piece of
+// it (-1 otherwise).
 __device__ __forceinline__ int* slot_tags() {
-    __shared__ int tags[kWaves];
+    __shared__ int tags[2 * kWaves];
     return tags;
 }
 
@@ -393,10 +395,7 @@ __device__ __forceinline__ int balanced_run(const AttnParams& a, int w, Walker& 
     const long long q = (total + W - 1) / W;
     const long long u0 = (long long)w * q;
     const long long u1 = (u0 + q < total) ? u0 + q : total;
-    if (u0 >= u1) {
-        if (lane == 0) a.ws_info[2 * w] = -1;    // holds no piece of any segment
-        return -1;
-    }
+    if (u0 >= u1) return -1;                     // holds no piece of any segment
     // The workgroup's waves hold units [g_lo, g_hi). A segment that starts
     // before u0 lies inside the workgroup if it starts at or after g_lo and
     // ends by g_hi; one that starts in this run and goes on past u1, if its
@@ -423,19 +422,13 @@ __device__ __forceinline__ int balanced_run(const AttnParams& a, int w, Walker& 
         base += __shfl(incl, 63, 64);
     }
 
-    // Tell the merge kernel whether this wave ends a split segment that it
-    // must merge: the one holding unit u0, if it started in an earlier wave
-    // and ends in this run, unless it lies inside the workgroup.
+    // Whether this wave ends a segment begun in an earlier workgroup (the
+    // one holding unit u0), which the merge kernel finishes.
     {
         const int nu = units_of(clamp_len(a, a.seq_lens[seq]));
         const int g = (int)((u0 - base) / nu);
         const long long seg0 = base + (long long)g * nu;
-        const bool inside = seg0 >= g_lo && seg0 + nu <= g_hi;
-        const bool ends_split = seg0 < u0 && seg0 + nu <= u1 && !inside;
-        if (lane == 0) {
-            a.ws_info[2 * w] = ends_split ? seq * a.num_kv_heads + g : -1;
-            a.ws_info[2 * w + 1] = (int)(seg0 / q);
-        }
+        if (lane == 0 && seg0 < g_lo && seg0 + nu <= u1) slot_tags()[kWaves + wl] = (int)(seg0 / q);
     }
 
     st.init(lane);
@@ -498,7 +491,10 @@ void paged_decode_balanced_kernel(const AttnParams a) {
     const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int w = blockIdx.x * kWaves + wl;
     int* tags = slot_tags();
-    if ((threadIdx.x & 63) == 0) tags[wl] = -1;
+    if ((threadIdx.x & 63) == 0) {
+        tags[wl] = -1;
+        tags[kWaves + wl] = -1;
+    }
     Walker st;
     bool ends_here = false;
     const int pending = w < a.num_items ? balanced_run<Walker>(a, w, st, &ends_here) : -1;
@@ -520,8 +516,9 @@ void paged_decode_balanced_kernel(const AttnParams a) {
         fold_slots<Walker>(a, n, acc_of, ml_of, ends_here, pending / hkv, pending % hkv,
                            2 * (size_t)w + 1);
     }
+    if (wl != 0) return;
     const int s0 = tags[0];
-    if (wl == 0 && s0 >= 0) {
+    if (s0 >= 0) {
         // the segment begun in an earlier workgroup that goes on into this
         // one: its pieces in slot 0 of the first waves
         int n = 1;
@@ -531,27 +528,36 @@ void paged_decode_balanced_kernel(const AttnParams a) {
             [&](int k) { return Walker::template slot_ml<0>(k); }, false, s0 / hkv, s0 % hkv,
             2 * (size_t)w);
     }
+    // the merge kernel's entry for this workgroup: the segment that ends
+    // here after beginning in an earlier workgroup (only s0 can), and its
+    // first wave
+    int wf = -1;
+    for (int j = 0; j < kWaves; ++j) wf = tags[kWaves + j] >= 0 ? tags[kWaves + j] : wf;
+    if ((threadIdx.x & 63) == 0) {
+        a.ws_info[2 * blockIdx.x] = wf >= 0 ? s0 : -1;
+        a.ws_info[2 * blockIdx.x + 1] = wf;
+    }
 }
 
-// Finish the balanced schedule. Wave (w, n) merges column n of the split
-// segment that ends in wave w's run, if any (ws_info[2w] = seq * Hkv + g,
-// ws_info[2w + 1] = wf, the first wave holding a piece). Wave wf wrote
-// record 2 wf + 1, waves wf+1 .. w record 2 v; a record holds one row per
-// column. The records are folded with the log-sum-exp rule (fold_records).
+// Finish the balanced schedule. Wave (b, n) merges column n of the segment
+// that ends in workgroup b after beginning in an earlier one, if any
+// (ws_info[2b] = seq * Hkv + g, ws_info[2b + 1] = wf, the first wave holding
+// a piece). Wave wf wrote record 2 wf + 1, the first wave of each later
+// workgroup up to b record 2 v; a record holds one row per column. The
+// records are folded with the log-sum-exp rule (fold_records).
 template <int D>
 __global__ __launch_bounds__(64 * kWaves)
 void balanced_reduce_kernel(const AttnParams a) {
     const int cols = a.num_queries * a.group;
     const int item = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (item >= a.num_items * cols) return;
-    const int w = item / cols, n = item % cols;
-    const int seg = a.ws_info[2 * w];
+    const int groups = (a.num_items + kWaves - 1) / kWaves;
+    if (item >= groups * cols) return;
+    const int b = item / cols, n = item % cols;
+    const int seg = a.ws_info[2 * b];
     if (seg < 0) return;
-    const int wf = a.ws_info[2 * w + 1];
-    // the starting wave's record, then that of the first wave of each later
-    // workgroup up to this wave's
+    const int wf = a.ws_info[2 * b + 1];
     const int wg0 = wf / kWaves;
-    fold_records<D>(a, 1 + w / kWaves - wg0,
+    fold_records<D>(a, 1 + b - wg0,
                     [&](int r) {
                         return (r == 0 ? 2 * (size_t)wf + 1 : 2 * (size_t)(wg0 + r) * kWaves) * cols + n;
                     },
@@ -605,7 +611,8 @@ hipError_t launch_balanced(const AttnParams& a_in, hipStream_t stream) {
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess || !stage_merges(a.stage)) return err;
     }
-    hipLaunchKernelGGL((balanced_reduce_kernel<D>), dim3((a.num_items * cols + kWaves - 1) / kWaves),
+    const int groups = (a.num_items + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL((balanced_reduce_kernel<D>), dim3((groups * cols + kWaves - 1) / kWaves),
                        dim3(64 * kWaves), 0, stream, a);
     return hipGetLastError();
 }

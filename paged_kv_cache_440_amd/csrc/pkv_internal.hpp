@@ -17,8 +17,8 @@ struct AttnParams {
                                    // [B][H][max_parts] rows (fixed partitions) or
                                    // [2 * kMaxBalancedWaves][G] rows (balanced)
     float* ws_ml;                  // per row: running max in log2 units, sum
-    int* ws_info;                  // balanced: 2 ints per persistent wave (split
-                                   // segment ending in its run, first wave holding it)
+    int* ws_info;                  // balanced: 2 ints per workgroup (segment ending
+                                   // in it that began earlier, first wave holding it)
     const void* q;
     const void* k_pool;
     const void* v_pool;
