@@ -36,8 +36,10 @@ size_t workspace_bytes_for(long long rows, int head_dim, long long parts) {
     return (size_t)(rows * parts) * (size_t)(head_dim + 2) * sizeof(float);
 }
 
-// Two records of `group` rows per persistent wave, then two ints of merge
-// information per wave.
+// Room for two records of `group` rows per persistent wave (record 2w + 1 of
+// a wave where a cut segment begins, 2w of the first wave of a workgroup),
+// then two ints of merge information per wave (one pair per workgroup is
+// used).
 size_t balanced_record_rows(int group) { return (size_t)2 * pkv::kMaxBalancedWaves * group; }
 size_t balanced_workspace_bytes(int group, int head_dim) {
     return balanced_record_rows(group) * (size_t)(head_dim + 2) * sizeof(float) +

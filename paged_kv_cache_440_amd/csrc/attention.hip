@@ -261,19 +261,17 @@ void lse_reduce_kernel(const AttnParams a) {
 // Segment (i, g) is cut into nu_i = ceil(L_i / kUnit) units of kUnit tokens;
 // segments are laid end to end in (i, g) order, giving U = Hkv * sum_i nu_i
 // units. Wave w of W takes units [w * q, (w + 1) * q), q = ceil(U / W). A
-// segment inside one wave's run is finished by that wave. A segment cut by
-// run boundaries gets one partial record per wave: the wave in which it
-// starts writes record 2w + 1, every later wave writes record 2w (a wave's
-// run begins inside at most one segment that started earlier, and ends inside
-// at most one that goes on). Record r holds G rows: ws_acc[r * G + h],
-// ws_ml[r * G + h]. The pieces of a cut segment first meet in LDS: each
-// wave parks its cut pieces there (the first of its run in slot 0, the last
-// in slot 1), and once the whole workgroup is done, the pieces that fall in
-// one workgroup are folded by one of its waves. If the segment starts and
+// segment inside one wave's run is finished by that wave. A wave's run
+// begins inside at most one segment that started earlier and ends inside at
+// most one that goes on; the pieces of such cut segments first meet in LDS.
+// Each wave parks its cut pieces there (the first of its run in slot 0, the
+// last in slot 1), and once the whole workgroup is done, the pieces that fall
+// in one workgroup are folded by one of its waves. If the segment starts and
 // ends in the workgroup, that wave writes the output; otherwise it writes
-// the workgroup's one record: the wave where the segment starts record
-// 2w + 1, the first wave of every later workgroup record 2w. The merge
-// kernel folds those records.
+// the workgroup's one partial record: the wave w where the segment starts
+// record 2w + 1, the first wave w of every later workgroup record 2w.
+// Record r holds one row per column: ws_acc[r * cols + c], ws_ml[r * cols + c].
+// The merge kernel folds those records.
 
 constexpr int kUnit = 32;
 
