@@ -557,7 +557,8 @@ void balanced_reduce_kernel(const AttnParams a) {
     const int wg0 = wf / kWaves;
     fold_records<D>(a, 1 + b - wg0,
                     [&](int r) {
-                        return (r == 0 ? 2 * (size_t)wf + 1 : 2 * (size_t)(wg0 + r) * kWaves) * cols + n;
+                        return (r == 0 ? 2 * (size_t)wf + 1 : 2 * (size_t)(wg0 + r) * kWaves) *
+                                   cols + n;
                     },
                     out_row(a, seg / a.num_kv_heads, seg % a.num_kv_heads, n));
 }
