@@ -308,8 +308,9 @@ __device__ __forceinline__ long long units_before(const AttnParams& a, int end) 
 // holds in its LDS slot 0 (-1: none), and, if that segment ends in its run
 // after beginning in an earlier workgroup, the first wave holding a piece of
 // it (-1 otherwise).
+template <int NW>
 __device__ __forceinline__ int* slot_tags() {
-    __shared__ int tags[2 * kWaves];
+    __shared__ int tags[2 * NW];
     return tags;
 }
 
@@ -378,8 +379,9 @@ __device__ __forceinline__ void fold_slots(const AttnParams& a, int nslots, AccO
 template <class Walker>
 __device__ __forceinline__ int balanced_run(const AttnParams& a, int w, Walker& st,
                                             bool* ends_here) {
+    constexpr int NW = Walker::kGroupWaves;
     const int lane = threadIdx.x & 63;
-    const int wl = w % kWaves;
+    const int wl = w % NW;
     const int W = a.num_items;
     // padding sequences (length 0) own no units: wave w zeroes the rows of
     // sequences w, w + W, ...
@@ -398,7 +400,7 @@ __device__ __forceinline__ int balanced_run(const AttnParams& a, int w, Walker& 
     // before u0 lies inside the workgroup if it starts at or after g_lo and
     // ends by g_hi; one that starts in this run and goes on past u1, if its
     // units past u1 number at most g_room.
-    const long long g_lo = (long long)(w - wl) * q, g_hi = g_lo + kWaves * q;
+    const long long g_lo = (long long)(w - wl) * q, g_hi = g_lo + NW * q;
     const int g_room = __builtin_amdgcn_readfirstlane(
         (int)(g_hi - u1 < 0x7fffffff ? g_hi - u1 : 0x7fffffff));
 
@@ -426,7 +428,7 @@ __device__ __forceinline__ int balanced_run(const AttnParams& a, int w, Walker& 
         const int nu = units_of(clamp_len(a, a.seq_lens[seq]));
         const int g = (int)((u0 - base) / nu);
         const long long seg0 = base + (long long)g * nu;
-        if (lane == 0 && seg0 < g_lo && seg0 + nu <= u1) slot_tags()[kWaves + wl] = (int)(seg0 / q);
+        if (lane == 0 && seg0 < g_lo && seg0 + nu <= u1) slot_tags<NW>()[NW + wl] = (int)(seg0 / q);
     }
 
     st.init(lane);
@@ -466,7 +468,7 @@ __device__ __forceinline__ int balanced_run(const AttnParams& a, int w, Walker& 
         } else if (k0 > 0) {
             // a later piece of a segment begun before this run (its first piece)
             st.template deposit<0>(wl);
-            if (lane == 0) slot_tags()[wl] = seq * a.num_kv_heads + g;
+            if (lane == 0) slot_tags<NW>()[wl] = seq * a.num_kv_heads + g;
         } else {
             // the first piece of a segment that goes on past this run (its last)
             st.template deposit<1>(wl);
@@ -483,15 +485,16 @@ __device__ __forceinline__ int balanced_run(const AttnParams& a, int w, Walker& 
 }
 
 template <class Walker>
-__global__ __launch_bounds__(64 * kWaves)
+__global__ __launch_bounds__(64 * Walker::kGroupWaves)
 __attribute__((amdgpu_waves_per_eu(Walker::kBalancedMinWavesPerSimd)))
 void paged_decode_balanced_kernel(const AttnParams a) {
+    constexpr int NW = Walker::kGroupWaves;
     const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int w = blockIdx.x * kWaves + wl;
-    int* tags = slot_tags();
+    const int w = blockIdx.x * NW + wl;
+    int* tags = slot_tags<NW>();
     if ((threadIdx.x & 63) == 0) {
         tags[wl] = -1;
-        tags[kWaves + wl] = -1;
+        tags[NW + wl] = -1;
     }
     Walker st;
     bool ends_here = false;
@@ -504,7 +507,7 @@ void paged_decode_balanced_kernel(const AttnParams a) {
         // the segment this wave begins: its piece in slot 1, the later ones
         // in slot 0 of the next waves of the workgroup
         int n = 1;
-        while (wl + n < kWaves && tags[wl + n] == pending) ++n;
+        while (wl + n < NW && tags[wl + n] == pending) ++n;
         auto acc_of = [&](int k) {
             return k == 0 ? Walker::template slot_acc<1>(wl) : Walker::template slot_acc<0>(wl + k);
         };
@@ -520,7 +523,7 @@ void paged_decode_balanced_kernel(const AttnParams a) {
         // the segment begun in an earlier workgroup that goes on into this
         // one: its pieces in slot 0 of the first waves
         int n = 1;
-        while (n < kWaves && tags[n] == s0) ++n;
+        while (n < NW && tags[n] == s0) ++n;
         fold_slots<Walker>(
             a, n, [&](int k) { return Walker::template slot_acc<0>(k); },
             [&](int k) { return Walker::template slot_ml<0>(k); }, false, s0 / hkv, s0 % hkv,
@@ -530,7 +533,7 @@ void paged_decode_balanced_kernel(const AttnParams a) {
     // here after beginning in an earlier workgroup (only s0 can), and its
     // first wave
     int wf = -1;
-    for (int j = 0; j < kWaves; ++j) wf = tags[kWaves + j] >= 0 ? tags[kWaves + j] : wf;
+    for (int j = 0; j < NW; ++j) wf = tags[NW + j] >= 0 ? tags[NW + j] : wf;
     if ((threadIdx.x & 63) == 0) {
         a.ws_info[2 * blockIdx.x] = wf >= 0 ? s0 : -1;
         a.ws_info[2 * blockIdx.x + 1] = wf;
@@ -542,22 +545,23 @@ void paged_decode_balanced_kernel(const AttnParams a) {
 // (ws_info[2b] = seq * Hkv + g, ws_info[2b + 1] = wf, the first wave holding
 // a piece). Wave wf wrote record 2 wf + 1, the first wave of each later
 // workgroup up to b record 2 v; a record holds one row per column. The
-// records are folded with the log-sum-exp rule (fold_records).
-template <int D>
+// records are folded with the log-sum-exp rule (fold_records). NW: waves per
+// workgroup of the decode kernel.
+template <int D, int NW>
 __global__ __launch_bounds__(64 * kWaves)
 void balanced_reduce_kernel(const AttnParams a) {
     const int cols = a.num_queries * a.group;
     const int item = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int groups = (a.num_items + kWaves - 1) / kWaves;
+    const int groups = (a.num_items + NW - 1) / NW;
     if (item >= groups * cols) return;
     const int b = item / cols, n = item % cols;
     const int seg = a.ws_info[2 * b];
     if (seg < 0) return;
     const int wf = a.ws_info[2 * b + 1];
-    const int wg0 = wf / kWaves;
+    const int wg0 = wf / NW;
     fold_records<D>(a, 1 + b - wg0,
                     [&](int r) {
-                        return (r == 0 ? 2 * (size_t)wf + 1 : 2 * (size_t)(wg0 + r) * kWaves) *
+                        return (r == 0 ? 2 * (size_t)wf + 1 : 2 * (size_t)(wg0 + r) * NW) *
                                    cols + n;
                     },
                     out_row(a, seg / a.num_kv_heads, seg % a.num_kv_heads, n));
@@ -567,23 +571,27 @@ void balanced_reduce_kernel(const AttnParams a) {
 // (register-limited), queried once per instance.
 template <class Walker>
 int balanced_resident_waves_per_cu() {
+    constexpr int NW = Walker::kGroupWaves;
     static std::atomic<int> cached{0};
     int v = cached.load(std::memory_order_relaxed);
     if (v > 0) return v;
     int groups = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &groups, reinterpret_cast<const void*>(&paged_decode_balanced_kernel<Walker>),
-            64 * kWaves, 0) != hipSuccess || groups <= 0)
+            64 * NW, 0) != hipSuccess || groups <= 0)
         return -1;
-    v = groups * kWaves;
+    v = groups * NW;
     cached.store(v, std::memory_order_relaxed);
     return v;
 }
 
 // The balanced schedule: persistent waves, then the merge of split segments.
-template <class Walker>
+// It runs the walker's own instance for the schedule (Walker::Balanced, whose
+// workgroups hold kGroupWaves waves).
+template <class AnyWalker>
 hipError_t launch_balanced(const AttnParams& a_in, hipStream_t stream) {
-    constexpr int D = Walker::D, G = Walker::G;
+    using Walker = typename AnyWalker::Balanced;
+    constexpr int D = Walker::D, G = Walker::G, NW = Walker::kGroupWaves;
     AttnParams a = a_in;
     // the LDS slots hold kSlotCols columns of a segment
     if (a.num_queries * G > Walker::kSlotCols) return hipErrorInvalidValue;
@@ -606,12 +614,12 @@ hipError_t launch_balanced(const AttnParams& a_in, hipStream_t stream) {
     const int cols = a.num_queries * G;
     if (stage_walks(a.stage)) {
         hipLaunchKernelGGL((paged_decode_balanced_kernel<Walker>),
-                           dim3((a.num_items + kWaves - 1) / kWaves), dim3(64 * kWaves), 0, stream, a);
+                           dim3((a.num_items + NW - 1) / NW), dim3(64 * NW), 0, stream, a);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess || !stage_merges(a.stage)) return err;
     }
-    const int groups = (a.num_items + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL((balanced_reduce_kernel<D>), dim3((groups * cols + kWaves - 1) / kWaves),
+    const int groups = (a.num_items + NW - 1) / NW;
+    hipLaunchKernelGGL((balanced_reduce_kernel<D, NW>), dim3((groups * cols + kWaves - 1) / kWaves),
                        dim3(64 * kWaves), 0, stream, a);
     return hipGetLastError();
 }

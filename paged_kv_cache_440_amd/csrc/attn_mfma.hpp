@@ -123,12 +123,12 @@ template <> __device__ __forceinline__ uint32_t fp8_pair<BF16, true>(uint32_t w)
 // dims 4 piece .. 4 piece + 3 of a row.
 // The calling wave's 8 KB slice of LDS (one allocation per kernel, however
 // many call sites).
+// (NW waves per workgroup; one allocation per kernel and NW.)
+template <int NW>
 __device__ __forceinline__ f32x4 (*wave_tile_at(int wave))[32] {
-    __shared__ f32x4 tile[kWaves][16][32];
+    __shared__ f32x4 tile[NW][16][32];
     return tile[wave];
 }
-
-__device__ __forceinline__ f32x4 (*wave_tile())[32] { return wave_tile_at(threadIdx.x >> 6); }
 
 template <class Store>
 __device__ __forceinline__ void store_column_tile(f32x4 (*t)[32], const f32x4 (&acc)[8], float scale,
@@ -201,7 +201,7 @@ __device__ __forceinline__ char* shared_chunk(int b) {
 }
 
 template <typename S, int G_, bool STREAM, bool FP8 = false, int NT = 1,
-          int WPS = (NT > 1 ? 1 : 2), bool SHARED = false>
+          int WPS = (NT > 1 ? 1 : 2), bool SHARED = false, int NWG = kWaves>
 struct MfmaWalker {
     static constexpr bool kStream = STREAM;     // K/V load policy
     // persistent waves per compute unit in the balanced schedule: for 16-bit
@@ -667,7 +667,7 @@ struct MfmaWalker {
         if constexpr (SHARED)
             return reinterpret_cast<f32x4(*)[32]>(shared_chunk(0) + 8192 * (threadIdx.x >> 6));
         else
-            return wave_tile();
+            return wave_tile_at<NWG>(threadIdx.x >> 6);
     }
 
     __device__ __forceinline__ void write_final(const AttnParams& a, int seq, int g) {
@@ -691,13 +691,22 @@ struct MfmaWalker {
     // with its last piece.
     static constexpr int kSlotCols = 16;
 
+    // Waves per workgroup (NWG): the balanced schedule runs its own instance,
+    // with eight waves (a compute unit's two per SIMD) for 16-bit K/V at one
+    // or two query heads per kv head, where one workgroup per compute unit
+    // keeps the two waves of a SIMD from the same workgroup and halves the
+    // cut segments that cross workgroups; four otherwise.
+    static constexpr int kGroupWaves = NWG;
+    using Balanced = MfmaWalker<S, G_, STREAM, FP8, NT, WPS, SHARED,
+                                (!FP8 && G_ < 4 && NT == 1 && !SHARED) ? 2 * kWaves : kWaves>;
+
     __device__ __forceinline__ static float* slot_rows() {
-        __shared__ __attribute__((aligned(16))) float rows[kWaves * 16 * 128];
+        __shared__ __attribute__((aligned(16))) float rows[NWG * 16 * 128];
         return rows;
     }
 
     __device__ __forceinline__ static float* slot_mls() {
-        __shared__ float ml[2 * kWaves * 32];
+        __shared__ float ml[2 * NWG * 32];
         return ml;
     }
 
@@ -707,12 +716,12 @@ struct MfmaWalker {
         if constexpr (K == 0)
             return slot_rows() + wave * 16 * 128;
         else
-            return reinterpret_cast<float*>(wave_tile_at(wave));
+            return reinterpret_cast<float*>(wave_tile_at<NWG>(wave));
     }
 
     template <int K>
     __device__ __forceinline__ static float* slot_ml(int wave) {
-        return slot_mls() + (K * kWaves + wave) * 32;
+        return slot_mls() + (K * NWG + wave) * 32;
     }
 
     template <int K>

@@ -246,6 +246,9 @@ struct VecWalker {
     // slot (K, wave) holds head h's unnormalised accumulator row at
     // slot_acc<K>(wave) + D h, its max and sum at slot_ml<K>(wave)[h] and [G + h].
     static constexpr int kSlotCols = G;
+    // waves per workgroup in the balanced schedule, which runs this type
+    static constexpr int kGroupWaves = kWaves;
+    using Balanced = VecWalker;
 
     __device__ __forceinline__ static float* slot_rows() {
         __shared__ __attribute__((aligned(16))) float rows[2 * kWaves * G * D];

@@ -13,9 +13,10 @@ segment that ends in the workgroup after beginning earlier. The merge kernel
 folds the records of those segments.
 
 This model makes the same decisions with the same integer rules and checks,
-over many shapes and wave counts, that every unit of every segment reaches
-exactly one output exactly once, that every parked piece and every record is
-used exactly once, and that a workgroup never has two segments to publish.
+over many shapes and wave counts and for workgroups of four and of eight
+waves, that every unit of every segment reaches exactly one output exactly
+once, that every parked piece and every record is used exactly once, and that
+a workgroup never has two segments to publish.
 The GPU parity tests check the kernel's numbers against the oracle; this
 checks the schedule over far more shapes and wave counts than a GPU run can.
 """
@@ -151,12 +152,13 @@ def random_case(rng):
     return lens, hkv, num_waves
 
 
-def test_every_unit_reaches_one_output_once():
-    rng = random.Random(20261203)
+@pytest.mark.parametrize("waves_per_group", [4, 8])
+def test_every_unit_reaches_one_output_once(waves_per_group):
+    rng = random.Random(20261203 + waves_per_group)
     merged = 0
     for _ in range(3000):
         lens, hkv, num_waves = random_case(rng)
-        records, entries = simulate(lens, hkv, num_waves)
+        records, entries = simulate(lens, hkv, num_waves, waves_per_group)
         merged += entries
     assert merged > 0        # the cases do reach the merge kernel
 
