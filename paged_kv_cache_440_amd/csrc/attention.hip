@@ -11,8 +11,10 @@
 // for the G query heads that share it. One wave64 walks a contiguous token
 // range of one segment at a time (a "walker": attn_vec.hpp on the vector
 // units, attn_mfma.hpp on the matrix cores for grouped-query attention);
-// workgroups hold kWaves independent waves (no LDS, no barriers). Three
-// schedules decide the ranges:
+// workgroups hold kWaves waves that share nothing, except under the balanced
+// schedule (its workgroups of Walker::kGroupWaves waves fold the pieces of cut
+// segments in LDS after one end-of-run barrier). Three schedules decide the
+// ranges:
 //   single pass      one wave per segment (partition_size 0);
 //   fixed partitions one wave per (segment, partition of part_len tokens),
 //                    handed out by the hardware dispatcher; numbered g
