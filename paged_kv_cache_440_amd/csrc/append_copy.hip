@@ -60,7 +60,11 @@ void append_kernel(const AppendParams a, long long total) {
                        (size_t)piece * 16;
     const char* s = reinterpret_cast<const char*>(which ? a.v_new : a.k_new);
     char* d = reinterpret_cast<char*>(which ? a.v_pool : a.k_pool);
-    store16(d + dst, load16(s + src));
+    // Non-temporal store: the attention walk reads these rows next, and
+    // lines left dirty in the caches would be written back in the middle of
+    // its read stream, which costs it more than the bytes (the appended rows
+    // of 4 new tokens on the OPT-13B layer: walk 230.5 -> 224.0 us)
+    __builtin_nontemporal_store(load16(s + src), reinterpret_cast<u32x4*>(d + dst));
 }
 
 // -- FP8 (OCP E4M3) quantisation for the FP8 append ----------------------
@@ -156,7 +160,8 @@ void append_fp8_kernel(const AppendFp8Params a, long long total) {
     const size_t row = (((size_t)phys * a.num_kv_heads + g) << a.log2_bs) + (size_t)slot;
     uint8_t* dst = (which ? a.v_pool : a.k_pool) + row * a.head_dim + (size_t)grp * 8;
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
+    // non-temporal for the reason given in append_kernel
+    __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2*>(dst));
 }
 
 // Grid: chunks_per_block * num_pairs * 2 workgroups; each moves
@@ -188,7 +193,8 @@ void copy_blocks_kernel(const CopyParams a, int chunks_per_block) {
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
         const long long p = base + (long long)u * kThreads;
-        if (p < pieces) store16(d + p * 16, v[u]);
+        if (p < pieces)   // non-temporal for the reason given in append_kernel
+            __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(d + p * 16));
     }
 }
 

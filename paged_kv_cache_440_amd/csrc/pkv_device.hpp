@@ -86,9 +86,6 @@ template <> struct Piece<BF16> : Piece16<BF16> {};
 __device__ __forceinline__ u32x4 load16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
-__device__ __forceinline__ void store16(void* p, const u32x4& v) {
-    *reinterpret_cast<u32x4*>(p) = v;
-}
 // Loads of K/V data. STREAM: non-temporal loads, for calls that read each
 // K/V byte once (the lines take the streaming replacement policy instead of
 // displacing data that is reused); otherwise ordinary cached loads, for
