@@ -219,7 +219,10 @@ PKV_API size_t pkv_paged_attention_workspace_size(int num_seqs, int num_heads, i
  *                           an equal share of
  *                           all tokens of the batch, whatever the lengths;
  *                           pieces of a sequence split between waves are
- *                           merged by a log-sum-exp reduce. The split points
+ *                           merged by a log-sum-exp reduce (in LDS among
+ *                           the waves of a workgroup, through the workspace
+ *                           and the merge launch across workgroups). The
+ *                           split points
  *                           depend on the lengths of the whole batch, so a
  *                           row's rounding can change when other rows change
  *                           (under 0 or fixed partitions it cannot: a row's
