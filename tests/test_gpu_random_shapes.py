@@ -3,8 +3,10 @@ float64 oracle: dtype, FP8 pools, head_dim, query heads per kv head, kv
 heads, block size, batch, lengths (empty rows included), schedule, K/V load
 policy and output type are drawn per case. Pools are compared bit for bit,
 attention within the path's tolerance (one more unit in the last place for
-16-bit outputs)."""
+16-bit outputs). PKV_RANDOM_CASES=N runs N cases of each kind instead of the
+default counts (a longer sweep for kernel changes; the seeds follow on)."""
 
+import os
 import sys
 
 import numpy as np
@@ -19,6 +21,10 @@ from tests.gpu_support import (Device, bits, expected_attention, expected_pools,
                                max_err, poison_unwritten_slots, tol, widen)
 
 pytestmark = pytest.mark.gpu
+
+
+def cases(default):
+    return range(int(os.environ.get("PKV_RANDOM_CASES", default)))
 
 
 @pytest.fixture(autouse=True)
@@ -38,7 +44,7 @@ def lengths(rng, batch, longest):
     return [int(x) for x in lens]
 
 
-@pytest.mark.parametrize("case", range(80))
+@pytest.mark.parametrize("case", cases(80))
 def test_decode(case):
     rng = np.random.default_rng(9000 + case)
     dtype = [torch.float32, torch.float16, torch.bfloat16][rng.integers(3)]
@@ -73,7 +79,7 @@ def test_decode(case):
         assert (np.abs(out.float().cpu().numpy() - rounded) <= ulp + tol(w)).all(), shape
 
 
-@pytest.mark.parametrize("case", range(50))
+@pytest.mark.parametrize("case", cases(50))
 def test_multi_query(case):
     rng = np.random.default_rng(9500 + case)
     dtype = [torch.float16, torch.bfloat16][rng.integers(2)]
@@ -116,7 +122,7 @@ def test_multi_query(case):
     assert err <= 2e-3, f"{shape}: max abs error {err:.3e}"
 
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", cases(24))
 def test_chunked_prefill(case):
     """Random chunked-prefill shapes: more than 16 (token, head) columns per
     (sequence, kv head), so the columns run in 16-column tiles, grouped eight
